@@ -1,0 +1,344 @@
+#!/usr/bin/env python3
+"""Benchmark of the chunked-prefill causal attention path on one MI355X.
+
+One step is one pass of the whole path over one batch of synthetic input:
+
+  1. a 131072-token prompt split into 8 chunks of 16384 tokens (64 query
+     heads over 8 KV heads, head dim 128, bf16, paged KV of 64-token blocks):
+     chunk k attends to the cache of chunks 0..k (VPP technical review,
+     English edition, §2.3; the per-chunk latency growth of its §3 / §4.1);
+  2. one mixed batch: a 2048-token prefill chunk at offset 65536 plus 256
+     single-token decode requests with contexts uniform on [1024, 32768]
+     (32 / 8 heads, head dim 128), which exercises the split-KV decode
+     kernel, its merge and the varlen dispatch.
+
+``value`` is the causal-effective TFLOP/s of the whole step: the sum over
+every query row of (visible keys) x 2 x (d_qk + d_v), divided by the step
+time.  Inputs are resident in HBM before timing starts.  Per-chunk latency,
+the split into prefill and decode parts, the prefill kernel's roofline
+fraction (bf16 matrix-core peak) and the decode part's HBM fraction are
+reported beside it, with the fp64 CPU oracle timed on a bounded sample of the
+same workload and its outputs compared with the GPU's.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 matrix peak: 256 CUs x 4096 flop/clk x 2.4 GHz (published 2.5 PF)
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+METRIC = "causal-effective attn TFLOP/s & per-chunk latency vs chunk index (1 MI355X)"
+
+
+def log(msg):
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+def causal_pairs(past: int, c: int) -> int:
+    """Visible (query, key) pairs of one head for a chunk of c tokens at offset past."""
+    return c * past + c * (c + 1) // 2
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=5)
+    p.add_argument("--warmup", type=int, default=2)
+    p.add_argument("--cpu-rows", type=int, default=512, help="oracle rows sampled per chunk for the CPU baseline")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--reps", type=int, default=10, help="repetitions for the decode-only / prefill-only timings")
+    return p.parse_args()
+
+
+class PrefillLoop:
+    """The long prompt: paged pool, block table, every chunk's queries, one output buffer."""
+
+    def __init__(self, L, inputs, torch):
+        w = inputs.WORKLOADS["gqa_128k"]
+        self.w = w
+        n, hkv, d, dv = w.seq_len, w.kv_heads, w.head_dim, w.head_dim_v
+        needed = math.ceil(n / 64)
+        self.table = torch.from_numpy(inputs.block_table(needed, w.seed + 3)).cuda()
+        self.k, self.v = L.paged_pool(inputs.pool_size(needed), hkv, d, dv, torch.bfloat16)
+        self.k.fill_(float("nan"))
+        self.v.fill_(float("nan"))
+        kk = inputs.normal_device((n, hkv, d), w.seed + 1, "bf16")
+        vv = inputs.normal_device((n, hkv, dv), w.seed + 2, "bf16")
+        L.chunkattn_kv_append(kk, vv, 0, self.table, self.k, self.v)
+        self.k_logical, self.v_logical = kk, vv        # kept for the oracle sample
+        self.q = [inputs.normal_device((w.chunk_len, w.heads, d), inputs.chunk_seeds(w, c), "bf16")
+                  for c in range(w.n_chunks)]
+        self.out = torch.empty((w.chunk_len, w.heads, dv), dtype=torch.bfloat16, device="cuda")
+        self.flops = [w.heads * causal_pairs(c * w.chunk_len, w.chunk_len) * 2 * (d + dv)
+                      for c in range(w.n_chunks)]
+
+    def run_chunk(self, L, c, out=None):
+        w = self.w
+        return L.chunk_prefill_attn(self.q[c], self.k, self.v, c * w.chunk_len, w.scale, kv_layout="paged",
+                                    block_table=self.table, out=self.out if out is None else out, num_splits=0)
+
+
+class MixedBatch:
+    """One prefill chunk + 256 decode requests in one shared paged pool."""
+
+    def __init__(self, L, inputs, torch, decode_only=False, prefill_only=False, parent=None):
+        w = inputs.WORKLOADS["mixed"]
+        self.w = w
+        hq, hkv, d, dv = w.heads, w.kv_heads, w.head_dim, w.head_dim_v
+        if parent is None:
+            dec = inputs.context_lengths(w.decode_requests, w.decode_ctx[0], w.decode_ctx[1], w.seed + 7)
+            q_lens = [w.chunk_len] + [1] * w.decode_requests
+            kv_lens = [w.prefill_past + w.chunk_len] + dec.tolist()
+            needed = [math.ceil(x / 64) for x in kv_lens]
+            pool_blocks = inputs.pool_size(sum(needed))
+            perm = inputs.block_table(sum(needed), w.seed + 8, pool_blocks)
+            max_blocks = max(needed)
+            tables = torch.zeros((len(kv_lens), max_blocks), dtype=torch.int32)
+            off = 0
+            for s, nb in enumerate(needed):
+                tables[s, :nb] = torch.from_numpy(perm[off: off + nb])
+                off += nb
+            self.tables = tables.cuda()
+            self.k, self.v = L.paged_pool(pool_blocks, hkv, d, dv, torch.bfloat16)
+            self.k.fill_(float("nan"))
+            self.v.fill_(float("nan"))
+            for s, n in enumerate(kv_lens):
+                kk = inputs.normal_device((n, hkv, d), w.seed + 100 + 2 * s, "bf16")
+                vv = inputs.normal_device((n, hkv, dv), w.seed + 101 + 2 * s, "bf16")
+                L.chunkattn_kv_append(kk, vv, 0, self.tables[s], self.k, self.v)
+            self.q_all = inputs.normal_device((sum(q_lens), hq, d), w.seed + 9, "bf16")
+            self.q_lens, self.kv_lens = q_lens, kv_lens
+        else:
+            self.k, self.v = parent.k, parent.v
+            sel = list(range(1, len(parent.kv_lens))) if decode_only else [0]
+            self.tables = parent.tables[sel].contiguous()
+            self.q_lens = [parent.q_lens[s] for s in sel]
+            self.kv_lens = [parent.kv_lens[s] for s in sel]
+            first = parent.q_lens[0]
+            self.q_all = (parent.q_all[first:] if decode_only else parent.q_all[:first]).contiguous()
+        cu = [0]
+        for x in self.q_lens:
+            cu.append(cu[-1] + x)
+        self.cu = cu
+        self.cu_dev = torch.tensor(cu, dtype=torch.int32, device="cuda")
+        self.kv_dev = torch.tensor(self.kv_lens, dtype=torch.int32, device="cuda")
+        need = L.chunkattn_varlen_workspace_size(cu, self.kv_lens, hq, hkv, dv)
+        self.ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+        self.out = torch.empty((cu[-1], hq, dv), dtype=torch.bfloat16, device="cuda")
+        pref = [(kv - ql, ql) for ql, kv in zip(self.q_lens, self.kv_lens) if ql * (hq // hkv) > 32]
+        decs = [kv for ql, kv in zip(self.q_lens, self.kv_lens) if 0 < ql * (hq // hkv) <= 32]
+        self.prefill_flops = sum(hq * causal_pairs(p, c) * 2 * (d + dv) for p, c in pref)
+        self.decode_flops = sum(hq * kv * 2 * (d + dv) for kv in decs)
+        # bytes the decode part must move: K and V of every cached token once per KV head, plus q and out
+        self.decode_bytes = sum(kv * hkv * (d + dv) * 2 for kv in decs) + len(decs) * hq * (d + dv) * 2
+        self.flops = self.prefill_flops + self.decode_flops
+
+    def run(self, L):
+        return L.chunk_attn_varlen(self.q_all, self.k, self.v, self.tables, self.cu, self.kv_lens, self.w.scale,
+                                   out=self.out, workspace=self.ws, cu_seqlens_q_dev=self.cu_dev,
+                                   kv_lens_dev=self.kv_dev)
+
+
+def median(xs):
+    s = sorted(xs)
+    return s[len(s) // 2] if len(s) % 2 else 0.5 * (s[len(s) // 2 - 1] + s[len(s) // 2])
+
+
+def fit_line(ks, ts):
+    n = len(ks)
+    mk, mt = sum(ks) / n, sum(ts) / n
+    sxx = sum((k - mk) ** 2 for k in ks)
+    b = sum((k - mk) * (t - mt) for k, t in zip(ks, ts)) / sxx
+    a = mt - b * mk
+    ss_res = sum((t - (a + b * k)) ** 2 for k, t in zip(ks, ts))
+    ss_tot = sum((t - mt) ** 2 for t in ts)
+    return a, b, 1 - ss_res / ss_tot if ss_tot else 1.0
+
+
+def cpu_baseline(args, loop, torch):
+    """The fp64 oracle, as it stands, on a bounded sample of the same workload (host cores)."""
+    import numpy as np
+
+    import oracle
+    from chunked_prefill_causal_amd import _lib as L
+    from chunked_prefill_causal_amd import inputs
+
+    w = loop.w
+    cores = len(os.sched_getaffinity(0))
+    k_host = inputs.to_oracle(loop.k_logical)
+    v_host = inputs.to_oracle(loop.v_logical)
+    total_flops, total_s, worst, rows = 0, 0.0, 0.0, 0
+    for c in range(w.n_chunks):
+        tok, head = inputs.sample_rows(w.chunk_len, w.heads, args.cpu_rows, w.seed * 7 + c)
+        q_host = inputs.to_oracle(loop.q[c])
+        past = c * w.chunk_len
+        kv_len = past + w.chunk_len
+        t0 = time.perf_counter()
+        ref, _ = oracle.attend_rows(q_host, k_host[:kv_len], v_host[:kv_len], past, w.scale, tok, head,
+                                    threads=cores)
+        total_s += time.perf_counter() - t0
+        total_flops += int(sum(past + t + 1 for t in tok.tolist())) * 2 * (w.head_dim + w.head_dim_v)
+        out = loop.run_chunk(L, c, out=torch.empty_like(loop.out))
+        got = out[torch.from_numpy(tok).cuda(), torch.from_numpy(head.astype(np.int64)).cuda()]
+        worst = max(worst, float(np.max(np.abs(got.float().cpu().numpy() - ref))))
+        rows += len(tok)
+        log(f"oracle chunk {c}: {len(tok)} rows, running max |gpu - oracle| = {worst:.3e}")
+    cpu_model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), "")
+    except OSError:
+        pass
+    return {"value": total_flops / total_s / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{args.cpu_rows} seeded (token, head) rows per chunk of the 131072-token prompt, all 8 "
+                      f"chunks ({rows} rows, {total_flops:.3e} causal-effective flops in fp64, "
+                      f"{total_s:.1f} s); CPU {cpu_model}",
+            "parity_max_abs_err_on_sample": worst}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures a single GPU; --gpus {args.gpus} is not supported: the attention path here "
+              "runs on one MI355X and has no multi-GPU mode.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from chunked_prefill_causal_amd import _lib as L
+    from chunked_prefill_causal_amd import inputs
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    L.lib()
+    torch.cuda.set_device(0)
+    log("generating inputs in HBM")
+    loop = PrefillLoop(L, inputs, torch)
+    mixed = MixedBatch(L, inputs, torch)
+    dec_only = MixedBatch(L, inputs, torch, decode_only=True, parent=mixed)
+    pre_only = MixedBatch(L, inputs, torch, prefill_only=True, parent=mixed)
+    torch.cuda.synchronize()
+    n_chunks = loop.w.n_chunks
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n_chunks + 1)]
+
+    def step(record):
+        for c in range(n_chunks):
+            if record:
+                ev[c][0].record()
+            loop.run_chunk(L, c)
+            if record:
+                ev[c][1].record()
+        if record:
+            ev[n_chunks][0].record()
+        mixed.run(L)
+        if record:
+            ev[n_chunks][1].record()
+
+    log(f"warmup {args.warmup} step(s)")
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} step(s)")
+    chunk_ms = [[] for _ in range(n_chunks)]
+    mixed_ms = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+        torch.cuda.synchronize()
+        for c in range(n_chunks):
+            chunk_ms[c].append(ev[c][0].elapsed_time(ev[c][1]))
+        mixed_ms.append(ev[n_chunks][0].elapsed_time(ev[n_chunks][1]))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    step_flops = sum(loop.flops) + mixed.flops
+    value = step_flops / (ms_per_step / 1e3) / 1e12
+
+    per_chunk = [median(x) for x in chunk_ms]
+    a, b, r2 = fit_line(list(range(n_chunks)), per_chunk)
+    prefill_tflops = sum(loop.flops) / (sum(per_chunk) / 1e3) / 1e12
+    log(f"step {ms_per_step:.2f} ms, {value:.1f} TFLOP/s; chunk loop {sum(per_chunk):.2f} ms "
+        f"({prefill_tflops:.1f} TFLOP/s); mixed {median(mixed_ms):.3f} ms")
+
+    # the two halves of the mixed batch on their own (for the decode HBM roofline)
+    def timed(fn, reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ts = []
+        for _ in range(reps):
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return median(ts)
+
+    dec_ms = timed(lambda: dec_only.run(L), args.reps)
+    pre_ms = timed(lambda: pre_only.run(L), args.reps)
+    dec_gbps = dec_only.decode_bytes / (dec_ms / 1e3) / 1e9
+    log(f"decode-only {dec_ms:.3f} ms = {dec_gbps:.0f} GB/s; mixed prefill-only {pre_ms:.3f} ms")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the fp64 oracle on a bounded sample")
+        cpu = cpu_baseline(args, loop, torch)
+
+    w = loop.w
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded iid N(0,1) bf16 inputs; random paged block tables)",
+        "config": {
+            "workload": "131072-token prompt as 8 chunks of 16384 (64 q / 8 KV heads, d 128, bf16, paged KV "
+                        "block 64) + mixed batch (2048-token chunk at past 65536 + 256 decodes, ctx U[1024,32768], "
+                        "32 q / 8 KV heads, d 128)",
+            "seq_len": w.seq_len, "chunk_len": w.chunk_len, "n_chunks": n_chunks, "heads": w.heads,
+            "kv_heads": w.kv_heads, "head_dim": w.head_dim, "kv_block": 64,
+            "decode_requests": mixed.w.decode_requests, "step_causal_flops": step_flops,
+        },
+        "per_chunk_ms": [round(x, 3) for x in per_chunk],
+        "per_chunk_fit": {"a_ms": round(a, 4), "b_ms_per_chunk": round(b, 4), "r2": round(r2, 5),
+                          "b_over_a": round(b / a, 3) if a else None},
+        "prefill_chunk_loop": {"ms": round(sum(per_chunk), 3), "tflops": round(prefill_tflops, 1)},
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "prefill_kernel<bf16, bf16, 128, 128, paged> (chunk loop launches)",
+            "achieved": round(prefill_tflops, 1),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(prefill_tflops / PEAK_BF16_TFLOPS, 4),
+            "avg_launch_ms": round(sum(per_chunk) / n_chunks, 4),
+            "avg_causal_flops_per_launch": sum(loop.flops) / n_chunks,
+            "traffic": None,
+        },
+        "mixed_batch": {
+            "ms": round(median(mixed_ms), 4),
+            "prefill_only_ms": round(pre_ms, 4),
+            "decode_only_ms": round(dec_ms, 4),
+            "prefill_tflops": round(mixed.prefill_flops / (pre_ms / 1e3) / 1e12, 1),
+            "roofline_decode": {"bound": "hbm", "achieved": round(dec_gbps, 1), "peak": PEAK_HBM_GBPS,
+                                "unit": "GB/s", "frac": round(dec_gbps / PEAK_HBM_GBPS, 4),
+                                "algorithmic_bytes": mixed.decode_bytes},
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

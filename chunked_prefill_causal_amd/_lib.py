@@ -1,0 +1,239 @@
+"""ctypes binding of libchunkattn: argument marshalling only.
+
+Every step of the attention path runs in the HIP kernels behind
+``include/chunkattn.h``.  This module turns torch tensors into device
+pointers, allocates outputs and workspaces with torch (plumbing), passes the
+current HIP stream, and raises :class:`ChunkAttnError` on a non-OK status.
+There is no CPU fallback: without the built library every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libchunkattn.so")
+
+CA_OK, CA_EINVAL, CA_EUNSUPPORTED, CA_ERANGE, CA_EWORKSPACE, CA_EHIP = 0, -1, -2, -3, -4, -5
+CA_F32, CA_BF16 = 0, 1
+CA_KV_CONTIGUOUS, CA_KV_PAGED = 0, 1
+BLOCK_SIZE = 64
+
+EXPORTED = ("ca_prefill_opts_init", "chunk_prefill_attn", "chunkattn_prefill_workspace_size",
+            "chunkattn_prefill_auto_splits", "chunk_attn_varlen", "chunkattn_varlen_workspace_size",
+            "chunkattn_kv_append", "chunkattn_last_error", "chunkattn_version")
+
+
+class ChunkAttnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"libchunkattn status {status}: {message}")
+        self.status = status
+
+
+class PrefillOpts(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int), ("out_dtype", ctypes.c_int), ("head_dim_v", ctypes.c_int32),
+                ("kv_layout", ctypes.c_int), ("kv_capacity", ctypes.c_int64),
+                ("block_table", ctypes.c_void_p), ("block_table_len", ctypes.c_int32),
+                ("num_blocks", ctypes.c_int32), ("lse_out", ctypes.c_void_p),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+                ("num_splits", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, sz, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
+    L.ca_prefill_opts_init.argtypes = [ctypes.POINTER(PrefillOpts)]
+    L.ca_prefill_opts_init.restype = None
+    L.chunk_prefill_attn.argtypes = [vp, vp, vp, i64, i64, i32, i32, i32, f32, vp, ctypes.POINTER(PrefillOpts), vp]
+    L.chunk_prefill_attn.restype = ctypes.c_int
+    L.chunkattn_prefill_workspace_size.argtypes = [i64, i32, i32, i32]
+    L.chunkattn_prefill_workspace_size.restype = sz
+    L.chunkattn_prefill_auto_splits.argtypes = [i64, i64, i32, i32]
+    L.chunkattn_prefill_auto_splits.restype = i32
+    L.chunk_attn_varlen.argtypes = [vp, vp, vp, vp, i32, i32, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32,
+                                    vp, vp, vp, sz, vp]
+    L.chunk_attn_varlen.restype = ctypes.c_int
+    L.chunkattn_varlen_workspace_size.argtypes = [vp, vp, i32, i32, i32, i32]
+    L.chunkattn_varlen_workspace_size.restype = sz
+    L.chunkattn_kv_append.argtypes = [vp, vp, i64, i64, i32, i32, i32, ctypes.c_int, vp, i32, i32, vp, vp, vp]
+    L.chunkattn_kv_append.restype = ctypes.c_int
+    L.chunkattn_last_error.argtypes = []
+    L.chunkattn_last_error.restype = ctypes.c_char_p
+    L.chunkattn_version.argtypes = []
+    L.chunkattn_version.restype = i32
+    _lib = L
+    return L
+
+
+def _check(status: int) -> None:
+    if status != CA_OK:
+        raise ChunkAttnError(status, lib().chunkattn_last_error().decode())
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+
+
+def _dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.bfloat16:
+        return CA_BF16
+    if dt == torch.float32:
+        return CA_F32
+    raise TypeError(f"unsupported dtype {dt}")
+
+
+def elems_per_16b(dt: torch.dtype) -> int:
+    return 16 // torch.empty((), dtype=dt).element_size()
+
+
+def paged_pool(num_blocks: int, kv_heads: int, head_dim: int, head_dim_v: int, dtype, device="cuda"):
+    """Allocate (uninitialised) K and V pools in the library's paged layout."""
+    x = elems_per_16b(dtype)
+    k = torch.empty((num_blocks, kv_heads, head_dim // x, BLOCK_SIZE, x), dtype=dtype, device=device)
+    v = torch.empty((num_blocks, kv_heads, BLOCK_SIZE // x, head_dim_v, x), dtype=dtype, device=device)
+    return k, v
+
+
+def version() -> int:
+    return lib().chunkattn_version()
+
+
+def chunkattn_prefill_workspace_size(chunk_len: int, heads: int, head_dim_v: int, num_splits: int) -> int:
+    return lib().chunkattn_prefill_workspace_size(chunk_len, heads, head_dim_v, num_splits)
+
+
+def chunkattn_prefill_auto_splits(past_len: int, chunk_len: int, heads: int, kv_heads: int) -> int:
+    return lib().chunkattn_prefill_auto_splits(past_len, chunk_len, heads, kv_heads)
+
+
+def chunk_prefill_attn(q, k_cache, v_cache, past_len: int, scale: float | None = None, *,
+                       kv_layout: str = "contiguous", block_table=None, num_blocks: int | None = None,
+                       kv_heads: int | None = None, head_dim_v: int | None = None, out=None, out_dtype=None,
+                       return_lse: bool = False, lse=None, num_splits: int = 0, workspace=None,
+                       kv_capacity: int | None = None, stream=None):
+    """One chunk of causal prefill attention; see ``chunk_prefill_attn`` in the header.
+
+    ``q`` is ``[chunk_len, heads, head_dim]``.  Contiguous caches are
+    ``[capacity, kv_heads, head_dim(_v)]``; paged pools come from
+    :func:`paged_pool` with ``block_table`` an int32 device tensor.
+    Returns ``out`` (and ``lse [heads, chunk_len]`` when requested).
+    """
+    c, heads, d = q.shape
+    paged = kv_layout == "paged"
+    if paged:
+        nb, hkv = k_cache.shape[0], k_cache.shape[1]
+        dv = v_cache.shape[3]
+    else:
+        hkv, dv = k_cache.shape[1], v_cache.shape[2]
+        nb = 0
+    if kv_heads is not None and kv_heads != hkv:
+        raise ValueError("kv_heads disagrees with the cache shape")
+    if head_dim_v is not None and head_dim_v != dv:
+        raise ValueError("head_dim_v disagrees with the value cache shape")
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((c, heads, dv), dtype=out_dtype, device=q.device)
+    if return_lse and lse is None:
+        lse = torch.empty((heads, c), dtype=torch.float32, device=q.device)
+    if num_splits == 0 and workspace is None:
+        auto = chunkattn_prefill_auto_splits(past_len, c, heads, hkv)
+        if auto > 1:
+            workspace = torch.empty(chunkattn_prefill_workspace_size(c, heads, dv, auto),
+                                    dtype=torch.uint8, device=q.device)
+    elif num_splits > 1 and workspace is None:
+        workspace = torch.empty(max(1, chunkattn_prefill_workspace_size(c, heads, dv, num_splits)),
+                                dtype=torch.uint8, device=q.device)
+    o = PrefillOpts()
+    lib().ca_prefill_opts_init(ctypes.byref(o))
+    o.dtype = _dtype_code(q.dtype)
+    o.out_dtype = _dtype_code(out.dtype)
+    o.head_dim_v = dv
+    o.kv_layout = CA_KV_PAGED if paged else CA_KV_CONTIGUOUS
+    if paged:
+        o.block_table = _ptr(block_table)
+        o.block_table_len = block_table.numel()
+        o.num_blocks = nb if num_blocks is None else num_blocks
+    else:
+        o.kv_capacity = k_cache.shape[0] if kv_capacity is None else kv_capacity
+    o.lse_out = _ptr(lse)
+    if workspace is not None:
+        o.workspace = _ptr(workspace)
+        o.workspace_bytes = workspace.numel() * workspace.element_size()
+    o.num_splits = num_splits
+    _check(lib().chunk_prefill_attn(_ptr(q), _ptr(k_cache), _ptr(v_cache), past_len, c, heads, hkv, d,
+                                    float(scale), _ptr(out), ctypes.byref(o), _stream(stream)))
+    return (out, lse) if return_lse else out
+
+
+def _host_i32(x):
+    t = torch.as_tensor(x, dtype=torch.int32).cpu().contiguous()
+    return t
+
+
+def chunkattn_varlen_workspace_size(cu_seqlens_q, kv_lens, heads: int, kv_heads: int, head_dim_v: int) -> int:
+    cu, kv = _host_i32(cu_seqlens_q), _host_i32(kv_lens)
+    return lib().chunkattn_varlen_workspace_size(cu.data_ptr(), kv.data_ptr(), kv.numel(), heads, kv_heads,
+                                                 head_dim_v)
+
+
+def chunk_attn_varlen(q, k_pool, v_pool, block_tables, cu_seqlens_q, kv_lens, scale: float | None = None, *,
+                      num_blocks: int | None = None, out=None, return_lse: bool = False, lse=None,
+                      workspace=None, cu_seqlens_q_dev=None, kv_lens_dev=None, stream=None):
+    """Mixed prefill + decode batch over a paged pool; see ``chunk_attn_varlen``.
+
+    ``cu_seqlens_q`` and ``kv_lens`` are host sequences (int32); device copies
+    are made unless given.  ``block_tables`` is ``[num_seqs, max_blocks]`` int32
+    on the device.
+    """
+    total_q, heads, d = q.shape
+    hkv, dv = k_pool.shape[1], v_pool.shape[3]
+    cu, kv = _host_i32(cu_seqlens_q), _host_i32(kv_lens)
+    n = kv.numel()
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    if cu_seqlens_q_dev is None:
+        cu_seqlens_q_dev = cu.to(q.device)
+    if kv_lens_dev is None:
+        kv_lens_dev = kv.to(q.device)
+    if out is None:
+        out = torch.empty((total_q, heads, dv), dtype=q.dtype, device=q.device)
+    if return_lse and lse is None:
+        lse = torch.empty((heads, total_q), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        need = lib().chunkattn_varlen_workspace_size(cu.data_ptr(), kv.data_ptr(), n, heads, hkv, dv)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(lib().chunk_attn_varlen(
+        _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables), block_tables.shape[1],
+        k_pool.shape[0] if num_blocks is None else num_blocks, _ptr(cu_seqlens_q_dev), _ptr(kv_lens_dev),
+        cu.data_ptr(), kv.data_ptr(), n, heads, hkv, d, dv, float(scale), _ptr(out), _ptr(lse),
+        _ptr(workspace), workspace.numel(), _stream(stream)))
+    return (out, lse) if return_lse else out
+
+
+def chunkattn_kv_append(k_new, v_new, start_pos: int, block_table, k_pool, v_pool, *, num_blocks: int | None = None,
+                        stream=None) -> None:
+    """Write ``k_new [n, kv_heads, d]`` / ``v_new [n, kv_heads, dv]`` at positions start_pos.."""
+    n, hkv, d = k_new.shape
+    dv = v_new.shape[2]
+    _check(lib().chunkattn_kv_append(_ptr(k_new), _ptr(v_new), start_pos, n, hkv, d, dv, _dtype_code(k_new.dtype),
+                                     _ptr(block_table), block_table.numel(),
+                                     k_pool.shape[0] if num_blocks is None else num_blocks,
+                                     _ptr(k_pool), _ptr(v_pool), _stream(stream)))

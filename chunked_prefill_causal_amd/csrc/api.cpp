@@ -1,0 +1,388 @@
+// C ABI of libchunkattn: argument validation, launch planning and dispatch.
+// Every check runs before the first HIP call, so a rejected call touches no
+// device state.  See include/chunkattn.h for the contract of each entry point.
+#include "chunkattn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "launch.h"
+
+using namespace chunkattn;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+ca_status fail(ca_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+ca_status ok() {
+  g_err[0] = '\0';
+  return CA_OK;
+}
+
+ca_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(CA_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+constexpr int kNumCUs = 256;          // MI355X
+constexpr int64_t kMaxTokens = (int64_t)1 << 30;
+
+// Largest of 4, 2, 1 that divides the GQA group: that many query heads of one
+// KV head share a prefill workgroup (128 query rows in total).
+int heads_per_wg(int group) { return group % 4 == 0 ? 4 : (group % 2 == 0 ? 2 : 1); }
+
+size_t prefill_ws_bytes(int64_t chunk_len, int heads, int dv, int splits) {
+  if (splits <= 1) return 0;
+  const size_t rows = (size_t)chunk_len * heads * splits;
+  return align_up(rows * dv * sizeof(float), 256) + rows * 2 * sizeof(float);
+}
+
+// Decode split length: aim for enough waves to fill the chip several times
+// over, in multiples of the 64-token tile.
+int decode_split_tokens(const int32_t* cu, const int32_t* kv, int num_seqs, int kv_heads, int group) {
+  int64_t tiles = 0;
+  for (int s = 0; s < num_seqs; ++s) {
+    const int q_len = cu[s + 1] - cu[s];
+    if (q_len >= 1 && q_len * group <= 32) tiles += (int64_t)(kv[s] + kBlock - 1) / kBlock * kv_heads;
+  }
+  const int64_t target_waves = (int64_t)kNumCUs * 4 * 16;
+  int64_t per = (tiles + target_waves - 1) / target_waves;   // tiles per wave
+  if (per < 4) per = 4;
+  if (per > 64) per = 64;
+  return (int)per * kBlock;
+}
+
+// Host plan of a varlen batch, from the host copies of the lengths.  The
+// device-side plan kernel derives the same offsets from the device copies.
+struct BatchPlan {
+  int split_tokens = 0;
+  int max_splits = 0;
+  int64_t slots = 0;          // decode partial slots
+  int64_t prefill_wgs = 0;    // prefill workgroups over all prefill-path sequences
+  int n_decode = 0, n_prefill = 0;
+  size_t ws_off_bytes = 0, wg_off_bytes = 0, o_bytes = 0, ml_bytes = 0;
+  size_t total() const {
+    return (n_decode || n_prefill) ? ws_off_bytes + wg_off_bytes + o_bytes + ml_bytes : 0;
+  }
+};
+
+BatchPlan plan_batch(const int32_t* cu, const int32_t* kv, int num_seqs, int heads, int kv_heads, int dv) {
+  BatchPlan p;
+  const int group = heads / kv_heads;
+  const int hpw = heads_per_wg(group);
+  const int tok_wg = 128 / hpw;
+  p.split_tokens = decode_split_tokens(cu, kv, num_seqs, kv_heads, group);
+  for (int s = 0; s < num_seqs; ++s) {
+    const int q_len = cu[s + 1] - cu[s];
+    if (q_len >= 1 && q_len * group <= 32) {
+      const int ns = (kv[s] + p.split_tokens - 1) / p.split_tokens;
+      p.slots += (int64_t)q_len * heads * ns;
+      if (ns > p.max_splits) p.max_splits = ns;
+      ++p.n_decode;
+    } else if (q_len > 0) {
+      p.prefill_wgs += (int64_t)((q_len + tok_wg - 1) / tok_wg) * (heads / hpw);
+      ++p.n_prefill;
+    }
+  }
+  p.ws_off_bytes = align_up((size_t)num_seqs * sizeof(int64_t), 256);
+  p.wg_off_bytes = align_up((size_t)(num_seqs + 1) * sizeof(int64_t), 256);
+  p.o_bytes = align_up((size_t)p.slots * dv * sizeof(float), 256);
+  p.ml_bytes = align_up((size_t)p.slots * 2 * sizeof(float), 256);
+  return p;
+}
+
+// Split count for a short chunk over a long prefix: enough workgroups for
+// about four per CU, each split keeping at least 16 key tiles.
+int auto_splits(int64_t past_len, int64_t chunk_len, int heads, int kv_heads) {
+  const int hpw = heads_per_wg(heads / kv_heads);
+  const int64_t base = (chunk_len + 128 / hpw - 1) / (128 / hpw) * (heads / hpw);
+  const int64_t n_tiles = (past_len + chunk_len + kBlock - 1) / kBlock;
+  if (base == 0 || base >= 2 * kNumCUs || n_tiles < 32) return 1;
+  int64_t want = (4 * kNumCUs + base - 1) / base;
+  const int64_t cap = n_tiles / 16;
+  if (want > cap) want = cap;
+  return want > 1 ? (int)want : 1;
+}
+
+ca_status check_dtype(int d) {
+  if (d != CA_F32 && d != CA_BF16) return fail(CA_EINVAL, "unknown dtype %d", d);
+  return CA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+void ca_prefill_opts_init(ca_prefill_opts* o) {
+  if (!o) return;
+  std::memset(o, 0, sizeof *o);
+  o->dtype = CA_BF16;
+  o->out_dtype = CA_BF16;
+  o->kv_layout = CA_KV_CONTIGUOUS;
+}
+
+const char* chunkattn_last_error(void) { return g_err; }
+
+int32_t chunkattn_version(void) { return CHUNKATTN_VERSION; }
+
+size_t chunkattn_prefill_workspace_size(int64_t chunk_len, int32_t heads, int32_t head_dim_v, int32_t num_splits) {
+  if (chunk_len <= 0 || heads <= 0 || head_dim_v <= 0) return 0;
+  return prefill_ws_bytes(chunk_len, heads, head_dim_v, num_splits);
+}
+
+int32_t chunkattn_prefill_auto_splits(int64_t past_len, int64_t chunk_len, int32_t heads, int32_t kv_heads) {
+  if (past_len < 0 || chunk_len < 0 || heads <= 0 || kv_heads <= 0 || heads % kv_heads) return 0;
+  return auto_splits(past_len, chunk_len, heads, kv_heads);
+}
+
+ca_status chunk_prefill_attn(const void* q, const void* k, const void* v, int64_t past_len, int64_t chunk_len,
+                             int32_t heads, int32_t kv_heads, int32_t head_dim, float scale, void* out,
+                             const ca_prefill_opts* opts_in, void* stream) {
+  ca_prefill_opts o;
+  ca_prefill_opts_init(&o);
+  if (opts_in) o = *opts_in;
+  // An empty chunk may come with null q/out (empty tensors have no storage).
+  if (!k || !v || (chunk_len != 0 && (!q || !out)))
+    return fail(CA_EINVAL, "q, k_cache, v_cache and out must be non-null");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
+    return fail(CA_EINVAL, "q, k_cache, v_cache and out must be 16-byte aligned");
+  if (past_len < 0 || chunk_len < 0) return fail(CA_EINVAL, "past_len and chunk_len must be >= 0");
+  if (past_len + chunk_len > kMaxTokens) return fail(CA_ERANGE, "past_len + chunk_len exceeds 2^30 tokens");
+  if (heads <= 0 || kv_heads <= 0 || heads % kv_heads != 0)
+    return fail(CA_EINVAL, "heads (%d) must be a positive multiple of kv_heads (%d)", heads, kv_heads);
+  if (!std::isfinite(scale) || !(scale > 0.f)) return fail(CA_EINVAL, "scale must be finite and > 0");
+  if (ca_status st = check_dtype(o.dtype)) return st;
+  if (ca_status st = check_dtype(o.out_dtype)) return st;
+  const int dv = o.head_dim_v ? o.head_dim_v : head_dim;
+  const DType din = (DType)o.dtype, dout = (DType)o.out_dtype;
+  if (!prefill_supported(din, dout, head_dim, dv))
+    return fail(CA_EUNSUPPORTED, "unsupported (head_dim, head_dim_v, dtype, out_dtype) = (%d, %d, %d, %d)",
+                head_dim, dv, (int)o.dtype, (int)o.out_dtype);
+  if (o.lse_out && !aligned(o.lse_out, 4)) return fail(CA_EINVAL, "lse_out must be 4-byte aligned");
+  const int64_t kv_len = past_len + chunk_len;
+  const bool paged = o.kv_layout == CA_KV_PAGED;
+  if (o.kv_layout != CA_KV_CONTIGUOUS && !paged) return fail(CA_EINVAL, "unknown kv_layout %d", (int)o.kv_layout);
+  if (paged) {
+    if (!o.block_table || !aligned(o.block_table, 4)) return fail(CA_EINVAL, "paged layout needs a block_table");
+    if (o.num_blocks <= 0) return fail(CA_EINVAL, "num_blocks must be > 0");
+    if ((int64_t)o.block_table_len * kBlock < kv_len)
+      return fail(CA_ERANGE, "block table covers %lld tokens, need %lld", (long long)o.block_table_len * kBlock,
+                  (long long)kv_len);
+  } else {
+    const int64_t cap = o.kv_capacity ? o.kv_capacity : kv_len;
+    if (cap < kv_len) return fail(CA_ERANGE, "kv_capacity %lld < past_len + chunk_len %lld", (long long)cap,
+                                  (long long)kv_len);
+  }
+  if (o.num_splits < 0) return fail(CA_EINVAL, "num_splits must be >= 0");
+
+  const int group = heads / kv_heads;
+  const int hpw = heads_per_wg(group);
+  const int tok_wg = 128 / hpw;
+  const int64_t n_tb = (chunk_len + tok_wg - 1) / tok_wg;
+  const int n_hg = heads / hpw;
+  const int64_t base = n_tb * n_hg;
+  const int64_t n_tiles = (kv_len + kBlock - 1) / kBlock;
+  int splits = o.num_splits;
+  if (splits == 0) {
+    const int want = auto_splits(past_len, chunk_len, heads, kv_heads);
+    splits = (want > 1 && o.workspace && o.workspace_bytes >= prefill_ws_bytes(chunk_len, heads, dv, want)) ? want : 1;
+  } else if (splits > n_tiles) {
+    splits = (int)(n_tiles > 0 ? n_tiles : 1);
+  }
+  if (splits > 1) {
+    const size_t need = prefill_ws_bytes(chunk_len, heads, dv, splits);
+    if (!o.workspace || o.workspace_bytes < need)
+      return fail(CA_EWORKSPACE, "split-KV with %d splits needs %zu workspace bytes", splits, need);
+    if (!aligned(o.workspace, 256)) return fail(CA_EINVAL, "workspace must be 256-byte aligned");
+  }
+  if (base * splits > 0x7fffffffLL) return fail(CA_ERANGE, "launch grid too large");
+  if (chunk_len == 0) return ok();
+
+  PrefillArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.lse = o.lse_out;
+  a.block_table = o.block_table;
+  a.past_len = past_len;
+  a.chunk_len = chunk_len;
+  a.kv_len = kv_len;
+  a.lse_stride = chunk_len;
+  a.heads = heads;
+  a.kv_heads = kv_heads;
+  a.group = group;
+  a.num_blocks = o.num_blocks;
+  a.hpw = hpw;
+  a.n_tok_blocks = (int)n_tb;
+  a.n_head_groups = n_hg;
+  a.num_splits = splits;
+  a.xcd_remap = (splits == 1 && n_hg % 8 == 0) ? 1 : 0;
+  a.scale_log2 = scale * kLog2e;
+  if (splits > 1) {
+    const size_t rows = (size_t)chunk_len * heads * splits;
+    a.ws_o = (float*)o.workspace;
+    a.ws_ml = (float*)((char*)o.workspace + align_up(rows * dv * sizeof(float), 256));
+  }
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = launch_prefill(din, dout, head_dim, dv, paged, a, (int)(base * splits), s);
+  if (e != hipSuccess) return hip_status(e, "prefill launch");
+  if (splits > 1) {
+    e = launch_prefill_merge(dout, dv, a, s);
+    if (e != hipSuccess) return hip_status(e, "prefill merge launch");
+  }
+  return ok();
+}
+
+size_t chunkattn_varlen_workspace_size(const int32_t* cu, const int32_t* kv, int32_t num_seqs, int32_t heads,
+                                       int32_t kv_heads, int32_t head_dim_v) {
+  if (!cu || !kv || num_seqs <= 0 || heads <= 0 || kv_heads <= 0 || heads % kv_heads || head_dim_v <= 0) return 0;
+  return plan_batch(cu, kv, num_seqs, heads, kv_heads, head_dim_v).total();
+}
+
+ca_status chunk_attn_varlen(const void* q, const void* k_pool, const void* v_pool, const int32_t* block_tables,
+                            int32_t max_blocks, int32_t num_blocks, const int32_t* cu_dev, const int32_t* kv_dev,
+                            const int32_t* cu, const int32_t* kv, int32_t num_seqs, int32_t heads, int32_t kv_heads,
+                            int32_t head_dim, int32_t head_dim_v, float scale, void* out, float* lse_out,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  if (!k_pool || !v_pool || !block_tables || !cu_dev || !kv_dev || !cu || !kv)
+    return fail(CA_EINVAL, "null pointer argument");
+  if (num_seqs > 0 && num_seqs <= 65535 && cu[num_seqs] != 0 && (!q || !out))
+    return fail(CA_EINVAL, "q and out must be non-null when the batch has query rows");
+  if (!aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(out, 16))
+    return fail(CA_EINVAL, "q, pools and out must be 16-byte aligned");
+  if (!aligned(block_tables, 4) || !aligned(cu_dev, 4) || !aligned(kv_dev, 4) || (lse_out && !aligned(lse_out, 4)))
+    return fail(CA_EINVAL, "int32 and fp32 arrays must be 4-byte aligned");
+  if (num_seqs <= 0 || num_seqs > 65535) return fail(CA_EINVAL, "num_seqs must be in [1, 65535]");
+  if (heads <= 0 || kv_heads <= 0 || heads % kv_heads != 0 || kv_heads > 65535)
+    return fail(CA_EINVAL, "heads (%d) must be a positive multiple of kv_heads (%d)", heads, kv_heads);
+  if (max_blocks <= 0 || num_blocks <= 0) return fail(CA_EINVAL, "max_blocks_per_seq and num_blocks must be > 0");
+  if (!std::isfinite(scale) || !(scale > 0.f)) return fail(CA_EINVAL, "scale must be finite and > 0");
+  if (!prefill_supported(DType::BF16, DType::BF16, head_dim, head_dim_v) || !decode_supported(head_dim, head_dim_v))
+    return fail(CA_EUNSUPPORTED, "unsupported (head_dim, head_dim_v) = (%d, %d)", head_dim, head_dim_v);
+  if (cu[0] != 0) return fail(CA_EINVAL, "cu_seqlens_q[0] must be 0");
+  for (int s = 0; s < num_seqs; ++s) {
+    const int q_len = cu[s + 1] - cu[s];
+    if (q_len < 0) return fail(CA_EINVAL, "cu_seqlens_q must be non-decreasing (sequence %d)", s);
+    if (kv[s] < 0 || (q_len > 0 && kv[s] < q_len))
+      return fail(CA_EINVAL, "kv_lens[%d] = %d is negative or below q_len %d", s, kv[s], q_len);
+    if ((int64_t)kv[s] > (int64_t)max_blocks * kBlock)
+      return fail(CA_ERANGE, "kv_lens[%d] = %d exceeds the block table (%d blocks)", s, kv[s], max_blocks);
+  }
+  const int64_t total_q = cu[num_seqs];
+  const int group = heads / kv_heads;
+  const BatchPlan plan = plan_batch(cu, kv, num_seqs, heads, kv_heads, head_dim_v);
+  if (plan.total()) {
+    if (!workspace || workspace_bytes < plan.total())
+      return fail(CA_EWORKSPACE, "this batch needs %zu workspace bytes", plan.total());
+    if (!aligned(workspace, 256)) return fail(CA_EINVAL, "workspace must be 256-byte aligned");
+  }
+  if (plan.prefill_wgs > 0x7fffffffLL) return fail(CA_ERANGE, "launch grid too large");
+  if (total_q == 0) return ok();
+
+  hipStream_t st = (hipStream_t)stream;
+  const float cs = scale * kLog2e;
+  const int hpw = heads_per_wg(group);
+  char* ws = (char*)workspace;
+  DecodeArgs d{};
+  d.q = q;
+  d.k = k_pool;
+  d.v = v_pool;
+  d.block_tables = block_tables;
+  d.cu_seqlens_q = cu_dev;
+  d.kv_lens = kv_dev;
+  d.ws_off = (int64_t*)ws;
+  d.wg_off = (int64_t*)(ws + plan.ws_off_bytes);
+  d.ws_o = (float*)(ws + plan.ws_off_bytes + plan.wg_off_bytes);
+  d.ws_ml = (float*)(ws + plan.ws_off_bytes + plan.wg_off_bytes + plan.o_bytes);
+  d.out = out;
+  d.lse = lse_out;
+  d.total_q = total_q;
+  d.total_slots = plan.slots;
+  d.num_seqs = num_seqs;
+  d.max_blocks = max_blocks;
+  d.num_blocks = num_blocks;
+  d.heads = heads;
+  d.kv_heads = kv_heads;
+  d.group = group;
+  d.split_tokens = plan.split_tokens;
+  d.tok_wg = 128 / hpw;
+  d.n_head_groups = heads / hpw;
+  d.scale_log2 = cs;
+  hipError_t e = launch_batch_plan(d, st);
+  if (e != hipSuccess) return hip_status(e, "varlen plan launch");
+  if (plan.n_prefill) {
+    // Prefill-path sequences: one launch, straight into out.
+    PrefillArgs a{};
+    a.q = q;
+    a.k = k_pool;
+    a.v = v_pool;
+    a.out = out;
+    a.lse = lse_out;
+    a.block_table = block_tables;
+    a.lse_stride = total_q;
+    a.heads = heads;
+    a.kv_heads = kv_heads;
+    a.group = group;
+    a.num_blocks = num_blocks;
+    a.hpw = hpw;
+    a.n_head_groups = heads / hpw;
+    a.num_splits = 1;
+    a.xcd_remap = 0;
+    a.scale_log2 = cs;
+    a.cu_seqlens_q = cu_dev;
+    a.kv_lens = kv_dev;
+    a.wg_off = d.wg_off;
+    a.num_seqs = num_seqs;
+    a.max_blocks = max_blocks;
+    e = launch_prefill_varlen(head_dim, head_dim_v, a, (int)plan.prefill_wgs, st);
+    if (e != hipSuccess) return hip_status(e, "varlen prefill launch");
+  }
+  if (plan.n_decode) {
+    e = launch_decode(head_dim, head_dim_v, d, plan.max_splits, st);
+    if (e == hipSuccess) e = launch_decode_merge(head_dim_v, d, st);
+    if (e != hipSuccess) return hip_status(e, "varlen decode launch");
+  }
+  return ok();
+}
+
+ca_status chunkattn_kv_append(const void* k_new, const void* v_new, int64_t start_pos, int64_t n_tokens,
+                              int32_t kv_heads, int32_t head_dim, int32_t head_dim_v, ca_dtype dtype,
+                              const int32_t* block_table, int32_t block_table_len, int32_t num_blocks, void* k_pool,
+                              void* v_pool, void* stream) {
+  if (!k_new || !v_new || !block_table || !k_pool || !v_pool) return fail(CA_EINVAL, "null pointer argument");
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) ||
+      !aligned(block_table, 4))
+    return fail(CA_EINVAL, "misaligned pointer argument");
+  if (ca_status st = check_dtype(dtype)) return st;
+  if (start_pos < 0 || n_tokens < 0) return fail(CA_EINVAL, "start_pos and n_tokens must be >= 0");
+  if (kv_heads <= 0 || num_blocks <= 0) return fail(CA_EINVAL, "kv_heads and num_blocks must be > 0");
+  const int x = dtype == CA_BF16 ? 8 : 4;
+  if (head_dim <= 0 || head_dim_v <= 0 || head_dim % x || head_dim_v % x || head_dim > 1024 || head_dim_v > 1024)
+    return fail(CA_EUNSUPPORTED, "head dims must be positive multiples of %d up to 1024", x);
+  if (start_pos + n_tokens > (int64_t)block_table_len * kBlock)
+    return fail(CA_ERANGE, "block table covers %lld tokens, need %lld", (long long)block_table_len * kBlock,
+                (long long)(start_pos + n_tokens));
+  if (n_tokens == 0) return ok();
+  hipError_t e = launch_kv_append((DType)dtype, head_dim, head_dim_v, k_new, v_new, start_pos, n_tokens, kv_heads,
+                                  block_table, num_blocks, k_pool, v_pool, (hipStream_t)stream);
+  return hip_status(e, "kv_append launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,89 @@
+// Host-visible kernel argument blocks and launchers of libchunkattn.
+// Internal to the library: the public ABI is include/chunkattn.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace chunkattn {
+
+constexpr int kBlock = 64;                     // tokens per paged block == keys per KV tile
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+enum class DType : int { F32 = 0, BF16 = 1 };
+
+// One chunk of causal prefill over one sequence's cache.
+struct PrefillArgs {
+  const void* q;             // [chunk_len, heads, D]
+  const void* k;             // contiguous [cap, kv_heads, D] or paged pool
+  const void* v;
+  void* out;                 // [chunk_len, heads, DV]
+  float* lse;                // optional [heads, lse_stride] (column = token)
+  const int32_t* block_table;
+  float* ws_o;               // split partials [S][chunk_len*heads][DV]
+  float* ws_ml;              // split partials [S][chunk_len*heads][2]
+  int64_t past_len;
+  int64_t chunk_len;
+  int64_t kv_len;            // past_len + chunk_len
+  int64_t lse_stride;
+  int32_t heads, kv_heads, group;
+  int32_t num_blocks;
+  int32_t hpw;               // query heads per workgroup: 1, 2 or 4
+  int32_t n_tok_blocks;
+  int32_t n_head_groups;
+  int32_t num_splits;
+  int32_t xcd_remap;
+  float scale_log2;          // scale * log2(e)
+  // Varlen batch: one launch covers every prefill-path sequence.  Then q, out
+  // and lse point at the whole batch, block_table at [num_seqs, max_blocks],
+  // and each sequence's chunk_len / past_len come from the device arrays.
+  const int32_t* cu_seqlens_q;   // [num_seqs + 1]
+  const int32_t* kv_lens;        // [num_seqs]
+  const int64_t* wg_off;         // [num_seqs + 1] first workgroup of each sequence
+  int32_t num_seqs, max_blocks;
+};
+
+// Split-KV decode over a varlen batch (sequences with q_len * group <= 32).
+struct DecodeArgs {
+  const void* q;             // [total_q, heads, D]
+  const void* k;             // paged pools
+  const void* v;
+  const int32_t* block_tables;   // [num_seqs, max_blocks]
+  const int32_t* cu_seqlens_q;   // [num_seqs + 1]
+  const int32_t* kv_lens;        // [num_seqs]
+  int64_t* ws_off;               // [num_seqs] first partial slot of each sequence
+  int64_t* wg_off;               // [num_seqs + 1] first prefill workgroup of each sequence
+  float* ws_o;                   // [slots][DV]
+  float* ws_ml;                  // [slots][2]
+  void* out;                     // [total_q, heads, DV] (merge)
+  float* lse;                    // optional [heads, total_q] (merge)
+  int64_t total_q;
+  int64_t total_slots;           // partial slots the workspace holds (bound on every access)
+  int32_t num_seqs, max_blocks, num_blocks;
+  int32_t heads, kv_heads, group;
+  int32_t split_tokens;          // keys per split (multiple of 64)
+  int32_t tok_wg;                // query tokens per prefill workgroup
+  int32_t n_head_groups;         // prefill workgroups per token block
+  float scale_log2;
+};
+
+// Prefill launch: returns the HIP launch status.
+hipError_t launch_prefill(DType in, DType out, int D, int DV, bool paged, const PrefillArgs& a,
+                          int grid, hipStream_t stream);
+hipError_t launch_prefill_merge(DType out, int DV, const PrefillArgs& a, hipStream_t stream);
+hipError_t launch_prefill_varlen(int D, int DV, const PrefillArgs& a, int grid, hipStream_t stream);
+bool prefill_supported(DType in, DType out, int D, int DV);
+
+hipError_t launch_batch_plan(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode(int D, int DV, const DecodeArgs& a, int max_splits, hipStream_t stream);
+hipError_t launch_decode_merge(int DV, const DecodeArgs& a, hipStream_t stream);
+bool decode_supported(int D, int DV);
+
+hipError_t launch_kv_append(DType dt, int D, int DV, const void* k_new, const void* v_new,
+                            int64_t start_pos, int64_t n_tokens, int kv_heads,
+                            const int32_t* block_table, int num_blocks, void* k_pool, void* v_pool,
+                            hipStream_t stream);
+
+}  // namespace chunkattn

@@ -1,0 +1,205 @@
+/*
+ * libchunkattn — chunked-prefill causal attention for AMD Instinct MI355X
+ * (gfx950), behind a plain C ABI.
+ *
+ * The operation.  A chunk of `chunk_len` query tokens whose first token sits
+ * at absolute position `past_len` attends, under the causal mask, to the
+ * cached keys and values of every earlier position and of itself:
+ *
+ *   out[i, h, :] = sum_{j <= past_len + i} softmax_j(scale * q[i,h,:] . k[j,g,:]) v[j,g,:]
+ *   g = h / (heads / kv_heads)          (grouped-query heads, contiguous groups)
+ *
+ * Sources: "VPP: Virtual Pipeline Parallelism for Efficient Chunked Prefill in
+ * Long-Context LLM Inference", technical review (English edition):
+ *   §2.2 Eq. (1) (softmax(QK^T/sqrt(d))V) and the causal rule beside it;
+ *   §2.3 (a later chunk attends to all preceding chunks' KV cache);
+ *   §2.1 (prefill is compute-bound, decode reads the whole cache).
+ * "Revisiting Pipeline Parallelism for LLM Serving" notes, preliminaries on
+ * chunks: a batch can mix prefill tokens with one token per decode request.
+ * "GLM5.3 CyberSec W4A16 — parallel strategy and PP split" notes, §1 and §7:
+ * a paged KV pool of 64-token blocks, and attention that returns the LSE so
+ * partial results can be merged.
+ *
+ * Conventions for every call:
+ *  - Pointers named *_host are host memory; every other pointer is device
+ *    memory owned by the caller.  The library allocates no device memory and
+ *    keeps no device state; scratch space is passed in as `workspace`.
+ *  - Calls enqueue work on `stream` (a hipStream_t; NULL = the default
+ *    stream) and return without synchronising.
+ *  - Arguments are validated before any HIP call.  A rejected call returns a
+ *    negative ca_status, enqueues nothing and leaves a message for
+ *    chunkattn_last_error() (thread-local).  A failed launch returns
+ *    CA_EHIP with the HIP error text.  No call aborts or throws.
+ *  - Calls are thread-safe; calls that share output or workspace buffers on
+ *    one stream are ordered by the stream, on different streams they race.
+ *  - Device pointers must be 16-byte aligned.
+ *  - All strides are dense; layouts are given per argument below.
+ *
+ * KV cache layouts (B = CA_BLOCK_SIZE = 64 tokens, X = 16 / sizeof(element)):
+ *  - CA_KV_CONTIGUOUS: k [capacity, kv_heads, head_dim],
+ *                      v [capacity, kv_heads, head_dim_v]  (token-major).
+ *  - CA_KV_PAGED:      k pool [num_blocks, kv_heads, head_dim / X, B, X]
+ *                      v pool [num_blocks, kv_heads, B / X, head_dim_v, X]
+ *    Each (block, KV head) tile is one contiguous run of B*head_dim (K) or
+ *    B*head_dim_v (V) elements.  Inside a K tile, 16-byte runs of one token's
+ *    features are interleaved across the block's tokens; inside a V tile,
+ *    16-byte runs of consecutive tokens for one feature are interleaved across
+ *    features.  Logical token t of a sequence lives in physical block
+ *    block_table[t / B] at slot t % B.  chunkattn_kv_append() writes this
+ *    layout.  Block ids are clamped to [0, num_blocks) on the device, so a bad
+ *    table gives wrong numbers but never an access outside the pool.
+ */
+#ifndef CHUNKATTN_H
+#define CHUNKATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CA_BLOCK_SIZE 64
+#define CHUNKATTN_VERSION 1
+
+typedef enum {
+  CA_OK = 0,
+  CA_EINVAL = -1,        /* bad argument: null/misaligned pointer, bad size, bad scale */
+  CA_EUNSUPPORTED = -2,  /* valid but not implemented: head dims, dtype pair */
+  CA_ERANGE = -3,        /* past_len + chunk_len beyond the cache or block table */
+  CA_EWORKSPACE = -4,    /* workspace missing or smaller than required */
+  CA_EHIP = -5           /* the HIP runtime reported an error */
+} ca_status;
+
+typedef enum { CA_F32 = 0, CA_BF16 = 1 } ca_dtype;
+typedef enum { CA_KV_CONTIGUOUS = 0, CA_KV_PAGED = 1 } ca_kv_layout;
+
+/*
+ * Options of chunk_prefill_attn.  Initialise with ca_prefill_opts_init();
+ * passing NULL means the defaults below.
+ */
+typedef struct ca_prefill_opts {
+  ca_dtype dtype;              /* element type of q, k, v.  Default CA_BF16. */
+  ca_dtype out_dtype;          /* element type of out.  Default CA_BF16.
+                                  Supported pairs: (bf16, bf16), (bf16, f32), (f32, f32). */
+  int32_t head_dim_v;          /* value head dim; 0 = head_dim.  Must be <= head_dim. */
+  ca_kv_layout kv_layout;      /* default CA_KV_CONTIGUOUS */
+  int64_t kv_capacity;         /* contiguous: tokens allocated in k and v;
+                                  0 = exactly past_len + chunk_len */
+  const int32_t* block_table;  /* paged: device int32 [block_table_len] */
+  int32_t block_table_len;     /* paged: >= ceil((past_len + chunk_len) / 64) */
+  int32_t num_blocks;          /* paged: blocks in the pool */
+  float* lse_out;              /* optional device fp32 [heads, chunk_len]:
+                                  natural-log sum of exp(scale * logits) per row */
+  void* workspace;             /* device scratch for split-KV partials */
+  size_t workspace_bytes;
+  int32_t num_splits;          /* 0 = choose (never needs more workspace than
+                                  given; no workspace => no split); 1 = never
+                                  split; > 1 = exactly this many key splits
+                                  (capped at the number of key tiles) */
+} ca_prefill_opts;
+
+void ca_prefill_opts_init(ca_prefill_opts* opts);
+
+/*
+ * chunk_prefill_attn — one chunk of causal prefill attention (VPP review §2.2
+ * Eq. (1) with the causal rule, §2.3 chunked prefill).
+ *
+ *   q_chunk  [chunk_len, heads, head_dim]        dtype
+ *   k_cache, v_cache: layout per opts->kv_layout; the cache already holds the
+ *            chunk's own keys and values at positions [past_len, past_len+chunk_len)
+ *   out      [chunk_len, heads, head_dim_v]      out_dtype
+ *   past_len >= 0, chunk_len >= 0 (0 is a no-op; q_chunk and out may then be
+ *   NULL), heads % kv_heads == 0,
+ *   (head_dim, head_dim_v) in {(64, 64), (128, 128), (192, 128)},
+ *   scale finite and > 0 (1/sqrt(head_dim) in the usual case).
+ * Keys at positions >= past_len + chunk_len are never read for V and never
+ * influence any row; K/V beyond a row's own position do not change that row.
+ * The result is deterministic (bitwise) for fixed arguments and split count.
+ */
+ca_status chunk_prefill_attn(const void* q_chunk, const void* k_cache, const void* v_cache,
+                             int64_t past_len, int64_t chunk_len,
+                             int32_t heads, int32_t kv_heads, int32_t head_dim, float scale,
+                             void* out, const ca_prefill_opts* opts, void* stream);
+
+/*
+ * Workspace bytes chunk_prefill_attn needs for `num_splits` key splits
+ * (0 for num_splits <= 1).
+ */
+size_t chunkattn_prefill_workspace_size(int64_t chunk_len, int32_t heads, int32_t head_dim_v,
+                                        int32_t num_splits);
+
+/*
+ * The split count chunk_prefill_attn picks for num_splits = 0 when the
+ * workspace is large enough (1 = no split).  Splitting pays when the chunk
+ * is short but its prefix is long: too few workgroups would hold the GPU.
+ * Returns 0 for invalid sizes.
+ */
+int32_t chunkattn_prefill_auto_splits(int64_t past_len, int64_t chunk_len, int32_t heads, int32_t kv_heads);
+
+/*
+ * chunk_attn_varlen — one batch mixing prefill chunks and decode requests
+ * over a paged KV pool (Revisiting Pipeline Parallelism for LLM Serving,
+ * preliminaries: prefill requests contribute many tokens, decode requests one;
+ * VPP review §2.1: decode reads the whole cache).
+ *
+ * Sequence s owns query rows [cu_seqlens_q[s], cu_seqlens_q[s+1]) of q and
+ * out; its kv_lens[s] cached tokens include those rows' own keys, so its
+ * queries sit at positions kv_lens[s] - q_len_s .. kv_lens[s] - 1.
+ *   q            [total_q, heads, head_dim] bf16,  out [total_q, heads, head_dim_v] bf16
+ *   k_pool, v_pool  paged layout above (bf16)
+ *   block_tables [num_seqs, max_blocks_per_seq] device int32
+ *   cu_seqlens_q [num_seqs + 1], kv_lens [num_seqs]   device int32
+ *   cu_seqlens_q_host, kv_lens_host                   the same values in host memory
+ *                (used only to size and plan launches; they must equal the device
+ *                copies — if they do not, results are undefined, but every kernel
+ *                still keeps its reads and writes inside the buffers described here)
+ *   lse_out      optional device fp32 [heads, total_q]
+ *   workspace    device scratch of chunkattn_varlen_workspace_size() bytes
+ *                (256-byte aligned; needed whenever the batch has query rows)
+ * Requires q_len_s <= kv_lens[s] <= 64 * max_blocks_per_seq for every
+ * sequence (q_len_s = 0 is allowed and skipped), 1 <= num_seqs <= 65535 and
+ * (head_dim, head_dim_v) in {(64, 64), (128, 128), (192, 128)}.  A sequence
+ * whose rows per KV head, q_len_s * (heads / kv_heads), are at most 32 takes
+ * the split-KV decode path; longer ones take the prefill path.  Both write
+ * straight into out.
+ */
+ca_status chunk_attn_varlen(const void* q, const void* k_pool, const void* v_pool,
+                            const int32_t* block_tables, int32_t max_blocks_per_seq,
+                            int32_t num_blocks,
+                            const int32_t* cu_seqlens_q, const int32_t* kv_lens,
+                            const int32_t* cu_seqlens_q_host, const int32_t* kv_lens_host,
+                            int32_t num_seqs, int32_t heads, int32_t kv_heads,
+                            int32_t head_dim, int32_t head_dim_v, float scale,
+                            void* out, float* lse_out,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes chunk_attn_varlen needs for this batch (host arrays). */
+size_t chunkattn_varlen_workspace_size(const int32_t* cu_seqlens_q_host, const int32_t* kv_lens_host,
+                                       int32_t num_seqs, int32_t heads, int32_t kv_heads,
+                                       int32_t head_dim_v);
+
+/*
+ * chunkattn_kv_append — write n_tokens new keys/values of one sequence into
+ * the paged pool at logical positions [start_pos, start_pos + n_tokens)
+ * (the cache write that precedes each chunk's attention, VPP review §2.3).
+ *   k_new [n_tokens, kv_heads, head_dim], v_new [n_tokens, kv_heads, head_dim_v]
+ *   block_table [block_table_len] device int32, covering start_pos + n_tokens.
+ * Bitwise copy; no arithmetic.  Block ids are clamped to [0, num_blocks).
+ */
+ca_status chunkattn_kv_append(const void* k_new, const void* v_new, int64_t start_pos, int64_t n_tokens,
+                              int32_t kv_heads, int32_t head_dim, int32_t head_dim_v, ca_dtype dtype,
+                              const int32_t* block_table, int32_t block_table_len, int32_t num_blocks,
+                              void* k_pool, void* v_pool, void* stream);
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char* chunkattn_last_error(void);
+
+/* CHUNKATTN_VERSION of the built library. */
+int32_t chunkattn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CHUNKATTN_H */

@@ -1,0 +1,231 @@
+"""GPU parity of the chunked-prefill path against the fp64 oracle (small and mid sizes).
+
+Every case compares the HIP kernels, called through the C ABI, element by
+element with the oracle on identical seeded inputs.  Tolerances: max abs
+error <= 1e-4 for fp32 inputs, <= 1.5e-2 for bf16 inputs with fp32
+accumulation; LSE (fp32) within 1e-3.  Sizes span several 64-key tiles and
+ragged tails; the edge cases cover chunk lengths around tile edges, offsets
+that are not multiples of 64, uneven last chunks, GQA ratios 1..8 and every
+supported head-dim pair.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from chunked_prefill_causal_amd import _lib as L
+from chunked_prefill_causal_amd import inputs
+
+from gpu_common import (BF16_TOL, F32_TOL, LSE_TOL, Pool, log, max_err, oracle_chunk, require_gpu,
+                        seq_kv, single_seq_pool, torch_dtype)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _gpu():
+    require_gpu()
+
+
+# ---------------------------------------------------------------- cache write --
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_kv_append_layout_bitwise(dtype):
+    """The pool layout written by the cache-write kernel, restated in torch."""
+    hkv, d, dv, n = 3, 64, 64, 200
+    k, v = seq_kv(n, hkv, d, dv, dtype, 11)
+    needed = math.ceil(n / 64)
+    table = torch.from_numpy(inputs.block_table(needed, 12)).cuda()
+    pool = Pool(inputs.pool_size(needed), hkv, d, dv, torch_dtype(dtype), poison=True)
+    pool.append(k[:37], v[:37], table, 0)          # unaligned split of the append
+    pool.append(k[37:], v[37:], table, 37)
+    torch.cuda.synchronize()
+    x = L.elems_per_16b(torch_dtype(dtype))
+    kp, vp = pool.k.cpu(), pool.v.cpu()
+    tab = table.cpu().numpy()
+    for t in range(n):
+        blk, slot = tab[t // 64], t % 64
+        for g in range(hkv):
+            kt = kp[blk, g, :, slot, :].reshape(-1)
+            assert torch.equal(kt.view(torch.int16 if dtype == "bf16" else torch.int32),
+                               k[t, g].view(torch.int16 if dtype == "bf16" else torch.int32))
+            vt = vp[blk, g, slot // x, :, slot % x]
+            assert torch.equal(vt.view(torch.int16 if dtype == "bf16" else torch.int32),
+                               v[t, g].view(torch.int16 if dtype == "bf16" else torch.int32))
+    # slots past the sequence end in its last block stay untouched (NaN)
+    last = tab[(n - 1) // 64]
+    assert torch.isnan(kp[last, :, :, n % 64:, :].float()).all()
+
+
+# ------------------------------------------------------------------ tiny fp32 --
+
+def test_tiny_f32_workload_all_rows():
+    """L=2048 as 4 chunks of 512, 8 heads, d=64, fp32, contiguous KV; every row."""
+    w = inputs.WORKLOADS["tiny_f32"]
+    k, v = seq_kv(w.seq_len, w.kv_heads, w.head_dim, w.head_dim_v, "f32", w.seed + 1)
+    kd, vd = k.cuda(), v.cuda()
+    for c in range(w.n_chunks):
+        past = c * w.chunk_len
+        q = inputs.normal((w.chunk_len, w.heads, w.head_dim), inputs.chunk_seeds(w, c), "f32")
+        out, lse = L.chunk_prefill_attn(q.cuda(), kd, vd, past, w.scale, return_lse=True)
+        ref, ref_lse = oracle_chunk(q, k[: past + w.chunk_len], v[: past + w.chunk_len], past, w.scale)
+        e, el = max_err(out, ref), max_err(lse, ref_lse)
+        log(f"tiny_f32 chunk {c}: max err {e:.2e}, lse err {el:.2e}")
+        assert e <= F32_TOL and el <= LSE_TOL
+
+
+# ------------------------------------------------------- bf16 prefill, edges --
+
+CASES = [
+    # (chunk_len, past_len, heads, kv_heads, d, dv, layout)
+    (1, 0, 8, 8, 128, 128, "paged"),
+    (63, 0, 8, 2, 128, 128, "paged"),
+    (64, 64, 32, 8, 128, 128, "paged"),
+    (65, 37, 32, 8, 128, 128, "paged"),
+    (127, 200, 6, 3, 128, 128, "paged"),
+    (129, 1000, 8, 1, 128, 128, "paged"),
+    (300, 333, 16, 16, 64, 64, "paged"),
+    (257, 700, 4, 4, 192, 128, "paged"),
+    (512, 1536, 64, 8, 128, 128, "paged"),
+    (130, 70, 32, 8, 128, 128, "contiguous"),
+    (200, 111, 5, 5, 64, 64, "contiguous"),
+    (96, 450, 8, 4, 192, 128, "contiguous"),
+]
+
+
+@pytest.mark.parametrize("c,past,hq,hkv,d,dv,layout", CASES)
+def test_prefill_bf16_vs_oracle(c, past, hq, hkv, d, dv, layout):
+    seed = 1000 + c + past + hq * 7 + d
+    n = past + c
+    k, v = seq_kv(n, hkv, d, dv, "bf16", seed)
+    q = inputs.normal((c, hq, d), seed + 5, "bf16")
+    scale = 1.0 / math.sqrt(d)
+    log(f"prefill case c={c} past={past} heads={hq}/{hkv} d={d}/{dv} {layout}")
+    if layout == "paged":
+        pool, table = single_seq_pool(k, v, seed + 9)
+        out, lse = L.chunk_prefill_attn(q.cuda(), pool.k, pool.v, past, scale, kv_layout="paged",
+                                        block_table=table, return_lse=True, num_splits=1)
+    else:
+        cap = n + 17   # capacity beyond kv_len holds NaN that must never be read
+        kc = torch.full((cap, hkv, d), float("nan"), dtype=torch.bfloat16)
+        vc = torch.full((cap, hkv, dv), float("nan"), dtype=torch.bfloat16)
+        kc[:n], vc[:n] = k, v
+        out, lse = L.chunk_prefill_attn(q.cuda(), kc.cuda(), vc.cuda(), past, scale, return_lse=True,
+                                        num_splits=1)
+    ref, ref_lse = oracle_chunk(q, k, v, past, scale)
+    e, el = max_err(out, ref), max_err(lse, ref_lse)
+    log(f"  max err {e:.3e}  lse err {el:.2e}")
+    assert e <= BF16_TOL and el <= LSE_TOL
+
+
+def test_prefill_bf16_fp32_output():
+    c, past, hq, hkv, d = 200, 300, 16, 4, 128
+    k, v = seq_kv(past + c, hkv, d, d, "bf16", 77)
+    q = inputs.normal((c, hq, d), 78, "bf16")
+    pool, table = single_seq_pool(k, v, 79)
+    out = L.chunk_prefill_attn(q.cuda(), pool.k, pool.v, past, 1 / math.sqrt(d), kv_layout="paged",
+                               block_table=table, out_dtype=torch.float32)
+    ref, _ = oracle_chunk(q, k, v, past, 1 / math.sqrt(d))
+    e = max_err(out, ref)
+    log(f"bf16 in / fp32 out: max err {e:.3e}")
+    assert out.dtype == torch.float32 and e <= BF16_TOL / 2
+
+
+@pytest.mark.parametrize("splits", [2, 3, 7, 0])
+def test_split_kv_vs_oracle(splits):
+    """Forced key splits + LSE merge; 0 lets the library choose (short chunk, long prefix)."""
+    c, past, hq, hkv, d = 70, 5000, 8, 2, 128
+    k, v = seq_kv(past + c, hkv, d, d, "bf16", 88)
+    q = inputs.normal((c, hq, d), 89, "bf16")
+    pool, table = single_seq_pool(k, v, 90)
+    out, lse = L.chunk_prefill_attn(q.cuda(), pool.k, pool.v, past, 1 / math.sqrt(d), kv_layout="paged",
+                                    block_table=table, return_lse=True, num_splits=splits)
+    ref, ref_lse = oracle_chunk(q, k, v, past, 1 / math.sqrt(d))
+    e, el = max_err(out, ref), max_err(lse, ref_lse)
+    log(f"splits={splits} (auto picks {L.chunkattn_prefill_auto_splits(past, c, hq, hkv)}): err {e:.3e} lse {el:.2e}")
+    assert e <= BF16_TOL and el <= LSE_TOL
+
+
+# ------------------------------------------------------------- invariants ----
+
+def _paged_run(q, pool, table, past, d, **kw):
+    return L.chunk_prefill_attn(q, pool.k, pool.v, past, 1 / math.sqrt(d), kv_layout="paged",
+                                block_table=table, **kw)
+
+
+def test_paged_equals_contiguous_bitwise():
+    c, past, hq, hkv, d = 160, 390, 16, 4, 128
+    k, v = seq_kv(past + c, hkv, d, d, "bf16", 101)
+    q = inputs.normal((c, hq, d), 102, "bf16").cuda()
+    pool, table = single_seq_pool(k, v, 103)
+    a = _paged_run(q, pool, table, past, d, num_splits=1)
+    b = L.chunk_prefill_attn(q, k.cuda(), v.cuda(), past, 1 / math.sqrt(d), num_splits=1)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_deterministic_bitwise():
+    c, past, hq, hkv, d = 300, 900, 32, 8, 128
+    k, v = seq_kv(past + c, hkv, d, d, "bf16", 111)
+    q = inputs.normal((c, hq, d), 112, "bf16").cuda()
+    pool, table = single_seq_pool(k, v, 113)
+    for splits in (1, 3):
+        a = _paged_run(q, pool, table, past, d, num_splits=splits)
+        b = _paged_run(q, pool, table, past, d, num_splits=splits)
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_chunks_equal_single_pass_bitwise():
+    """Concatenated chunk outputs equal one causal pass over the whole prompt."""
+    n, hq, hkv, d = 1000, 8, 2, 128
+    k, v = seq_kv(n, hkv, d, d, "bf16", 121)
+    q = inputs.normal((n, hq, d), 122, "bf16").cuda()
+    pool, table = single_seq_pool(k, v, 123)
+    full = _paged_run(q, pool, table, 0, d, num_splits=1)
+    for bounds in ([0, 256, 512, 768, 1000], [0, 300, 600, 1000], [0, 1, 65, 1000]):
+        parts = [_paged_run(q[a:b].contiguous(), pool, table, a, d, num_splits=1)
+                 for a, b in zip(bounds[:-1], bounds[1:])]
+        assert torch.equal(torch.cat(parts).view(torch.int16), full.view(torch.int16)), bounds
+
+
+def test_rows_ignore_future_kv_bitwise():
+    """Rewriting K/V past the chunk end (finite junk or NaN) changes no output bit."""
+    c, past, hq, hkv, d = 100, 150, 8, 2, 128
+    n = past + c
+    k, v = seq_kv(n + 200, hkv, d, d, "bf16", 131)
+    q = inputs.normal((c, hq, d), 132, "bf16").cuda()
+    needed = math.ceil((n + 200) / 64)
+    table = torch.from_numpy(inputs.block_table(needed, 133)).cuda()
+    outs = []
+    for fill in ("data", "junk", "nan"):
+        pool = Pool(inputs.pool_size(needed), hkv, d, d, torch.bfloat16, poison=True)
+        kk, vv = k.clone(), v.clone()
+        if fill == "junk":
+            kk[n:] = inputs.normal(kk[n:].shape, 134, "bf16") * 9
+            vv[n:] = inputs.normal(vv[n:].shape, 135, "bf16") * 9
+        elif fill == "nan":
+            kk[n:] = float("nan")
+            vv[n:] = float("nan")
+        pool.append(kk, vv, table)
+        outs.append(_paged_run(q, pool, table, past, d, num_splits=1))
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
+    assert torch.equal(outs[0].view(torch.int16), outs[2].view(torch.int16))
+
+
+def test_zero_length_chunk_is_noop():
+    q = torch.empty((0, 8, 128), dtype=torch.bfloat16, device="cuda")
+    k = torch.zeros((64, 8, 128), dtype=torch.bfloat16, device="cuda")
+    out = L.chunk_prefill_attn(q, k, k, 10, 0.1)
+    assert out.shape == (0, 8, 128)
+
+
+def test_rejected_arguments_raise():
+    q = torch.zeros((4, 8, 128), dtype=torch.bfloat16, device="cuda")
+    k = torch.zeros((1024, 8, 128), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(L.ChunkAttnError) as e:
+        L.chunk_prefill_attn(q, k, k, 1021, 0.1)        # 1025 tokens > capacity 1024
+    assert e.value.status == L.CA_ERANGE
+    with pytest.raises(L.ChunkAttnError) as e:           # 8 key tiles, 4 splits, 16-byte workspace
+        L.chunk_prefill_attn(q, k, k, 500, 0.1, num_splits=4,
+                             workspace=torch.empty(16, dtype=torch.uint8, device="cuda"))
+    assert e.value.status == L.CA_EWORKSPACE

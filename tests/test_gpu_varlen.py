@@ -1,0 +1,98 @@
+"""GPU parity of the mixed prefill + decode batch (varlen entry) against the fp64 oracle.
+
+A batch mixes prefill chunks (many query tokens at an offset) with decode
+requests (one query token, or a few, reading the whole cache), as in the
+notes on "Revisiting Pipeline Parallelism for LLM Serving" (preliminaries).
+Each sequence owns its own blocks of one shared paged pool; every output row
+and every LSE value is compared with the oracle run on that sequence alone.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from chunked_prefill_causal_amd import _lib as L
+from chunked_prefill_causal_amd import inputs
+
+from gpu_common import BF16_TOL, LSE_TOL, Pool, log, max_err, oracle_chunk, require_gpu, seq_kv
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _gpu():
+    require_gpu()
+
+
+def build_batch(q_lens, kv_lens, hq, hkv, d, dv, seed, poison=True):
+    """Per-sequence seeded K/V and queries placed in one pool with disjoint random blocks."""
+    n = len(q_lens)
+    max_blocks = max(math.ceil(k / 64) for k in kv_lens)
+    needed = [math.ceil(k / 64) for k in kv_lens]
+    total = sum(needed)
+    pool_blocks = inputs.pool_size(total)
+    perm = inputs.block_table(total, seed, pool_blocks)
+    pool = Pool(pool_blocks, hkv, d, dv, torch.bfloat16, poison=poison)
+    tables = np.zeros((n, max_blocks), dtype=np.int32)
+    seqs = []
+    off = 0
+    for s in range(n):
+        tables[s, : needed[s]] = perm[off: off + needed[s]]
+        off += needed[s]
+        k, v = seq_kv(kv_lens[s], hkv, d, dv, "bf16", seed + 10 * s + 1)
+        q = inputs.normal((q_lens[s], hq, d), seed + 10 * s + 5, "bf16")
+        seqs.append((q, k, v))
+    tables_d = torch.from_numpy(tables).cuda()
+    for s in range(n):
+        pool.append(seqs[s][1], seqs[s][2], tables_d[s])
+    cu = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
+    q_all = torch.cat([x[0] for x in seqs]) if cu[-1] else torch.empty((0, hq, d), dtype=torch.bfloat16)
+    return pool, tables_d, cu, q_all, seqs
+
+
+def check_batch(q_lens, kv_lens, hq, hkv, d, dv, seed):
+    pool, tables, cu, q_all, seqs = build_batch(q_lens, kv_lens, hq, hkv, d, dv, seed)
+    scale = 1.0 / math.sqrt(d)
+    out, lse = L.chunk_attn_varlen(q_all.cuda(), pool.k, pool.v, tables, cu, kv_lens, scale, return_lse=True)
+    worst, worst_lse = 0.0, 0.0
+    for s, (q, k, v) in enumerate(seqs):
+        if q_lens[s] == 0:
+            continue
+        ref, ref_lse = oracle_chunk(q, k, v, kv_lens[s] - q_lens[s], scale)
+        worst = max(worst, max_err(out[cu[s]: cu[s + 1]], ref))
+        worst_lse = max(worst_lse, max_err(lse[:, cu[s]: cu[s + 1]], ref_lse))
+    log(f"varlen q_lens={q_lens[:6]}... kv_lens={kv_lens[:6]}...: max err {worst:.3e}, lse {worst_lse:.2e}")
+    assert worst <= BF16_TOL and worst_lse <= LSE_TOL
+
+
+def test_mixed_small():
+    check_batch([200, 1, 1, 1, 1], [1300, 1, 64, 65, 3000], 32, 8, 128, 128, 5000)
+
+
+def test_decode_only_ragged_contexts():
+    rng = np.random.default_rng(3)
+    kv = rng.integers(1, 5000, size=24).tolist()
+    check_batch([1] * 24, kv, 32, 8, 128, 128, 5100)
+
+
+def test_short_multi_token_rows_take_decode_path():
+    """q_len * group <= 32 rides the split-KV path with a causal mask inside the group."""
+    check_batch([2, 8, 3, 40], [900, 2100, 3, 600], 16, 4, 128, 128, 5200)
+
+
+def test_mixed_mha_d64_and_mla_dims():
+    check_batch([130, 1, 1], [500, 777, 64], 8, 8, 64, 64, 5300)
+    check_batch([100, 1, 1], [300, 1000, 129], 4, 4, 192, 128, 5400)
+
+
+def test_empty_sequences_are_skipped():
+    check_batch([0, 1, 0, 70, 1], [10, 10, 5, 100, 2000], 8, 2, 128, 128, 5500)
+
+
+def test_lse_and_out_rows_untouched_outside_batch_rows():
+    """The output of a batch holds exactly total_q rows; nothing else is written."""
+    pool, tables, cu, q_all, seqs = build_batch([1, 1], [100, 200], 8, 2, 128, 128, 5600)
+    out = torch.full((4, 8, 128), 7.0, dtype=torch.bfloat16, device="cuda")
+    L.chunk_attn_varlen(q_all.cuda(), pool.k, pool.v, tables, cu, [100, 200], 0.1, out=out[:2])
+    assert torch.all(out[2:] == 7.0)
