@@ -1,0 +1,150 @@
+"""The C ABI on the CPU: the library loads, exports what the header declares,
+and rejects bad arguments before any HIP call (so these run without a GPU).
+
+Pointers handed to rejected calls are fake (never dereferenced): validation
+must fail before a single byte of device memory is touched.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from chunked_prefill_causal_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "chunkattn.h")
+FAKE = 1 << 20          # 16-byte aligned, never dereferenced
+MISALIGNED = FAKE + 4
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_binding_surface():
+    assert declared_functions() == sorted(L.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = L.lib()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_defaults():
+    assert L.version() == 1
+    o = L.PrefillOpts()
+    o.num_splits = 7
+    L.lib().ca_prefill_opts_init(ctypes.byref(o))
+    assert (o.dtype, o.out_dtype, o.kv_layout, o.num_splits, o.head_dim_v) == (L.CA_BF16, L.CA_BF16,
+                                                                                L.CA_KV_CONTIGUOUS, 0, 0)
+    assert ctypes.sizeof(L.PrefillOpts) == 72
+
+
+def prefill(q=FAKE, k=FAKE, v=FAKE, past=0, c=4, hq=8, hkv=8, d=128, scale=0.1, out=FAKE, opts=None):
+    return L.lib().chunk_prefill_attn(q, k, v, past, c, hq, hkv, d, scale, out,
+                                      None if opts is None else ctypes.byref(opts), None)
+
+
+def opts(**kw):
+    o = L.PrefillOpts()
+    L.lib().ca_prefill_opts_init(ctypes.byref(o))
+    for key, val in kw.items():
+        setattr(o, key, val)
+    return o
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(k=None), L.CA_EINVAL),
+    (dict(q=None), L.CA_EINVAL),
+    (dict(q=MISALIGNED), L.CA_EINVAL),
+    (dict(past=-1), L.CA_EINVAL),
+    (dict(c=-5), L.CA_EINVAL),
+    (dict(hq=8, hkv=3), L.CA_EINVAL),
+    (dict(hkv=0), L.CA_EINVAL),
+    (dict(scale=0.0), L.CA_EINVAL),
+    (dict(scale=float("inf")), L.CA_EINVAL),
+    (dict(scale=float("nan")), L.CA_EINVAL),
+    (dict(d=96), L.CA_EUNSUPPORTED),
+    (dict(d=192), L.CA_EUNSUPPORTED),                                   # needs head_dim_v = 128
+    (dict(opts=opts(dtype=L.CA_F32, out_dtype=L.CA_BF16)), L.CA_EUNSUPPORTED),
+    (dict(opts=opts(dtype=7)), L.CA_EINVAL),
+    (dict(opts=opts(kv_layout=9)), L.CA_EINVAL),
+    (dict(opts=opts(kv_capacity=3)), L.CA_ERANGE),
+    (dict(past=(1 << 30), c=1), L.CA_ERANGE),
+    (dict(opts=opts(kv_layout=L.CA_KV_PAGED)), L.CA_EINVAL),            # no block table
+    (dict(opts=opts(kv_layout=L.CA_KV_PAGED, block_table=FAKE, block_table_len=1, num_blocks=4), past=61),
+     L.CA_ERANGE),                                                       # 65 tokens, 1 block
+    (dict(opts=opts(kv_layout=L.CA_KV_PAGED, block_table=FAKE, block_table_len=1, num_blocks=0)),
+     L.CA_EINVAL),
+    (dict(opts=opts(num_splits=-1)), L.CA_EINVAL),
+    (dict(opts=opts(num_splits=4), past=1000, c=24), L.CA_EWORKSPACE),  # no workspace given
+    (dict(opts=opts(num_splits=4, workspace=FAKE, workspace_bytes=16), past=1000, c=24), L.CA_EWORKSPACE),
+    (dict(opts=opts(lse_out=FAKE + 2)), L.CA_EINVAL),
+])
+def test_prefill_rejections(kwargs, status):
+    assert prefill(**kwargs) == status
+    assert L.lib().chunkattn_last_error().decode()
+
+
+def test_zero_length_chunk_succeeds_without_touching_memory():
+    assert prefill(q=None, out=None, c=0) == L.CA_OK
+    assert L.lib().chunkattn_last_error().decode() == ""
+
+
+def test_workspace_queries():
+    assert L.chunkattn_prefill_workspace_size(100, 8, 128, 1) == 0
+    need = L.chunkattn_prefill_workspace_size(100, 8, 128, 3)
+    assert need >= 3 * 100 * 8 * (128 + 2) * 4
+    assert L.chunkattn_prefill_auto_splits(0, 16384, 64, 8) == 1        # big chunk: no split
+    assert L.chunkattn_prefill_auto_splits(100000, 64, 8, 2) > 1         # short chunk, long prefix
+    assert L.chunkattn_prefill_auto_splits(-1, 4, 8, 8) == 0
+    assert L.chunkattn_varlen_workspace_size([0, 1, 3], [100, 50], 8, 2, 128) > 0
+
+
+def varlen(q=FAKE, cu=(0, 1, 2), kv=(10, 20), hq=8, hkv=2, d=128, dv=128, ws=FAKE, ws_bytes=1 << 30,
+           max_blocks=4, num_blocks=8, scale=0.1, out=FAKE, k=FAKE):
+    cu_a = (ctypes.c_int32 * len(cu))(*cu)
+    kv_a = (ctypes.c_int32 * len(kv))(*kv)
+    return L.lib().chunk_attn_varlen(q, k, FAKE, FAKE, max_blocks, num_blocks, FAKE, FAKE,
+                                     ctypes.addressof(cu_a), ctypes.addressof(kv_a), len(kv), hq, hkv, d, dv,
+                                     scale, out, None, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(k=None), L.CA_EINVAL),
+    (dict(q=None), L.CA_EINVAL),
+    (dict(cu=(1, 2, 3)), L.CA_EINVAL),                 # cu[0] != 0
+    (dict(cu=(0, 2, 1)), L.CA_EINVAL),                 # decreasing
+    (dict(kv=(0, 20)), L.CA_EINVAL),                   # kv_len below q_len
+    (dict(kv=(10, 300)), L.CA_ERANGE),                 # 300 tokens > 4 blocks of 64
+    (dict(hq=8, hkv=3), L.CA_EINVAL),
+    (dict(d=128, dv=64), L.CA_EUNSUPPORTED),
+    (dict(ws=None), L.CA_EWORKSPACE),
+    (dict(ws_bytes=64), L.CA_EWORKSPACE),
+    (dict(ws=FAKE + 16), L.CA_EINVAL),                 # workspace must be 256-byte aligned
+    (dict(scale=-1.0), L.CA_EINVAL),
+    (dict(max_blocks=0), L.CA_EINVAL),
+])
+def test_varlen_rejections(kwargs, status):
+    assert varlen(**kwargs) == status
+
+
+def test_varlen_empty_batch_succeeds():
+    assert varlen(q=None, out=None, cu=(0, 0, 0), kv=(5, 9), ws=None) == L.CA_OK
+
+
+def test_kv_append_rejections():
+    lib = L.lib()
+    f = lambda **kw: lib.chunkattn_kv_append(kw.get("k", FAKE), FAKE, kw.get("start", 0), kw.get("n", 10), 2,
+                                             kw.get("d", 128), 128, kw.get("dt", L.CA_BF16), FAKE,
+                                             kw.get("tl", 1), 4, FAKE, FAKE, None)
+    assert f(k=None) == L.CA_EINVAL
+    assert f(start=-1) == L.CA_EINVAL
+    assert f(d=100) == L.CA_EUNSUPPORTED
+    assert f(dt=5) == L.CA_EINVAL
+    assert f(start=60, n=10) == L.CA_ERANGE
+    assert f(n=0) == L.CA_OK
