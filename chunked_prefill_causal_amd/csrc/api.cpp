@@ -43,9 +43,16 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 constexpr int kNumCUs = 256;          // MI355X
 constexpr int64_t kMaxTokens = (int64_t)1 << 30;
 
-// Largest of 4, 2, 1 that divides the GQA group: that many query heads of one
-// KV head share a prefill workgroup (128 query rows in total).
-int heads_per_wg(int group) { return group % 4 == 0 ? 4 : (group % 2 == 0 ? 2 : 1); }
+// Query heads of one KV head that share a prefill workgroup: the largest
+// power of two up to the workgroup's wave count dividing the GQA group.  The
+// 4-wave kernel (contiguous or fp32 caches) holds 128 query rows, the 8-wave
+// paged bf16 kernel 256.
+int heads_per_wg(int group, int waves) {
+  for (int h = waves; h > 1; h >>= 1)
+    if (group % h == 0) return h;
+  return 1;
+}
+constexpr int kWavesSmall = 4, kWavesPaged = 8;
 
 size_t prefill_ws_bytes(int64_t chunk_len, int heads, int dv, int splits) {
   if (splits <= 1) return 0;
@@ -85,8 +92,8 @@ struct BatchPlan {
 BatchPlan plan_batch(const int32_t* cu, const int32_t* kv, int num_seqs, int heads, int kv_heads, int dv) {
   BatchPlan p;
   const int group = heads / kv_heads;
-  const int hpw = heads_per_wg(group);
-  const int tok_wg = 128 / hpw;
+  const int hpw = heads_per_wg(group, kWavesPaged);
+  const int tok_wg = 256 / hpw;
   p.split_tokens = decode_split_tokens(cu, kv, num_seqs, kv_heads, group);
   for (int s = 0; s < num_seqs; ++s) {
     const int q_len = cu[s + 1] - cu[s];
@@ -107,14 +114,15 @@ BatchPlan plan_batch(const int32_t* cu, const int32_t* kv, int num_seqs, int hea
   return p;
 }
 
-// Split count for a short chunk over a long prefix: enough workgroups for
-// about four per CU, each split keeping at least 16 key tiles.
+// Split count for a short chunk over a long prefix (sized for the 8-wave
+// paged kernel, one workgroup per CU): enough workgroups for about two per
+// CU, each split keeping at least 16 key tiles.
 int auto_splits(int64_t past_len, int64_t chunk_len, int heads, int kv_heads) {
-  const int hpw = heads_per_wg(heads / kv_heads);
-  const int64_t base = (chunk_len + 128 / hpw - 1) / (128 / hpw) * (heads / hpw);
+  const int hpw = heads_per_wg(heads / kv_heads, kWavesPaged);
+  const int64_t base = (chunk_len + 256 / hpw - 1) / (256 / hpw) * (heads / hpw);
   const int64_t n_tiles = (past_len + chunk_len + kBlock - 1) / kBlock;
-  if (base == 0 || base >= 2 * kNumCUs || n_tiles < 32) return 1;
-  int64_t want = (4 * kNumCUs + base - 1) / base;
+  if (base == 0 || base >= kNumCUs || n_tiles < 32) return 1;
+  int64_t want = (2 * kNumCUs + base - 1) / base;
   const int64_t cap = n_tiles / 16;
   if (want > cap) want = cap;
   return want > 1 ? (int)want : 1;
@@ -192,8 +200,9 @@ ca_status chunk_prefill_attn(const void* q, const void* k, const void* v, int64_
   if (o.num_splits < 0) return fail(CA_EINVAL, "num_splits must be >= 0");
 
   const int group = heads / kv_heads;
-  const int hpw = heads_per_wg(group);
-  const int tok_wg = 128 / hpw;
+  const bool use_paged_kernel = paged && din == DType::BF16 && prefill_paged_supported(head_dim, dv);
+  const int hpw = heads_per_wg(group, use_paged_kernel ? kWavesPaged : kWavesSmall);
+  const int tok_wg = (use_paged_kernel ? 256 : 128) / hpw;
   const int64_t n_tb = (chunk_len + tok_wg - 1) / tok_wg;
   const int n_hg = heads / hpw;
   const int64_t base = n_tb * n_hg;
@@ -241,7 +250,8 @@ ca_status chunk_prefill_attn(const void* q, const void* k, const void* v, int64_
     a.ws_ml = (float*)((char*)o.workspace + align_up(rows * dv * sizeof(float), 256));
   }
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e = launch_prefill(din, dout, head_dim, dv, paged, a, (int)(base * splits), s);
+  hipError_t e = use_paged_kernel ? launch_prefill_paged(dout, head_dim, dv, a, (int)(base * splits), s)
+                                  : launch_prefill(din, dout, head_dim, dv, paged, a, (int)(base * splits), s);
   if (e != hipSuccess) return hip_status(e, "prefill launch");
   if (splits > 1) {
     e = launch_prefill_merge(dout, dv, a, s);
@@ -298,7 +308,7 @@ ca_status chunk_attn_varlen(const void* q, const void* k_pool, const void* v_poo
 
   hipStream_t st = (hipStream_t)stream;
   const float cs = scale * kLog2e;
-  const int hpw = heads_per_wg(group);
+  const int hpw = heads_per_wg(group, kWavesPaged);
   char* ws = (char*)workspace;
   DecodeArgs d{};
   d.q = q;
@@ -322,7 +332,7 @@ ca_status chunk_attn_varlen(const void* q, const void* k_pool, const void* v_poo
   d.kv_heads = kv_heads;
   d.group = group;
   d.split_tokens = plan.split_tokens;
-  d.tok_wg = 128 / hpw;
+  d.tok_wg = 256 / hpw;
   d.n_head_groups = heads / hpw;
   d.scale_log2 = cs;
   hipError_t e = launch_batch_plan(d, st);
@@ -351,7 +361,7 @@ ca_status chunk_attn_varlen(const void* q, const void* k_pool, const void* v_poo
     a.wg_off = d.wg_off;
     a.num_seqs = num_seqs;
     a.max_blocks = max_blocks;
-    e = launch_prefill_varlen(head_dim, head_dim_v, a, (int)plan.prefill_wgs, st);
+    e = launch_prefill_paged_varlen(head_dim, head_dim_v, a, (int)plan.prefill_wgs, st);
     if (e != hipSuccess) return hip_status(e, "varlen prefill launch");
   }
   if (plan.n_decode) {

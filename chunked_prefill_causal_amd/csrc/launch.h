@@ -30,7 +30,7 @@ struct PrefillArgs {
   int64_t lse_stride;
   int32_t heads, kv_heads, group;
   int32_t num_blocks;
-  int32_t hpw;               // query heads per workgroup: 1, 2 or 4
+  int32_t hpw;               // query heads per workgroup (1/2/4; paged bf16 path 1/2/4/8)
   int32_t n_tok_blocks;
   int32_t n_head_groups;
   int32_t num_splits;
@@ -74,6 +74,10 @@ hipError_t launch_prefill(DType in, DType out, int D, int DV, bool paged, const 
                           int grid, hipStream_t stream);
 hipError_t launch_prefill_merge(DType out, int DV, const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_prefill_varlen(int D, int DV, const PrefillArgs& a, int grid, hipStream_t stream);
+// Paged bf16 path: 8-wave workgroups (256 query rows), direct-to-LDS tiles.
+bool prefill_paged_supported(int D, int DV);
+hipError_t launch_prefill_paged(DType out, int D, int DV, const PrefillArgs& a, int grid, hipStream_t stream);
+hipError_t launch_prefill_paged_varlen(int D, int DV, const PrefillArgs& a, int grid, hipStream_t stream);
 bool prefill_supported(DType in, DType out, int D, int DV);
 
 hipError_t launch_batch_plan(const DecodeArgs& a, hipStream_t stream);

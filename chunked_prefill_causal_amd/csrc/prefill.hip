@@ -299,16 +299,18 @@ __global__ __launch_bounds__(256, sizeof(E) == 2 ? 2 : 1) void prefill_kernel(co
     const float mb = (m_run == -INFINITY) ? 0.f : m_run * cs;
     float psum = 0.f;
     if constexpr (kBf16) {
+      // Same summation order as the paged kernel, so both give identical bits.
       uint32_t pk[16];
 #pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-        for (int rr = 0; rr < 8; ++rr) {
-          const float p0 = fast_exp2(__builtin_fmaf(s[kb2][2 * rr], cs, -mb));
-          const float p1 = fast_exp2(__builtin_fmaf(s[kb2][2 * rr + 1], cs, -mb));
-          psum += p0 + p1;
-          pk[kb2 * 8 + rr] = pack_bf16(p0, p1);
-        }
+      for (int rr = 0; rr < 8; ++rr) {
+        const float p0 = fast_exp2(__builtin_fmaf(s[0][2 * rr], cs, -mb));
+        const float p1 = fast_exp2(__builtin_fmaf(s[0][2 * rr + 1], cs, -mb));
+        const float p2 = fast_exp2(__builtin_fmaf(s[1][2 * rr], cs, -mb));
+        const float p3 = fast_exp2(__builtin_fmaf(s[1][2 * rr + 1], cs, -mb));
+        psum += (p0 + p1) + (p2 + p3);
+        pk[rr] = pack_bf16(p0, p1);
+        pk[8 + rr] = pack_bf16(p2, p3);
+      }
       l_run += psum;
 #pragma unroll
       for (int st = 0; st < 4; ++st) {

@@ -1,0 +1,325 @@
+// Chunked-prefill causal attention over the paged bf16 KV pool, gfx950.
+//
+// Same result as prefill_kernel (VPP technical review, English edition, §2.2
+// Eq. (1) with its causal rule, §2.3 for the chunk offset); this is the
+// kernel the paged bf16 path runs, built around the costs measured on MI355X:
+//  * A workgroup is 8 waves x 32 query rows = 256 rows sharing one KV head
+//    (the whole GQA group of 8 heads over 32 tokens, 4 heads x 64 tokens,
+//    2 x 128 or 1 x 256), so each 64-key K/V tile crosses the L2 once per 256
+//    rows instead of once per 128.
+//  * Tiles move HBM/L2 -> LDS by direct-to-LDS loads (global_load_lds_dwordx4):
+//    no staging registers, no LDS write instructions.  Three LDS stages keep
+//    two tiles in flight while the current one is computed; one barrier per
+//    tile.  The vector-memory counter is managed by hand: inside the key loop
+//    the only vector-memory operations are these loads (block-table entries
+//    come through the scalar unit, one tile ahead), so "s_waitcnt vmcnt(N)"
+//    with N = loads of the newer tile is exact.
+//  * The per-wave matrix work is the same as prefill_kernel's: S^T = K Q^T
+//    and O^T = V^T P^T on v_mfma_f32_32x32x16_bf16, one query row per lane
+//    pair, rescale skipped when no row's maximum grew.
+//  * Values of keys past the sequence end are zeroed in registers after the
+//    LDS read (only on the last tile), logits past a row's position masked
+//    with a select, so NaN in unused pool slots never reaches an output.
+#include "device_common.h"
+#include "launch.h"
+
+namespace chunkattn {
+
+template <int D, int DV>
+struct PagedCfg {
+  static constexpr int kThreads = 512;
+  static constexpr int kStages = 3;
+  static constexpr int KBytes = D * kBlock * 2;
+  static constexpr int VBytes = DV * kBlock * 2;
+  static constexpr int Stage = KBytes + VBytes;
+  static constexpr int KPT = KBytes / 16 / kThreads;   // direct loads per thread per tile
+  static constexpr int VPT = VBytes / 16 / kThreads;
+  static constexpr int LPT = KPT + VPT;
+  static constexpr int NQ = D / 16;
+  static constexpr int NB = DV / 32;
+  static_assert(KBytes % (16 * kThreads) == 0 && VBytes % (16 * kThreads) == 0, "tile split");
+};
+
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) void*)p);
+}
+
+// 16 bytes per lane from global memory straight into LDS at m0 + 16 * lane.
+__device__ __forceinline__ void load_to_lds16(const void* g, uint32_t lds_wave_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_wave_base), "v"(g) : "memory", "m0");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+__device__ __forceinline__ void workgroup_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <typename EO, int D, int DV, bool kVarlen>
+__global__ __launch_bounds__(512, 1) void prefill_paged_kernel(const PrefillArgs a) {
+  using C = PagedCfg<D, DV>;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[C::kStages * C::Stage];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hl = lane >> 5, col = lane & 31;
+  const int hpw = a.hpw;                 // heads per workgroup: 8, 4, 2 or 1
+  const int tok_wg = 256 / hpw;
+
+  // ---- which (sequence, token block, head group, split) this workgroup owns --
+  const uint16_t* qbase = (const uint16_t*)a.q;
+  EO* obase = (EO*)a.out;
+  float* lse = a.lse;
+  const int32_t* btab = a.block_table;
+  int64_t c = a.chunk_len, P = a.past_len, kv_len = a.kv_len;
+  int n_tb = a.n_tok_blocks;
+  const int S = a.num_splits;
+  int split, w;
+  if constexpr (kVarlen) {
+    const int64_t bid = blockIdx.x;
+    int lo = 0, hi = a.num_seqs;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (a.wg_off[mid] <= bid) lo = mid;
+      else hi = mid;
+    }
+    const int q0 = a.cu_seqlens_q[lo];
+    c = a.cu_seqlens_q[lo + 1] - q0;
+    kv_len = a.kv_lens[lo];
+    P = kv_len - c;
+    n_tb = (int)((c + tok_wg - 1) / tok_wg);
+    qbase += (int64_t)q0 * a.heads * D;
+    obase += (int64_t)q0 * a.heads * DV;
+    if (lse) lse += q0;
+    btab += (int64_t)lo * a.max_blocks;
+    split = 0;
+    w = (int)(bid - a.wg_off[lo]);
+    if (c <= 0 || P < 0 || kv_len > (int64_t)a.max_blocks * kBlock || w >= n_tb * a.n_head_groups) return;
+  } else {
+    split = blockIdx.x % S;
+    w = blockIdx.x / S;
+  }
+  int tb, hg;
+  if (a.xcd_remap) {
+    const int xcd = w & 7, slot = w >> 3, hpx = a.n_head_groups >> 3;
+    hg = xcd * hpx + slot % hpx;
+    tb = n_tb - 1 - slot / hpx;
+  } else {
+    hg = w % a.n_head_groups;
+    tb = n_tb - 1 - w / a.n_head_groups;
+  }
+  const int h = hg * hpw + (wave % hpw);
+  const int g = (hg * hpw) / a.group;
+  const int64_t t_wg0 = (int64_t)tb * tok_wg;
+  const int64_t t0 = t_wg0 + (int64_t)(wave / hpw) * 32;
+  const int64_t t_wg_last = min(t_wg0 + tok_wg, c) - 1;
+  const int n_tiles = (int)((P + t_wg_last) / kBlock) + 1;
+  const int tps = (n_tiles + S - 1) / S;
+  const int j_lo = split * tps;
+  const int j_hi = min(n_tiles, j_lo + tps);
+
+  const int64_t t = t0 + col;
+  const bool row_valid = t < c;
+  const int64_t t_c = row_valid ? t : c - 1;
+  const int64_t pos = P + t_c;
+  const bool wave_active = t0 < c;
+  const int wave_last_tile = wave_active ? (int)((P + min(t0 + 31, c - 1)) / kBlock) : -1;
+  const int64_t wave_first_pos = P + t0;
+  const float cs = a.scale_log2;
+
+  if (j_lo >= j_hi) {
+    if (row_valid && hl == 0) {
+      const int64_t row = t * a.heads + h;
+      *(float2*)(a.ws_ml + ((int64_t)split * c * a.heads + row) * 2) = make_float2(-INFINITY, 0.f);
+    }
+    return;
+  }
+
+  // Query row of this lane as B operands, held for the whole key loop.
+  u32x4_t qreg[C::NQ];
+  {
+    const uint16_t* qrow = qbase + (t_c * a.heads + h) * (int64_t)D;
+#pragma unroll
+    for (int i = 0; i < C::NQ; ++i) qreg[i] = *(const u32x4_t*)(qrow + 16 * i + 8 * hl);
+  }
+
+  // ---- tile transfer: block table through the scalar unit, data straight into LDS ----
+  const __attribute__((address_space(4))) int32_t* bt4 = (const __attribute__((address_space(4))) int32_t*)btab;
+  const unsigned char* kpool = (const unsigned char*)a.k;
+  const unsigned char* vpool = (const unsigned char*)a.v;
+  const uint32_t smem_base = lds_address(smem);
+  auto issue = [&](int32_t block_id, int st) {
+    const int phys = clamp_block(block_id, a.num_blocks);
+    const int64_t tile = (int64_t)phys * a.kv_heads + g;
+    const unsigned char* kb = kpool + tile * C::KBytes;
+    const unsigned char* vb = vpool + tile * C::VBytes;
+    const uint32_t ks = smem_base + st * C::Stage;
+#pragma unroll
+    for (int i = 0; i < C::KPT; ++i) {
+      const int chunk = wave * 64 + i * C::kThreads;
+      load_to_lds16(kb + (chunk + lane) * 16, __builtin_amdgcn_readfirstlane(ks + chunk * 16));
+    }
+#pragma unroll
+    for (int i = 0; i < C::VPT; ++i) {
+      const int chunk = wave * 64 + i * C::kThreads;
+      load_to_lds16(vb + (chunk + lane) * 16, __builtin_amdgcn_readfirstlane(ks + C::KBytes + chunk * 16));
+    }
+  };
+
+  f32x16_t o[C::NB];
+#pragma unroll
+  for (int b = 0; b < C::NB; ++b) o[b] = f32x16_t{};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  auto compute_tile = [&](int j, int st) {
+    const unsigned char* ks = smem + st * C::Stage;
+    const unsigned char* vs = ks + C::KBytes;
+    f32x16_t s0 = f32x16_t{}, s1 = f32x16_t{};
+    const int krow0 = bf16_key_of_row(col);
+#pragma unroll
+    for (int i = 0; i < C::NQ; ++i) {
+      const unsigned char* p = ks + ((2 * i + hl) * kBlock + krow0) * 16;
+      const u32x4_t k0 = *(const u32x4_t*)p;
+      const u32x4_t k1 = *(const u32x4_t*)(p + 32 * 16);
+      s0 = mfma_bf16(k0, qreg[i], s0);
+      s1 = mfma_bf16(k1, qreg[i], s1);
+    }
+    const int64_t key0 = (int64_t)j * kBlock;
+    if (key0 + kBlock - 1 > wave_first_pos) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        if (key0 + bf16_key_of_reg(0, r, hl) > pos) s0[r] = -INFINITY;
+        if (key0 + bf16_key_of_reg(1, r, hl) > pos) s1[r] = -INFINITY;
+      }
+    }
+    float mx = fmaxf(s0[0], s1[0]);
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
+    mx = half_max(mx);
+    const float m_new = fmaxf(m_run, mx);
+    const bool grow = m_new > m_run;
+    if (__any(grow)) {
+      const float alpha = grow ? fast_exp2((m_run - m_new) * cs) : 1.f;
+      l_run *= alpha;
+#pragma unroll
+      for (int b = 0; b < C::NB; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[b][r] *= alpha;
+      m_run = m_new;
+    }
+    const float mb = (m_run == -INFINITY) ? 0.f : m_run * cs;
+    uint32_t pk[16];
+    float psum = 0.f;
+#pragma unroll
+    for (int rr = 0; rr < 8; ++rr) {
+      const float p0 = fast_exp2(__builtin_fmaf(s0[2 * rr], cs, -mb));
+      const float p1 = fast_exp2(__builtin_fmaf(s0[2 * rr + 1], cs, -mb));
+      const float p2 = fast_exp2(__builtin_fmaf(s1[2 * rr], cs, -mb));
+      const float p3 = fast_exp2(__builtin_fmaf(s1[2 * rr + 1], cs, -mb));
+      psum += (p0 + p1) + (p2 + p3);
+      pk[rr] = pack_bf16(p0, p1);
+      pk[8 + rr] = pack_bf16(p2, p3);
+    }
+    l_run += psum;
+    const bool tail = key0 + kBlock > kv_len;
+#pragma unroll
+    for (int stp = 0; stp < 4; ++stp) {
+      const int base = (stp >> 1) * 8 + 4 * (stp & 1);
+      const u32x4_t pb = u32x4_t{pk[base], pk[base + 1], pk[base + 2], pk[base + 3]};
+#pragma unroll
+      for (int b = 0; b < C::NB; ++b) {
+        u32x4_t va = *(const u32x4_t*)(vs + ((2 * stp + hl) * DV + 32 * b + col) * 16);
+        if (tail) {   // values of keys past the sequence end: zero (0 * NaN guard)
+          const int64_t kfirst = key0 + 16 * stp + 8 * hl;
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (kfirst + e >= kv_len) va[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
+        }
+        o[b] = mfma_bf16(va, pb, o[b]);
+      }
+    }
+  };
+
+  // ---- key loop: two tiles in flight, one barrier per tile ------------------------
+  // The block id of the tile issued in the next iteration is loaded one
+  // iteration early, so its scalar load never stalls the issue.
+  issue(bt4[j_lo], 0);
+  if (j_lo + 1 < j_hi) issue(bt4[j_lo + 1], 1);
+  int32_t block_ahead = (j_lo + 2 < j_hi) ? bt4[j_lo + 2] : 0;
+  int st = 0;
+  for (int j = j_lo; j < j_hi; ++j) {
+    if (j + 1 < j_hi) wait_vmem<C::LPT>();   // this tile landed; the next may still fly
+    else wait_vmem<0>();
+    workgroup_barrier();                     // every wave's part landed; stage (st+2)%3 free
+    if (j + 2 < j_hi) issue(block_ahead, st == 0 ? 2 : st - 1);
+    block_ahead = (j + 3 < j_hi) ? bt4[j + 3] : 0;
+    if (j <= wave_last_tile) compute_tile(j, st);
+    st = st == 2 ? 0 : st + 1;
+  }
+
+  // ---- epilogue ------------------------------------------------------------------
+  const float l_tot = half_sum(l_run);
+  if (!row_valid) return;
+  if (S == 1) {
+    const float inv = 1.f / l_tot;
+    EO* orow = obase + (t * a.heads + h) * (int64_t)DV;
+#pragma unroll
+    for (int b = 0; b < C::NB; ++b)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        const int dv0 = 32 * b + 8 * rq + 4 * hl;
+        const float v0 = o[b][4 * rq] * inv, v1 = o[b][4 * rq + 1] * inv;
+        const float v2 = o[b][4 * rq + 2] * inv, v3 = o[b][4 * rq + 3] * inv;
+        if constexpr (sizeof(EO) == 2) *(u32x2_t*)(orow + dv0) = u32x2_t{pack_bf16(v0, v1), pack_bf16(v2, v3)};
+        else *(f32x4_t*)(orow + dv0) = f32x4_t{v0, v1, v2, v3};
+      }
+    if (lse && hl == 0) lse[(int64_t)h * a.lse_stride + t] = (m_run * cs + __log2f(l_tot)) * kLn2;
+  } else {
+    const int64_t R = c * a.heads;
+    const int64_t row = t * a.heads + h;
+    float* wo = a.ws_o + ((int64_t)split * R + row) * DV;
+#pragma unroll
+    for (int b = 0; b < C::NB; ++b)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq)
+        *(f32x4_t*)(wo + 32 * b + 8 * rq + 4 * hl) =
+            f32x4_t{o[b][4 * rq], o[b][4 * rq + 1], o[b][4 * rq + 2], o[b][4 * rq + 3]};
+    if (hl == 0)
+      *(float2*)(a.ws_ml + ((int64_t)split * R + row) * 2) =
+          make_float2(m_run == -INFINITY ? -INFINITY : m_run * cs, l_tot);
+  }
+}
+
+// ---- host launchers -----------------------------------------------------------------
+
+bool prefill_paged_supported(int D, int DV) {
+  return (D == 64 && DV == 64) || (D == 128 && DV == 128) || (D == 192 && DV == 128);
+}
+
+template <typename EO, bool kVarlen>
+static hipError_t launch_paged_dims(int D, int DV, const PrefillArgs& a, int grid, hipStream_t s) {
+  if (D == 64 && DV == 64)
+    hipLaunchKernelGGL((prefill_paged_kernel<EO, 64, 64, kVarlen>), dim3(grid), dim3(512), 0, s, a);
+  else if (D == 128 && DV == 128)
+    hipLaunchKernelGGL((prefill_paged_kernel<EO, 128, 128, kVarlen>), dim3(grid), dim3(512), 0, s, a);
+  else if (D == 192 && DV == 128)
+    hipLaunchKernelGGL((prefill_paged_kernel<EO, 192, 128, kVarlen>), dim3(grid), dim3(512), 0, s, a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_paged(DType out, int D, int DV, const PrefillArgs& a, int grid, hipStream_t stream) {
+  if (out == DType::BF16) return launch_paged_dims<uint16_t, false>(D, DV, a, grid, stream);
+  return launch_paged_dims<float, false>(D, DV, a, grid, stream);
+}
+
+hipError_t launch_prefill_paged_varlen(int D, int DV, const PrefillArgs& a, int grid, hipStream_t stream) {
+  return launch_paged_dims<uint16_t, true>(D, DV, a, grid, stream);
+}
+
+}  // namespace chunkattn
