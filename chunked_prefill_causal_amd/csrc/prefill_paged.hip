@@ -8,18 +8,19 @@
 //    2 x 128 or 1 x 256), so each 64-key K/V tile crosses the L2 once per 256
 //    rows instead of once per 128.
 //  * Tiles move HBM/L2 -> LDS by direct-to-LDS loads (global_load_lds_dwordx4):
-//    no staging registers, no LDS write instructions.  Three LDS stages keep
-//    two tiles in flight while the current one is computed; one barrier per
-//    tile.  The vector-memory counter is managed by hand: inside the key loop
+//    no staging registers, no LDS write instructions.  Four LDS stages (three
+//    at d = 192) give each load two tile-times to land; one barrier per tile.  The vector-memory counter is managed by hand: inside the key loop
 //    the only vector-memory operations are these loads (block-table entries
 //    come through the scalar unit, one tile ahead), so "s_waitcnt vmcnt(N)"
 //    with N = loads of the newer tile is exact.
 //  * The per-wave matrix work is the same as prefill_kernel's: S^T = K Q^T
 //    and O^T = V^T P^T on v_mfma_f32_32x32x16_bf16, one query row per lane
-//    pair, rescale skipped when no row's maximum grew.
-//  * Values of keys past the sequence end are zeroed in registers after the
-//    LDS read (only on the last tile), logits past a row's position masked
-//    with a select, so NaN in unused pool slots never reaches an output.
+//    pair, rescale skipped when no row's maximum grew.  The two waves that
+//    share a SIMD run the same tiles half an interval apart (ping-pong), so
+//    one feeds the matrix cores while the other computes its softmax.
+//  * Values of keys past the sequence end are zeroed in LDS once the tile
+//    holding the sequence end has landed, logits past a row's position are
+//    masked with a select, so NaN in unused pool slots never reaches an output.
 #include "device_common.h"
 #include "launch.h"
 
@@ -28,7 +29,7 @@ namespace chunkattn {
 template <int D, int DV>
 struct PagedCfg {
   static constexpr int kThreads = 512;
-  static constexpr int kStages = 3;
+  static constexpr int kStages = (D + DV) * kBlock * 2 * 4 <= 131072 ? 4 : 3;   // LDS stages (160 KB per CU)
   static constexpr int KBytes = D * kBlock * 2;
   static constexpr int VBytes = DV * kBlock * 2;
   static constexpr int Stage = KBytes + VBytes;
@@ -126,9 +127,7 @@ __global__ __launch_bounds__(512, 1) void prefill_paged_kernel(const PrefillArgs
   const bool row_valid = t < c;
   const int64_t t_c = row_valid ? t : c - 1;
   const int64_t pos = P + t_c;
-  const bool wave_active = t0 < c;
-  const int wave_last_tile = wave_active ? (int)((P + min(t0 + 31, c - 1)) / kBlock) : -1;
-  const int64_t wave_first_pos = P + t0;
+  const int64_t wave_first_pos = P + min(t0, c - 1);
   const float cs = a.scale_log2;
 
   if (j_lo >= j_hi) {
@@ -174,11 +173,18 @@ __global__ __launch_bounds__(512, 1) void prefill_paged_kernel(const PrefillArgs
 #pragma unroll
   for (int b = 0; b < C::NB; ++b) o[b] = f32x16_t{};
   float m_run = -INFINITY, l_run = 0.f;
+  f32x16_t s0 = f32x16_t{}, s1 = f32x16_t{};   // S^T of the tile between QK and softmax
+  u32x4_t pkv[4];                               // bf16 P of the tile between softmax and PV,
+#pragma unroll                                    // one MFMA B operand per 16-key step
+  for (int i = 0; i < 4; ++i) pkv[i] = u32x4_t{0u, 0u, 0u, 0u};
 
-  auto compute_tile = [&](int j, int st) {
-    const unsigned char* ks = smem + st * C::Stage;
-    const unsigned char* vs = ks + C::KBytes;
-    f32x16_t s0 = f32x16_t{}, s1 = f32x16_t{};
+  auto stage_ptr = [&](int st) { return smem + st * C::Stage; };
+
+  // S^T = K Q^T for one 64-key tile (two 32-key halves).
+  auto qk = [&](int st) {
+    const unsigned char* ks = stage_ptr(st);
+    s0 = f32x16_t{};
+    s1 = f32x16_t{};
     const int krow0 = bf16_key_of_row(col);
 #pragma unroll
     for (int i = 0; i < C::NQ; ++i) {
@@ -188,6 +194,10 @@ __global__ __launch_bounds__(512, 1) void prefill_paged_kernel(const PrefillArgs
       s0 = mfma_bf16(k0, qreg[i], s0);
       s1 = mfma_bf16(k1, qreg[i], s1);
     }
+  };
+
+  // Online softmax of tile j: mask, running max, rescale, P in bf16, running sum.
+  auto softmax = [&](int j) {
     const int64_t key0 = (int64_t)j * kBlock;
     if (key0 + kBlock - 1 > wave_first_pos) {
 #pragma unroll
@@ -212,7 +222,6 @@ __global__ __launch_bounds__(512, 1) void prefill_paged_kernel(const PrefillArgs
       m_run = m_new;
     }
     const float mb = (m_run == -INFINITY) ? 0.f : m_run * cs;
-    uint32_t pk[16];
     float psum = 0.f;
 #pragma unroll
     for (int rr = 0; rr < 8; ++rr) {
@@ -221,44 +230,143 @@ __global__ __launch_bounds__(512, 1) void prefill_paged_kernel(const PrefillArgs
       const float p2 = fast_exp2(__builtin_fmaf(s1[2 * rr], cs, -mb));
       const float p3 = fast_exp2(__builtin_fmaf(s1[2 * rr + 1], cs, -mb));
       psum += (p0 + p1) + (p2 + p3);
-      pk[rr] = pack_bf16(p0, p1);
-      pk[8 + rr] = pack_bf16(p2, p3);
+      pkv[rr >> 2][rr & 3] = pack_bf16(p0, p1);
+      pkv[2 + (rr >> 2)][rr & 3] = pack_bf16(p2, p3);
     }
     l_run += psum;
-    const bool tail = key0 + kBlock > kv_len;
+  };
+
+  // O^T += V^T P^T for tile j.
+  auto pv = [&](int st) {
+    const unsigned char* vs = stage_ptr(st) + C::KBytes;
 #pragma unroll
     for (int stp = 0; stp < 4; ++stp) {
-      const int base = (stp >> 1) * 8 + 4 * (stp & 1);
-      const u32x4_t pb = u32x4_t{pk[base], pk[base + 1], pk[base + 2], pk[base + 3]};
 #pragma unroll
       for (int b = 0; b < C::NB; ++b) {
-        u32x4_t va = *(const u32x4_t*)(vs + ((2 * stp + hl) * DV + 32 * b + col) * 16);
-        if (tail) {   // values of keys past the sequence end: zero (0 * NaN guard)
-          const int64_t kfirst = key0 + 16 * stp + 8 * hl;
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (kfirst + e >= kv_len) va[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
-        }
-        o[b] = mfma_bf16(va, pb, o[b]);
+        const u32x4_t va = *(const u32x4_t*)(vs + ((2 * stp + hl) * DV + 32 * b + col) * 16);
+        o[b] = mfma_bf16(va, pkv[stp], o[b]);
       }
     }
   };
 
-  // ---- key loop: two tiles in flight, one barrier per tile ------------------------
-  // The block id of the tile issued in the next iteration is loaded one
-  // iteration early, so its scalar load never stalls the issue.
-  issue(bt4[j_lo], 0);
-  if (j_lo + 1 < j_hi) issue(bt4[j_lo + 1], 1);
-  int32_t block_ahead = (j_lo + 2 < j_hi) ? bt4[j_lo + 2] : 0;
-  int st = 0;
-  for (int j = j_lo; j < j_hi; ++j) {
-    if (j + 1 < j_hi) wait_vmem<C::LPT>();   // this tile landed; the next may still fly
-    else wait_vmem<0>();
-    workgroup_barrier();                     // every wave's part landed; stage (st+2)%3 free
-    if (j + 2 < j_hi) issue(block_ahead, st == 0 ? 2 : st - 1);
-    block_ahead = (j + 3 < j_hi) ? bt4[j + 3] : 0;
-    if (j <= wave_last_tile) compute_tile(j, st);
-    st = st == 2 ? 0 : st + 1;
+  // PV of tile jp and QK of the next tile, issued alternately: six independent
+  // accumulator chains (four O blocks, two S halves), so no matrix-core
+  // instruction waits on the one just before it.
+  auto pv_qk = [&](int st_prev, int st_cur) {
+    const unsigned char* vs = stage_ptr(st_prev) + C::KBytes;
+    const unsigned char* ks = stage_ptr(st_cur);
+    const int krow0 = bf16_key_of_row(col);
+    f32x16_t n0 = f32x16_t{}, n1 = f32x16_t{};
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      {   // PV step (stp, b) = (u / NB, u % NB), covering all 16 for NB = 4
+        constexpr int kPv = 4 * C::NB;
+        if (u < kPv) {
+          const int stp = u / C::NB, b = u % C::NB;
+          const u32x4_t va = *(const u32x4_t*)(vs + ((2 * stp + hl) * DV + 32 * b + col) * 16);
+          o[b] = mfma_bf16(va, pkv[stp], o[b]);
+        }
+      }
+      {   // QK step (i, half) = (u / 2, u % 2)
+        const int i = u >> 1;
+        if (i < C::NQ) {
+          const unsigned char* p = ks + ((2 * i + hl) * kBlock + krow0 + 32 * (u & 1)) * 16;
+          const u32x4_t kk = *(const u32x4_t*)p;
+          if (u & 1) n1 = mfma_bf16(kk, qreg[i], n1);
+          else n0 = mfma_bf16(kk, qreg[i], n0);
+        }
+      }
+      if ((u & 3) == 3) __builtin_amdgcn_sched_barrier(0);   // bound operand prefetch (registers)
+    }
+#pragma unroll
+    for (int u = 16; u < 2 * C::NQ; ++u) {   // remaining QK steps when d > 128
+      const int i = u >> 1;
+      const unsigned char* p = ks + ((2 * i + hl) * kBlock + krow0 + 32 * (u & 1)) * 16;
+      const u32x4_t kk = *(const u32x4_t*)p;
+      if (u & 1) n1 = mfma_bf16(kk, qreg[i], n1);
+      else n0 = mfma_bf16(kk, qreg[i], n0);
+    }
+    s0 = n0;
+    s1 = n1;
+  };
+
+  // ---- key loop -------------------------------------------------------------------
+  // Interval i (between two barriers) does, for every wave, PV of tile i-1,
+  // QK of tile i and the softmax of the tile in between.  Waves 0-3 run
+  // "PV(i-1), QK(i), softmax(i)"; waves 4-7 run "softmax(i-1), PV(i-1), QK(i)".
+  // Waves w and w+4 share a SIMD, so while one streams matrix-core work the
+  // other runs its softmax on the vector ALUs, and they swap halfway.
+  // Tile t is read in intervals t and t+1; its stage is refilled with tile
+  // t + kStages, issued in interval t + 2, which leaves kStages - 2 intervals
+  // for the load to land.
+  constexpr int NS = C::kStages;
+  const int n = j_hi - j_lo;
+#pragma unroll
+  for (int p = 0; p < NS - 2; ++p)
+    if (p < n) issue(bt4[j_lo + p], p);
+  int32_t block_ahead = (NS - 2 < n) ? bt4[j_lo + NS - 2] : 0;
+  // Start of interval i: tile i must have landed (tiles i+1 .. i+NS-3 may
+  // still be in flight); after the barrier the stage of tile i-2 is free and
+  // receives tile i+NS-2.
+  auto interval_start = [&](int i) {
+    if (i < n) {
+      if (min(NS - 3, n - 1 - i) >= 1) wait_vmem<C::LPT>();
+      else wait_vmem<0>();
+    }
+    workgroup_barrier();
+    if (i + NS - 2 < n) issue(block_ahead, (i + NS - 2) % NS);
+    block_ahead = (i + NS - 1 < n) ? bt4[j_lo + i + NS - 1] : 0;
+    const int64_t key0 = (int64_t)(j_lo + i) * kBlock;
+    if (i < n && key0 + kBlock > kv_len) {
+      // The tile holding the sequence end: zero its values of keys >= kv_len
+      // in LDS (a masked key has probability 0, but 0 * NaN would poison the
+      // sum).  Nobody reads this V before the next barrier.
+      uint16_t* vt = (uint16_t*)(stage_ptr(i % NS) + C::KBytes);
+      const int first = (int)(kv_len - key0);          // 1..63 keys stay
+      const int count = (kBlock - first) * DV;
+      for (int e = tid; e < count; e += C::kThreads) {
+        const int key = first + e / DV, dv = e % DV;
+        vt[((key >> 3) * DV + dv) * 8 + (key & 7)] = 0;
+      }
+    }
+  };
+  // Each group has its own copy of the loop, so only P (leading waves) or
+  // only S (trailing waves) stays live across the barrier.  Every wave runs
+  // every tile of the workgroup's range: a tile past a wave's rows is fully
+  // masked (probability 0 against finite values), which leaves its output
+  // unchanged and keeps one straight-line loop body.  Scheduling fences keep
+  // the matrix and vector phases in one piece each, so the two waves of a
+  // SIMD stay interleaved as written.
+  if (wave < 4) {
+    interval_start(0);
+    qk(0);
+    __builtin_amdgcn_sched_barrier(0);
+    softmax(j_lo);
+    __builtin_amdgcn_sched_barrier(0);
+    for (int i = 1; i < n; ++i) {
+      interval_start(i);
+      pv_qk((i - 1) % NS, i % NS);
+      __builtin_amdgcn_sched_barrier(0);
+      softmax(j_lo + i);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    interval_start(n);
+    pv((n - 1) % NS);
+  } else {
+    interval_start(0);
+    qk(0);
+    __builtin_amdgcn_sched_barrier(0);
+    for (int i = 1; i < n; ++i) {
+      interval_start(i);
+      softmax(j_lo + i - 1);
+      __builtin_amdgcn_sched_barrier(0);
+      pv_qk((i - 1) % NS, i % NS);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    interval_start(n);
+    softmax(j_lo + n - 1);
+    __builtin_amdgcn_sched_barrier(0);
+    pv((n - 1) % NS);
   }
 
   // ---- epilogue ------------------------------------------------------------------
