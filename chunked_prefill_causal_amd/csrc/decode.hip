@@ -167,9 +167,9 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb2][r]);
     mx = half_max(mx);
-    const float m_new = fmaxf(m_run, mx);
-    const bool grow = m_new > m_run;
+    const bool grow = mx * cs > m_run * cs + kLazyRescale;   // lazy maximum (see kLazyRescale)
     if (__any(grow)) {
+      const float m_new = grow ? mx : m_run;
       const float alpha = grow ? fast_exp2((m_run - m_new) * cs) : 1.f;
       l_run *= alpha;
 #pragma unroll

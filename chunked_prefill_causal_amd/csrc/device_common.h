@@ -61,6 +61,13 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, p);
 }
 
+// Online-softmax maximum policy: a row's running maximum is raised only when
+// a new logit exceeds it by more than kLazyRescale (log2 units, after the
+// scale), so exp2(s - m) stays <= 2^kLazyRescale while O and l are rescaled
+// rarely.  Numerator and normaliser share the same offset, so the result is
+// exact whatever offset is used.
+constexpr float kLazyRescale = 8.0f;
+
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 
 __device__ __forceinline__ int clamp_block(int32_t id, int32_t num_blocks) {

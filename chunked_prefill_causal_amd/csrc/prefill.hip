@@ -285,9 +285,10 @@ __global__ __launch_bounds__(256, sizeof(E) == 2 ? 2 : 1) void prefill_kernel(co
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb2][r]);
     mx = half_max(mx);
-    const float m_new = fmaxf(m_run, mx);
-    const bool grow = m_new > m_run;
+    // The running maximum is raised lazily (see kLazyRescale).
+    const bool grow = mx * cs > m_run * cs + kLazyRescale;
     if (__any(grow)) {
+      const float m_new = grow ? mx : m_run;
       const float alpha = grow ? fast_exp2((m_run - m_new) * cs) : 1.f;
       l_run *= alpha;
 #pragma unroll
@@ -299,7 +300,8 @@ __global__ __launch_bounds__(256, sizeof(E) == 2 ? 2 : 1) void prefill_kernel(co
     const float mb = (m_run == -INFINITY) ? 0.f : m_run * cs;
     float psum = 0.f;
     if constexpr (kBf16) {
-      // Same summation order as the paged kernel, so both give identical bits.
+      // Same arithmetic, in the same order, as the paged kernel, so both give
+      // identical bits.
       uint32_t pk[16];
 #pragma unroll
       for (int rr = 0; rr < 8; ++rr) {

@@ -181,38 +181,42 @@ __global__ __launch_bounds__(512, 1) void prefill_paged_kernel(const PrefillArgs
   auto stage_ptr = [&](int st) { return smem + st * C::Stage; };
 
   // S^T = K Q^T for one 64-key tile (two 32-key halves).
+  const int k_lane = (hl * kBlock + bf16_key_of_row(col)) * 16;   // this lane's K operand offset
+  const int v_lane = C::KBytes + (hl * DV + col) * 16;             // this lane's V operand offset
   auto qk = [&](int st) {
-    const unsigned char* ks = stage_ptr(st);
+    const unsigned char* kb = stage_ptr(st) + k_lane;
     s0 = f32x16_t{};
     s1 = f32x16_t{};
-    const int krow0 = bf16_key_of_row(col);
 #pragma unroll
     for (int i = 0; i < C::NQ; ++i) {
-      const unsigned char* p = ks + ((2 * i + hl) * kBlock + krow0) * 16;
-      const u32x4_t k0 = *(const u32x4_t*)p;
-      const u32x4_t k1 = *(const u32x4_t*)(p + 32 * 16);
+      const u32x4_t k0 = *(const u32x4_t*)(kb + 2 * i * kBlock * 16);
+      const u32x4_t k1 = *(const u32x4_t*)(kb + (2 * i * kBlock + 32) * 16);
       s0 = mfma_bf16(k0, qreg[i], s0);
       s1 = mfma_bf16(k1, qreg[i], s1);
     }
   };
 
-  // Online softmax of tile j: mask, running max, rescale, P in bf16, running sum.
+  // Online softmax of tile j: mask, running max (raised lazily), rescale,
+  // P in bf16, running sum of the fp32 P.
   auto softmax = [&](int j) {
     const int64_t key0 = (int64_t)j * kBlock;
     if (key0 + kBlock - 1 > wave_first_pos) {
+      const int lim = (int)(pos - key0);          // keys past lim are invisible to this row
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        if (key0 + bf16_key_of_reg(0, r, hl) > pos) s0[r] = -INFINITY;
-        if (key0 + bf16_key_of_reg(1, r, hl) > pos) s1[r] = -INFINITY;
+        if (bf16_key_of_reg(0, r, hl) > lim) s0[r] = -INFINITY;
+        if (bf16_key_of_reg(1, r, hl) > lim) s1[r] = -INFINITY;
       }
     }
-    float mx = fmaxf(s0[0], s1[0]);
+    float mx = s0[0];
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s0[r]);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s1[r]);
     mx = half_max(mx);
-    const float m_new = fmaxf(m_run, mx);
-    const bool grow = m_new > m_run;
+    const bool grow = mx * cs > m_run * cs + kLazyRescale;
     if (__any(grow)) {
+      const float m_new = grow ? mx : m_run;
       const float alpha = grow ? fast_exp2((m_run - m_new) * cs) : 1.f;
       l_run *= alpha;
 #pragma unroll
@@ -238,12 +242,12 @@ __global__ __launch_bounds__(512, 1) void prefill_paged_kernel(const PrefillArgs
 
   // O^T += V^T P^T for tile j.
   auto pv = [&](int st) {
-    const unsigned char* vs = stage_ptr(st) + C::KBytes;
+    const unsigned char* vb = stage_ptr(st) + v_lane;
 #pragma unroll
     for (int stp = 0; stp < 4; ++stp) {
 #pragma unroll
       for (int b = 0; b < C::NB; ++b) {
-        const u32x4_t va = *(const u32x4_t*)(vs + ((2 * stp + hl) * DV + 32 * b + col) * 16);
+        const u32x4_t va = *(const u32x4_t*)(vb + (2 * stp * DV + 32 * b) * 16);
         o[b] = mfma_bf16(va, pkv[stp], o[b]);
       }
     }
@@ -253,9 +257,8 @@ __global__ __launch_bounds__(512, 1) void prefill_paged_kernel(const PrefillArgs
   // accumulator chains (four O blocks, two S halves), so no matrix-core
   // instruction waits on the one just before it.
   auto pv_qk = [&](int st_prev, int st_cur) {
-    const unsigned char* vs = stage_ptr(st_prev) + C::KBytes;
-    const unsigned char* ks = stage_ptr(st_cur);
-    const int krow0 = bf16_key_of_row(col);
+    const unsigned char* vb = stage_ptr(st_prev) + v_lane;
+    const unsigned char* kb = stage_ptr(st_cur) + k_lane;
     f32x16_t n0 = f32x16_t{}, n1 = f32x16_t{};
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
@@ -263,31 +266,38 @@ __global__ __launch_bounds__(512, 1) void prefill_paged_kernel(const PrefillArgs
         constexpr int kPv = 4 * C::NB;
         if (u < kPv) {
           const int stp = u / C::NB, b = u % C::NB;
-          const u32x4_t va = *(const u32x4_t*)(vs + ((2 * stp + hl) * DV + 32 * b + col) * 16);
+          const u32x4_t va = *(const u32x4_t*)(vb + (2 * stp * DV + 32 * b) * 16);
           o[b] = mfma_bf16(va, pkv[stp], o[b]);
         }
       }
       {   // QK step (i, half) = (u / 2, u % 2)
         const int i = u >> 1;
         if (i < C::NQ) {
-          const unsigned char* p = ks + ((2 * i + hl) * kBlock + krow0 + 32 * (u & 1)) * 16;
-          const u32x4_t kk = *(const u32x4_t*)p;
+          const u32x4_t kk = *(const u32x4_t*)(kb + (2 * i * kBlock + 32 * (u & 1)) * 16);
           if (u & 1) n1 = mfma_bf16(kk, qreg[i], n1);
           else n0 = mfma_bf16(kk, qreg[i], n0);
         }
       }
-      if ((u & 3) == 3) __builtin_amdgcn_sched_barrier(0);   // bound operand prefetch (registers)
     }
 #pragma unroll
     for (int u = 16; u < 2 * C::NQ; ++u) {   // remaining QK steps when d > 128
       const int i = u >> 1;
-      const unsigned char* p = ks + ((2 * i + hl) * kBlock + krow0 + 32 * (u & 1)) * 16;
-      const u32x4_t kk = *(const u32x4_t*)p;
+      const u32x4_t kk = *(const u32x4_t*)(kb + (2 * i * kBlock + 32 * (u & 1)) * 16);
       if (u & 1) n1 = mfma_bf16(kk, qreg[i], n1);
       else n0 = mfma_bf16(kk, qreg[i], n0);
     }
     s0 = n0;
     s1 = n1;
+    // Issue order: kLead LDS operand reads ahead, then one matrix op per read,
+    // so about kLead reads are in flight while the matrix cores run.
+    constexpr int kReads = 4 * C::NB + 2 * C::NQ, kLead = 6;
+    __builtin_amdgcn_sched_group_barrier(0x100, kLead, 0);
+#pragma unroll
+    for (int r = 0; r < kReads - kLead; ++r) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, kLead, 0);
   };
 
   // ---- key loop -------------------------------------------------------------------
