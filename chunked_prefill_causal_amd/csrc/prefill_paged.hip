@@ -9,10 +9,16 @@
 //    rows instead of once per 128.
 //  * Tiles move HBM/L2 -> LDS by direct-to-LDS loads (global_load_lds_dwordx4):
 //    no staging registers, no LDS write instructions.  Four LDS stages (three
-//    at d = 192) give each load two tile-times to land; one barrier per tile.  The vector-memory counter is managed by hand: inside the key loop
-//    the only vector-memory operations are these loads (block-table entries
-//    come through the scalar unit, one tile ahead), so "s_waitcnt vmcnt(N)"
-//    with N = loads of the newer tile is exact.
+//    at d = 192) give each load two tile-times to land; one barrier per tile.
+//    Only the four leading waves issue them, right after the barrier, so the
+//    tile lands while those waves stream their matrix work; measured on
+//    MI355X, data landing in LDS during the trailing waves' matrix phase
+//    stalls their operand reads, and loads issued by the trailing waves queue
+//    behind the leading ones on their critical path.  The vector-memory
+//    counter is managed by hand: inside the key loop the only vector-memory
+//    operations are these loads (block-table entries come through the scalar
+//    unit, one tile ahead), so "s_waitcnt vmcnt(N)" with N = loads of the
+//    newer tile is exact (the trailing waves have none outstanding and pass).
 //  * The per-wave matrix work is the same as prefill_kernel's: S^T = K Q^T
 //    and O^T = V^T P^T on v_mfma_f32_32x32x16_bf16, one query row per lane
 //    pair, rescale skipped when no row's maximum grew.  The two waves that
@@ -33,12 +39,13 @@ struct PagedCfg {
   static constexpr int KBytes = D * kBlock * 2;
   static constexpr int VBytes = DV * kBlock * 2;
   static constexpr int Stage = KBytes + VBytes;
-  static constexpr int KPT = KBytes / 16 / kThreads;   // direct loads per thread per tile
-  static constexpr int VPT = VBytes / 16 / kThreads;
+  static constexpr int kLoaders = 256;                 // the four leading waves move the tiles
+  static constexpr int KPT = KBytes / 16 / kLoaders;   // direct loads per loading thread per tile
+  static constexpr int VPT = VBytes / 16 / kLoaders;
   static constexpr int LPT = KPT + VPT;
   static constexpr int NQ = D / 16;
   static constexpr int NB = DV / 32;
-  static_assert(KBytes % (16 * kThreads) == 0 && VBytes % (16 * kThreads) == 0, "tile split");
+  static_assert(KBytes % (16 * kLoaders) == 0 && VBytes % (16 * kLoaders) == 0, "tile split");
 };
 
 __device__ __forceinline__ uint32_t lds_address(const void* p) {
@@ -152,6 +159,7 @@ __global__ __launch_bounds__(512, 1) void prefill_paged_kernel(const PrefillArgs
   const unsigned char* vpool = (const unsigned char*)a.v;
   const uint32_t smem_base = lds_address(smem);
   auto issue = [&](int32_t block_id, int st) {
+    if (wave >= 4) return;
     const int phys = clamp_block(block_id, a.num_blocks);
     const int64_t tile = (int64_t)phys * a.kv_heads + g;
     const unsigned char* kb = kpool + tile * C::KBytes;
@@ -159,12 +167,12 @@ __global__ __launch_bounds__(512, 1) void prefill_paged_kernel(const PrefillArgs
     const uint32_t ks = smem_base + st * C::Stage;
 #pragma unroll
     for (int i = 0; i < C::KPT; ++i) {
-      const int chunk = wave * 64 + i * C::kThreads;
+      const int chunk = wave * 64 + i * C::kLoaders;
       load_to_lds16(kb + (chunk + lane) * 16, __builtin_amdgcn_readfirstlane(ks + chunk * 16));
     }
 #pragma unroll
     for (int i = 0; i < C::VPT; ++i) {
-      const int chunk = wave * 64 + i * C::kThreads;
+      const int chunk = wave * 64 + i * C::kLoaders;
       load_to_lds16(vb + (chunk + lane) * 16, __builtin_amdgcn_readfirstlane(ks + C::KBytes + chunk * 16));
     }
   };
