@@ -23,9 +23,12 @@ same workload and its outputs compared with the GPU's.
 from __future__ import annotations
 
 import argparse
+import csv
+import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -36,6 +39,13 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 matrix peak: 256 CUs x 4096 flop/clk x 2.4 GHz (published 2.5 PF)
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 METRIC = "causal-effective attn TFLOP/s & per-chunk latency vs chunk index (1 MI355X)"
+DOMINANT = "prefill_paged_kernel<bf16 out, d 128, d_v 128> (chunk loop launches)"
+DOMINANT_NAMES = ("prefill_paged_kernel<unsigned short, 128, 128, false>",   # rocprofv3, demangled
+                  "prefill_paged_kernelItLi128ELi128ELb0E")                # mangled
+KERNEL_SOURCES = ["chunked_prefill_causal_amd/csrc/prefill_paged.hip",
+                  "chunked_prefill_causal_amd/csrc/device_common.h", "chunked_prefill_causal_amd/csrc/launch.h"]
+TRAFFIC_SUMMARY = "profiles/prefill_paged_gqa128k_traffic.md"
+CALIB_BYTES = 1 << 30                                             # the calibration copy: reads and writes 1 GiB
 
 
 def log(msg):
@@ -52,10 +62,93 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=5)
     p.add_argument("--warmup", type=int, default=2)
-    p.add_argument("--cpu-rows", type=int, default=512, help="oracle rows sampled per chunk for the CPU baseline")
+    p.add_argument("--cpu-rows", type=int, default=1024, help="oracle rows sampled per chunk for the CPU baseline")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--reps", type=int, default=10, help="repetitions for the decode-only / prefill-only timings")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="after the timed region, copy 1 GiB device to device (a known-size kernel for counter scaling)")
+    p.add_argument("--summarize-profile", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
+                   help="write the traffic summary from rocprofv3 output of this script (no GPU needed)")
     return p.parse_args()
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic():
+    """HBM-side bytes per chunk-loop launch from the committed counter summary, or None (with the reason)
+    when there is no summary or the kernel sources changed since its counters were taken."""
+    try:
+        with open(os.path.join(ROOT, TRAFFIC_SUMMARY)) as f:
+            text = f.read()
+    except OSError:
+        return None, "no counter summary"
+    m = re.search(r"<!-- traffic (\{.*?\}) -->", text)
+    if not m:
+        return None, "counter summary has no traffic record"
+    rec = json.loads(m.group(1))
+    if rec.get("kernel_sha256") != kernel_source_hash():
+        return None, "kernel sources changed since the counters were taken"
+    return rec, None
+
+
+def _csv_rows(directory, suffix):
+    for root, _, files in os.walk(directory):
+        for name in files:
+            if name.endswith(suffix):
+                with open(os.path.join(root, name), newline="") as f:
+                    return list(csv.DictReader(f))
+    raise FileNotFoundError(f"no *{suffix} under {directory}")
+
+
+def _counter_per_dispatch(directory, counter):
+    vals, names = {}, {}
+    for r in _csv_rows(directory, "counter_collection.csv"):
+        if r["Counter_Name"] != counter:
+            continue
+        d = int(r["Dispatch_Id"])
+        vals[d] = vals.get(d, 0.0) + float(r["Counter_Value"])
+        names[d] = r["Kernel_Name"]
+    return vals, names
+
+
+def summarize_profile(trace_dir, fetch_dir, write_dir):
+    """Markdown summary of the bench command's kernel trace and its FETCH_SIZE / WRITE_SIZE passes."""
+    stats = _csv_rows(trace_dir, "kernel_stats.csv")
+    trace = _csv_rows(trace_dir, "kernel_trace.csv")
+    lines = ["## --stats summary (kernels of the library)", "",
+             "| Kernel | Calls | Average (ms) | Min (ms) | Max (ms) |", "|---|---|---|---|---|"]
+    for r in stats:
+        if "chunkattn" not in r["Name"]:
+            continue
+        short = re.sub(r"\(.*", "", r["Name"]).replace("void ", "")
+        lines.append(f"| `{short}` | {r['Calls']} | {float(r['AverageNs']) / 1e6:.4f} | "
+                     f"{float(r['MinNs']) / 1e6:.4f} | {float(r['MaxNs']) / 1e6:.4f} |")
+    durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e6 for r in trace
+            if any(n in r["Kernel_Name"] for n in DOMINANT_NAMES)]
+    lines += ["", f"Dominant kernel `{DOMINANT}`: {len(durs)} dispatches in the trace, average "
+              f"{sum(durs) / len(durs):.4f} ms."]
+    out = {"kernel_sha256": kernel_source_hash()}
+    for counter, directory in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        vals, names = _counter_per_dispatch(directory, counter)
+        calib = [d for d in vals if "copyBuffer" in names[d] or "copy" in names[d].lower()]
+        cal = max(calib, key=lambda d: vals[d])
+        factor = CALIB_BYTES / (vals[cal] * 1024)
+        dom = sorted(d for d in vals if any(n in names[d] for n in DOMINANT_NAMES))
+        per = [vals[d] * 1024 * factor for d in dom]
+        out[counter] = {"calibration_kib": vals[cal], "factor": round(factor, 4), "dispatches": len(dom),
+                        "bytes_per_launch": sum(per) / len(per), "bytes_by_chunk": [round(x) for x in per]}
+        lines += ["", f"{counter}: the 1 GiB calibration copy (`{re.sub(r'[(<].*', '', names[cal])}`) counts "
+                  f"{vals[cal]:.0f} KiB, so bytes = KiB x 1024 x {factor:.4f}.  Dominant kernel, by launch: "
+                  + ", ".join(f"{x / 1e9:.2f} GB" for x in per) + f" (mean {sum(per) / len(per) / 1e9:.3f} GB)."]
+    out["bytes_per_launch"] = out["FETCH_SIZE"]["bytes_per_launch"] + out["WRITE_SIZE"]["bytes_per_launch"]
+    lines += ["", f"<!-- traffic {json.dumps(out)} -->"]
+    return "\n".join(lines) + "\n"
 
 
 class PrefillLoop:
@@ -206,6 +299,9 @@ def cpu_baseline(args, loop, torch):
 
 def main():
     args = parse()
+    if args.summarize_profile:
+        sys.stdout.write(summarize_profile(*args.summarize_profile))
+        return
     if args.gpus != 1:
         print(f"bench.py measures a single GPU; --gpus {args.gpus} is not supported: the attention path here "
               "runs on one MI355X and has no multi-GPU mode.", file=sys.stderr)
@@ -284,12 +380,22 @@ def main():
     dec_gbps = dec_only.decode_bytes / (dec_ms / 1e3) / 1e9
     log(f"decode-only {dec_ms:.3f} ms = {dec_gbps:.0f} GB/s; mixed prefill-only {pre_ms:.3f} ms")
 
+    if args.copy_calibration:
+        src = torch.empty(CALIB_BYTES, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log("calibration copy of 1 GiB done")
+
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the fp64 oracle on a bounded sample")
         cpu = cpu_baseline(args, loop, torch)
 
     w = loop.w
+    traffic, traffic_note = recorded_traffic()
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -317,14 +423,17 @@ def main():
         "prefill_chunk_loop": {"ms": round(sum(per_chunk), 3), "tflops": round(prefill_tflops, 1)},
         "roofline": {
             "bound": "mfma",
-            "kernel": "prefill_kernel<bf16, bf16, 128, 128, paged> (chunk loop launches)",
+            "kernel": DOMINANT,
             "achieved": round(prefill_tflops, 1),
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(prefill_tflops / PEAK_BF16_TFLOPS, 4),
             "avg_launch_ms": round(sum(per_chunk) / n_chunks, 4),
             "avg_causal_flops_per_launch": sum(loop.flops) / n_chunks,
-            "traffic": None,
+            "traffic": round(traffic["bytes_per_launch"]) if traffic else None,
+            "traffic_note": ("HBM-side bytes per launch (L2 misses to the fabric, MALL hits included) from "
+                             f"rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled by a 1 GiB copy; {TRAFFIC_SUMMARY}"
+                             if traffic else traffic_note),
         },
         "mixed_batch": {
             "ms": round(median(mixed_ms), 4),
