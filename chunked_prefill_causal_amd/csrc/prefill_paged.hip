@@ -10,11 +10,14 @@
 //  * Tiles move HBM/L2 -> LDS by direct-to-LDS loads (global_load_lds_dwordx4):
 //    no staging registers, no LDS write instructions.  Four LDS stages (three
 //    at d = 192) give each load two tile-times to land; one barrier per tile.
-//    Only the four leading waves issue them, right after the barrier, so the
-//    tile lands while those waves stream their matrix work; measured on
-//    MI355X, data landing in LDS during the trailing waves' matrix phase
-//    stalls their operand reads, and loads issued by the trailing waves queue
-//    behind the leading ones on their critical path.  The vector-memory
+//    Only the four leading waves issue them, one load after every fourth MFMA
+//    of their matrix phase.  Measured on MI355X, the direct-to-LDS path drains
+//    ~40 B/clk per CU, so a tile issued as a burst holds the issuing wave at
+//    issue for several hundred cycles; that delayed the leading waves' matrix
+//    phase into the trailing waves' and the trailing waves, younger, lost the
+//    matrix cores to them.  Spread out, the loads never stall issue.  The
+//    first interval of a workgroup, which has no matrix phase before its
+//    barrier, still issues its tile as a burst.  The vector-memory
 //    counter is managed by hand: inside the key loop the only vector-memory
 //    operations are these loads (block-table entries come through the scalar
 //    unit, one tile ahead), so "s_waitcnt vmcnt(N)" with N = loads of the
@@ -176,6 +179,28 @@ __global__ __launch_bounds__(512, 1) void prefill_paged_kernel(const PrefillArgs
       load_to_lds16(vb + (chunk + lane) * 16, __builtin_amdgcn_readfirstlane(ks + C::KBytes + chunk * 16));
     }
   };
+  // The same transfer spread over the leading waves' matrix phase: prep() fixes
+  // the tile and stage, dma_one(j) moves this thread's j-th 16-byte chunk
+  // (K chunks first, then V).  Issued in a burst, the loads would hold the wave
+  // for as long as the direct-to-LDS path needs to drain a tile; one load per
+  // four MFMAs stays under that rate, so the wave never waits at issue.
+  const unsigned char* pend_k = kpool;
+  const unsigned char* pend_v = vpool;
+  uint32_t pend_lds = 0;
+  auto prep = [&](int32_t block_id, int st) {
+    const int phys = clamp_block(block_id, a.num_blocks);
+    const int64_t tile = (int64_t)phys * a.kv_heads + g;
+    pend_k = kpool + tile * C::KBytes + (wave * 64 + lane) * 16;
+    pend_v = vpool + tile * C::VBytes + (wave * 64 + lane) * 16;
+    pend_lds = smem_base + st * C::Stage + wave * 64 * 16;
+  };
+  auto dma_one = [&](int j) {
+    if (j < C::KPT)
+      load_to_lds16(pend_k + j * C::kLoaders * 16, __builtin_amdgcn_readfirstlane(pend_lds + j * C::kLoaders * 16));
+    else
+      load_to_lds16(pend_v + (j - C::KPT) * C::kLoaders * 16,
+                    __builtin_amdgcn_readfirstlane(pend_lds + C::KBytes + (j - C::KPT) * C::kLoaders * 16));
+  };
 
   f32x16_t o[C::NB];
 #pragma unroll
@@ -308,6 +333,49 @@ __global__ __launch_bounds__(512, 1) void prefill_paged_kernel(const PrefillArgs
     __builtin_amdgcn_sched_group_barrier(0x008, kLead, 0);
   };
 
+  // pv_qk for the leading waves with the pending tile's loads interleaved: the
+  // operand reads are software-pipelined by hand (kAhead in flight) and one
+  // load goes out after every fourth MFMA, fenced so the order stays as written.
+  auto pv_qk_dma = [&](int st_prev, int st_cur, bool with_dma) {
+    const unsigned char* vb = stage_ptr(st_prev) + v_lane;
+    const unsigned char* kb = stage_ptr(st_cur) + k_lane;
+    constexpr int kPv = 4 * C::NB, kQk = 2 * C::NQ, kOps = kPv + kQk, kAhead = 6;
+    // op k: PV and QK alternate while both remain, then the rest of QK
+    auto is_pv = [&](int k) { return k < 2 * kPv ? (k & 1) == 0 : false; };
+    auto op_ptr = [&](int k) -> const u32x4_t* {
+      if (is_pv(k)) {
+        const int u = k >> 1, stp = u / C::NB, b = u % C::NB;
+        return (const u32x4_t*)(vb + (2 * stp * DV + 32 * b) * 16);
+      }
+      const int q = k < 2 * kPv ? (k >> 1) : k - kPv;      // QK step index
+      return (const u32x4_t*)(kb + (2 * (q >> 1) * kBlock + 32 * (q & 1)) * 16);
+    };
+    f32x16_t n0 = f32x16_t{}, n1 = f32x16_t{};
+    u32x4_t rd[kOps];
+#pragma unroll
+    for (int k = 0; k < kAhead; ++k) rd[k] = *op_ptr(k);
+#pragma unroll
+    for (int k = 0; k < kOps; ++k) {
+      if (is_pv(k)) {
+        const int u = k >> 1, stp = u / C::NB, b = u % C::NB;
+        o[b] = mfma_bf16(rd[k], pkv[stp], o[b]);
+      } else {
+        const int q = k < 2 * kPv ? (k >> 1) : k - kPv;
+        if (q & 1) n1 = mfma_bf16(rd[k], qreg[q >> 1], n1);
+        else n0 = mfma_bf16(rd[k], qreg[q >> 1], n0);
+      }
+      if (k + kAhead < kOps) rd[k + kAhead] = *op_ptr(k + kAhead);
+      if ((k & 3) == 3 && (k >> 2) < C::LPT) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (with_dma) dma_one(k >> 2);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    static_assert(kOps >= 4 * C::LPT, "one load per four MFMAs must fit in the matrix phase");
+    s0 = n0;
+    s1 = n1;
+  };
+
   // ---- key loop -------------------------------------------------------------------
   // Interval i (between two barriers) does, for every wave, PV of tile i-1,
   // QK of tile i and the softmax of the tile in between.  Waves 0-3 run
@@ -326,13 +394,18 @@ __global__ __launch_bounds__(512, 1) void prefill_paged_kernel(const PrefillArgs
   // Start of interval i: tile i must have landed (tiles i+1 .. i+NS-3 may
   // still be in flight); after the barrier the stage of tile i-2 is free and
   // receives tile i+NS-2.
+  bool pending = false;
   auto interval_start = [&](int i) {
     if (i < n) {
       if (min(NS - 3, n - 1 - i) >= 1) wait_vmem<C::LPT>();
       else wait_vmem<0>();
     }
     workgroup_barrier();
-    if (i + NS - 2 < n) issue(block_ahead, (i + NS - 2) % NS);
+    pending = i + NS - 2 < n;
+    if (pending) {
+      if (i == 0) issue(block_ahead, NS - 2);          // no matrix phase to hide it in
+      else prep(block_ahead, (i + NS - 2) % NS);       // issued inside pv_qk_dma
+    }
     block_ahead = (i + NS - 1 < n) ? bt4[j_lo + i + NS - 1] : 0;
     const int64_t key0 = (int64_t)(j_lo + i) * kBlock;
     if (i < n && key0 + kBlock > kv_len) {
@@ -363,7 +436,7 @@ __global__ __launch_bounds__(512, 1) void prefill_paged_kernel(const PrefillArgs
     __builtin_amdgcn_sched_barrier(0);
     for (int i = 1; i < n; ++i) {
       interval_start(i);
-      pv_qk((i - 1) % NS, i % NS);
+      pv_qk_dma((i - 1) % NS, i % NS, pending);
       __builtin_amdgcn_sched_barrier(0);
       softmax(j_lo + i);
       __builtin_amdgcn_sched_barrier(0);
