@@ -6,10 +6,10 @@ count), and seeded sampled rows are compared with the fp64 oracle, which
 reads the same inputs copied to the host.  The sample always includes each
 chunk's first and last token and tokens on both sides of tile boundaries.
 
-Row counts per chunk: 4096 for the 32K prompt, 1024 for the 128K prompt,
-256 for the 512K MLA-shaped prompt (4096 with CHUNKATTN_FULL_SAMPLES=1; the
-fp64 oracle needs ~10 CPU-minutes on 16 cores for that), every decode row and
-2048 prefill rows of the mixed batch.
+Row counts per chunk: 4096 for the 32K and 128K prompts, 256 for the 512K
+MLA-shaped prompt (4096 with CHUNKATTN_FULL_SAMPLES=1; the fp64 oracle needs
+~8 CPU-minutes on 16 cores for that), every decode row and 2048 prefill rows
+of the mixed batch (all 65536 with CHUNKATTN_FULL_SAMPLES=1).
 """
 import math
 import os
@@ -68,7 +68,7 @@ def test_gqa_32k_all_chunks():
 
 
 def test_gqa_128k_all_chunks():
-    run_prompt("gqa_128k", 1024)
+    run_prompt("gqa_128k", 4096)
 
 
 def test_mla_512k_all_chunks():
@@ -114,7 +114,11 @@ def test_mixed_batch_full_size():
         worst_lse = max(worst_lse, max_err(lse[:, row], ref_lse))
     log(f"mixed: 256 decode requests x {hq} heads, max err {worst:.3e}, lse err {worst_lse:.2e}")
     # sampled prefill rows
-    tok, head = inputs.sample_rows(w.chunk_len, hq, 2048, w.seed * 13)
+    if FULL:    # every (token, head) row of the chunk
+        tok = np.repeat(np.arange(w.chunk_len, dtype=np.int64), hq)
+        head = np.tile(np.arange(hq, dtype=np.int32), w.chunk_len)
+    else:
+        tok, head = inputs.sample_rows(w.chunk_len, hq, 2048, w.seed * 13)
     ref, ref_lse = oracle_rows(q_host[: w.chunk_len], kv_host[0][0], kv_host[0][1], w.prefill_past, w.scale,
                                tok, head)
     ti, hi = torch.from_numpy(tok).cuda(), torch.from_numpy(head.astype(np.int64)).cuda()
