@@ -256,6 +256,22 @@ def fit_line(ks, ts):
     return a, b, 1 - ss_res / ss_tot if ss_tot else 1.0
 
 
+def schedule_summary(L, tau):
+    """Two-rank CPP / VPP / VPP-Async schedules (VPP review §4.2-§4.5) driven by the measured per-chunk
+    latencies: one request, and two back-to-back requests with and without Alg. 2 packing."""
+    out = {"tau_ms": [round(x, 4) for x in tau], "comm_ms": 0.0}
+    names = {L.CA_SCHED_CPP: "cpp", L.CA_SCHED_VPP: "vpp", L.CA_SCHED_VPP_ASYNC: "vpp_async"}
+    for kind, name in names.items():
+        one = L.chunkattn_sched_simulate(kind, tau)
+        two = {p: L.chunkattn_sched_simulate(kind, list(tau) * 2, request=[0] * len(tau) + [1] * len(tau), pack=p)
+               for p in (False, True)}
+        bubble = lambda r: 1.0 - float(r["busy"].sum()) / (2 * r["makespan"])
+        out[name] = {"makespan_ms": round(one["makespan"], 3), "bubble_frac": round(bubble(one), 4),
+                     "two_requests_ms": round(two[False]["makespan"], 3),
+                     "two_requests_packed_ms": round(two[True]["makespan"], 3)}
+    return out
+
+
 def cpu_baseline(args, loop, torch):
     """The fp64 oracle, as it stands, on a bounded sample of the same workload (host cores)."""
     import numpy as np
@@ -389,6 +405,10 @@ def main():
         del src, dst
         log("calibration copy of 1 GiB done")
 
+    sched = schedule_summary(L, per_chunk)
+    log(f"schedules on the measured chunk latencies: CPP {sched['cpp']['makespan_ms']} ms, "
+        f"VPP {sched['vpp']['makespan_ms']} ms, VPP-Async {sched['vpp_async']['makespan_ms']} ms")
+
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the fp64 oracle on a bounded sample")
@@ -444,6 +464,7 @@ def main():
                                 "unit": "GB/s", "frac": round(dec_gbps / PEAK_HBM_GBPS, 4),
                                 "algorithmic_bytes": mixed.decode_bytes},
         },
+        "schedule_sim": sched,
         "cpu_baseline": cpu,
     }
     print(json.dumps(result), flush=True)

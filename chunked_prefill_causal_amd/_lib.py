@@ -20,11 +20,13 @@ LIB_PATH = os.path.join(_HERE, "libchunkattn.so")
 CA_OK, CA_EINVAL, CA_EUNSUPPORTED, CA_ERANGE, CA_EWORKSPACE, CA_EHIP = 0, -1, -2, -3, -4, -5
 CA_F32, CA_BF16 = 0, 1
 CA_KV_CONTIGUOUS, CA_KV_PAGED = 0, 1
+CA_SCHED_CPP, CA_SCHED_VPP, CA_SCHED_VPP_ASYNC = 0, 1, 2
 BLOCK_SIZE = 64
 
 EXPORTED = ("ca_prefill_opts_init", "chunk_prefill_attn", "chunkattn_prefill_workspace_size",
             "chunkattn_prefill_auto_splits", "chunk_attn_varlen", "chunkattn_varlen_workspace_size",
-            "chunkattn_kv_append", "chunkattn_last_error", "chunkattn_version")
+            "chunkattn_kv_append", "chunkattn_sched_simulate", "chunkattn_sched_drain_pack",
+            "chunkattn_last_error", "chunkattn_version")
 
 
 class ChunkAttnError(RuntimeError):
@@ -69,6 +71,11 @@ def lib() -> ctypes.CDLL:
     L.chunkattn_varlen_workspace_size.restype = sz
     L.chunkattn_kv_append.argtypes = [vp, vp, i64, i64, i32, i32, i32, ctypes.c_int, vp, i32, i32, vp, vp, vp]
     L.chunkattn_kv_append.restype = ctypes.c_int
+    f64 = ctypes.c_double
+    L.chunkattn_sched_simulate.argtypes = [i32, i32, vp, vp, f64, i32, vp, vp, vp, vp]
+    L.chunkattn_sched_simulate.restype = ctypes.c_int
+    L.chunkattn_sched_drain_pack.argtypes = [i32, f64, i32, vp, vp]
+    L.chunkattn_sched_drain_pack.restype = i32
     L.chunkattn_last_error.argtypes = []
     L.chunkattn_last_error.restype = ctypes.c_char_p
     L.chunkattn_version.argtypes = []
@@ -114,6 +121,40 @@ def paged_pool(num_blocks: int, kv_heads: int, head_dim: int, head_dim_v: int, d
 
 def version() -> int:
     return lib().chunkattn_version()
+
+
+def chunkattn_sched_simulate(kind: int, tau, comm: float = 0.0, request=None, pack: bool = True) -> dict:
+    """Two-rank CPP / VPP / VPP-Async schedule of chunks with per-stage latencies ``tau`` (host only).
+
+    Returns start and end times of every (chunk, virtual stage) as ``[n, 4]``
+    float64 arrays, the busy time of each rank and the makespan.
+    """
+    import numpy as np
+
+    t = np.ascontiguousarray(tau, dtype=np.float64)
+    n = t.shape[0]
+    req = None if request is None else np.ascontiguousarray(request, dtype=np.int32)
+    start = np.empty((n, 4), dtype=np.float64)
+    end = np.empty((n, 4), dtype=np.float64)
+    busy = np.empty(2, dtype=np.float64)
+    span = ctypes.c_double()
+    _check(lib().chunkattn_sched_simulate(kind, n, t.ctypes.data if n else None,
+                                          None if req is None else req.ctypes.data, float(comm), int(bool(pack)),
+                                          start.ctypes.data, end.ctypes.data, busy.ctypes.data, ctypes.byref(span)))
+    return {"start": start, "end": end, "busy": busy, "makespan": span.value}
+
+
+def chunkattn_sched_drain_pack(n_chunks: int, t: float, tau_next) -> tuple[int, float]:
+    """Alg. 2: leading chunks of the next request that fit in the (N + 1) t drain window, and what is left."""
+    import numpy as np
+
+    tn = np.ascontiguousarray(tau_next, dtype=np.float64)
+    left = ctypes.c_double()
+    j = lib().chunkattn_sched_drain_pack(n_chunks, float(t), tn.shape[0], tn.ctypes.data if tn.shape[0] else None,
+                                         ctypes.byref(left))
+    if j < 0:
+        _check(j)
+    return j, left.value
 
 
 def chunkattn_prefill_workspace_size(chunk_len: int, heads: int, head_dim_v: int, num_splits: int) -> int:

@@ -135,6 +135,17 @@ ca_status check_dtype(int d) {
 
 }  // namespace
 
+namespace chunkattn {
+// Error string of the calling thread, shared with the host-only entry points.
+void set_error(const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+}
+void clear_error() { g_err[0] = '\0'; }
+}  // namespace chunkattn
+
 extern "C" {
 
 void ca_prefill_opts_init(ca_prefill_opts* o) {

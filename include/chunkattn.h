@@ -192,6 +192,52 @@ ca_status chunkattn_kv_append(const void* k_new, const void* v_new, int64_t star
                               const int32_t* block_table, int32_t block_table_len, int32_t num_blocks,
                               void* k_pool, void* v_pool, void* stream);
 
+/*
+ * Pipeline schedules that chunked prefill feeds (host only: no GPU work, no
+ * stream).  VPP technical review (English edition) §4.1 Eq. (2) (per-stage
+ * chunk latency tau_k, near-linear in k), §4.2 Alg. 1 / Eq. (3a)-(3b) (the
+ * V-shaped layout: s0, s3 on rank pp0 and s1, s2 on pp1; while pp1 runs chunk
+ * k's middle stages pp0 runs s3 of chunk k-1, then s0 of chunk k+1), §4.4
+ * (VPP-Async: pp0's pair issued the other way round), §2.4 (the conventional
+ * layout: s0, s1 on pp0, s2, s3 on pp1) and §4.5 Alg. 2 / Eq. (4a) (the next
+ * request's leading chunks packed into the (N + 1) t drain window).
+ */
+typedef enum { CA_SCHED_CPP = 0, CA_SCHED_VPP = 1, CA_SCHED_VPP_ASYNC = 2 } ca_sched_kind;
+
+/*
+ * chunkattn_sched_simulate — start and end time of every virtual stage of
+ * n_chunks chunks on two ranks.
+ *   kind            ca_sched_kind.
+ *   tau[n_chunks]   host, per-virtual-stage latency of each chunk (finite, >= 0, any time unit).
+ *   request         host int32 [n_chunks], non-decreasing request id of each chunk, or NULL (one request).
+ *   comm            delay of a hand-off between the two ranks (same unit, >= 0); it occupies neither rank.
+ *   pack            0: a request's first stage waits for the previous request's last stage.
+ *                   1: under the V layouts the next request's leading entry stages (count from
+ *                      chunkattn_sched_drain_pack with t = the current request's first tau) run in
+ *                      pp0's drain slot before the current request's last exit stage; under CPP the
+ *                      barrier between requests is simply dropped.
+ *   stage_start, stage_end   host double [n_chunks * 4] (chunk-major, stage minor) or NULL.
+ *   rank_busy       host double [2] or NULL: summed stage time of pp0 and pp1.
+ *   makespan        host double, required: the last stage's end time.
+ * Every stage of chunk k takes tau[k]; a stage starts when its rank has
+ * finished the stage before it in the rank's order and the chunk's previous
+ * stage has ended (plus comm when that stage ran on the other rank).
+ * Returns CA_OK or CA_EINVAL.  All buffers belong to the caller.
+ */
+ca_status chunkattn_sched_simulate(int32_t kind, int32_t n_chunks, const double* tau, const int32_t* request,
+                                   double comm, int32_t pack, double* stage_start, double* stage_end,
+                                   double* rank_busy, double* makespan);
+
+/*
+ * chunkattn_sched_drain_pack — Alg. 2 / Eq. (4a): the number of leading
+ * chunks of the next request (host tau_next[n_next]) whose latencies fit,
+ * in order, into the drain window (n_chunks + 1) * t of the current request;
+ * stops at the first chunk that does not fit.  *window_left (optional)
+ * receives what is left of the window.  Returns the count (>= 0) or CA_EINVAL.
+ */
+int32_t chunkattn_sched_drain_pack(int32_t n_chunks, double t, int32_t n_next, const double* tau_next,
+                                   double* window_left);
+
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* chunkattn_last_error(void);
 
