@@ -272,6 +272,78 @@ def schedule_summary(L, tau):
     return out
 
 
+def latency_predictor(L, loop, torch, reps=3):
+    """ALP-style attention-latency predictor (FastPP notes §2.3) fitted to this kernel's own timings.
+
+    Batches on the 128K prompt's cache (64 q / 8 KV heads, d 128): single prefill chunks over a grid of
+    (past, chunk) sizes, decode-only batches and mixed batches, all through the varlen entry.  A seeded
+    half trains the library's recursive least-squares fit, the other half is held out; the token-count-only
+    model (constant + total new tokens) is fitted the same way for comparison."""
+    import numpy as np
+
+    w = loop.w
+    rng = np.random.default_rng(w.seed + 17)
+    cases = []
+    for c in (512, 1024, 2048, 4096, 8192, 16384):
+        for past in (0, 8192, 24576, 49152, 81920, 114688):
+            if past + c <= w.seq_len:
+                cases.append(([c], [past + c]))
+    for m in (16, 64, 128, 256):
+        cases.append(([1] * m, rng.integers(1024, w.seq_len + 1, m).tolist()))
+        for c in (1024, 4096):
+            past = int(rng.integers(0, w.seq_len - c + 1))
+            cases.append(([c] + [1] * m, [past + c] + rng.integers(1024, w.seq_len + 1, m).tolist()))
+    max_q = max(sum(q) for q, _ in cases)
+    max_s = max(len(q) for q, _ in cases)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(w.seed + 18)
+    q_buf = torch.randn((max_q, w.heads, w.head_dim), generator=gen, device="cuda").to(torch.bfloat16)
+    out_buf = torch.empty((max_q, w.heads, w.head_dim_v), dtype=torch.bfloat16, device="cuda")
+    tables = loop.table.unsqueeze(0).expand(max_s, -1).contiguous()
+    times = []
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for q_lens, kv_lens in cases:
+        n, tq = len(q_lens), sum(q_lens)
+        cu = [0]
+        for x in q_lens:
+            cu.append(cu[-1] + x)
+        ws = torch.empty(max(L.chunkattn_varlen_workspace_size(cu, kv_lens, w.heads, w.kv_heads, w.head_dim_v), 1),
+                         dtype=torch.uint8, device="cuda")
+        cu_d = torch.tensor(cu, dtype=torch.int32, device="cuda")
+        kv_d = torch.tensor(kv_lens, dtype=torch.int32, device="cuda")
+        run = lambda: L.chunk_attn_varlen(q_buf[:tq], loop.k, loop.v, tables[:n], cu, kv_lens, w.scale,
+                                          out=out_buf[:tq], workspace=ws, cu_seqlens_q_dev=cu_d, kv_lens_dev=kv_d)
+        run()
+        ts = []
+        for _ in range(reps):
+            e0.record()
+            run()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        times.append(median(ts))
+    order = rng.permutation(len(cases))
+    train, test = order[: len(cases) // 2], order[len(cases) // 2:]
+    fits = {}
+    # The times span three orders of magnitude and the score is relative, so each observation is
+    # weighted by 1/T^2: the fit sees x / T with target 1 (relative least squares).
+    for name, feat in (("token_count_only", lambda q, kv: [1.0, sum(q) / 1e3, 0.0, 0.0]),
+                       ("alp_features", lambda q, kv: list(L.chunkattn_alp_features(q, kv)))):
+        model = L.AlpPredictor(1.0, 1e6)
+        for i in train:
+            model.update([v / times[i] for v in feat(*cases[i])], 1.0)
+        err = [abs(model.predict(feat(*cases[i])) - times[i]) / times[i] for i in test]
+        fits[name] = {"mape_holdout": round(float(np.mean(err)), 4), "max_ape": round(float(np.max(err)), 4),
+                      "theta": [round(t, 6) for t in model.theta]}
+    samples = [[sum(q), len(q)] + [round(v, 6) for v in L.chunkattn_alp_features(q, kv)[1:]] + [round(t, 5)]
+               for (q, kv), t in zip(cases, times)]
+    return {"cases": len(cases), "train": len(train), "holdout": len(test), "unit": "ms",
+            "features": "[1, sum(L_past*L_pre)/1e6, sum(L_pre^2)/1e6, sum(L_dec)/1e3]",
+            "fit": "recursive least squares on x/T -> 1 (relative error), lambda 1, delta 1e6", **fits,
+            "samples": {"columns": ["new_tokens", "sequences", "past_x_pre_M", "pre_sq_M", "dec_ctx_K", "ms"],
+                        "rows": samples}}
+
+
 def cpu_baseline(args, loop, torch):
     """The fp64 oracle, as it stands, on a bounded sample of the same workload (host cores)."""
     import numpy as np
@@ -405,6 +477,10 @@ def main():
         del src, dst
         log("calibration copy of 1 GiB done")
 
+    log("timing the latency-predictor grid")
+    alp = latency_predictor(L, loop, torch)
+    log(f"latency predictor held-out MAPE: token count only {alp['token_count_only']['mape_holdout']:.3f}, "
+        f"ALP features {alp['alp_features']['mape_holdout']:.3f}")
     sched = schedule_summary(L, per_chunk)
     log(f"schedules on the measured chunk latencies: CPP {sched['cpp']['makespan_ms']} ms, "
         f"VPP {sched['vpp']['makespan_ms']} ms, VPP-Async {sched['vpp_async']['makespan_ms']} ms")
@@ -465,6 +541,7 @@ def main():
                                 "algorithmic_bytes": mixed.decode_bytes},
         },
         "schedule_sim": sched,
+        "latency_predictor": alp,
         "cpu_baseline": cpu,
     }
     print(json.dumps(result), flush=True)

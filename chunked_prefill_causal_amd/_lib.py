@@ -26,6 +26,7 @@ BLOCK_SIZE = 64
 EXPORTED = ("ca_prefill_opts_init", "chunk_prefill_attn", "chunkattn_prefill_workspace_size",
             "chunkattn_prefill_auto_splits", "chunk_attn_varlen", "chunkattn_varlen_workspace_size",
             "chunkattn_kv_append", "chunkattn_sched_simulate", "chunkattn_sched_drain_pack",
+            "chunkattn_alp_features", "chunkattn_alp_init", "chunkattn_alp_predict", "chunkattn_alp_update",
             "chunkattn_last_error", "chunkattn_version")
 
 
@@ -42,6 +43,14 @@ class PrefillOpts(ctypes.Structure):
                 ("num_blocks", ctypes.c_int32), ("lse_out", ctypes.c_void_p),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
                 ("num_splits", ctypes.c_int32)]
+
+
+ALP_FEATURES = 4
+
+
+class AlpState(ctypes.Structure):
+    _fields_ = [("theta", ctypes.c_double * ALP_FEATURES), ("info", ctypes.c_double * (ALP_FEATURES * ALP_FEATURES)),
+                ("rhs", ctypes.c_double * ALP_FEATURES), ("lambda_", ctypes.c_double), ("n_obs", ctypes.c_int64)]
 
 
 _lib = None
@@ -76,6 +85,14 @@ def lib() -> ctypes.CDLL:
     L.chunkattn_sched_simulate.restype = ctypes.c_int
     L.chunkattn_sched_drain_pack.argtypes = [i32, f64, i32, vp, vp]
     L.chunkattn_sched_drain_pack.restype = i32
+    L.chunkattn_alp_features.argtypes = [i32, vp, vp, vp]
+    L.chunkattn_alp_features.restype = ctypes.c_int
+    L.chunkattn_alp_init.argtypes = [ctypes.POINTER(AlpState), f64, f64]
+    L.chunkattn_alp_init.restype = ctypes.c_int
+    L.chunkattn_alp_predict.argtypes = [ctypes.POINTER(AlpState), vp]
+    L.chunkattn_alp_predict.restype = f64
+    L.chunkattn_alp_update.argtypes = [ctypes.POINTER(AlpState), vp, f64, vp]
+    L.chunkattn_alp_update.restype = ctypes.c_int
     L.chunkattn_last_error.argtypes = []
     L.chunkattn_last_error.restype = ctypes.c_char_p
     L.chunkattn_version.argtypes = []
@@ -142,6 +159,44 @@ def chunkattn_sched_simulate(kind: int, tau, comm: float = 0.0, request=None, pa
                                           None if req is None else req.ctypes.data, float(comm), int(bool(pack)),
                                           start.ctypes.data, end.ctypes.data, busy.ctypes.data, ctypes.byref(span)))
     return {"start": start, "end": end, "busy": busy, "makespan": span.value}
+
+
+def chunkattn_alp_features(q_lens, kv_lens):
+    """ALP feature vector of a batch (FastPP notes §2.3): [1, sum Lpast*Lpre/1e6, sum Lpre^2/1e6, sum Ldec/1e3]."""
+    import numpy as np
+
+    q = np.ascontiguousarray(q_lens, dtype=np.int32)
+    kv = np.ascontiguousarray(kv_lens, dtype=np.int32)
+    x = np.empty(ALP_FEATURES, dtype=np.float64)
+    _check(lib().chunkattn_alp_features(q.shape[0], q.ctypes.data if q.shape[0] else None,
+                                        kv.ctypes.data if kv.shape[0] else None, x.ctypes.data))
+    return x
+
+
+class AlpPredictor:
+    """Recursive least-squares fit of the ALP coefficients (information form), state in the library's struct."""
+
+    def __init__(self, lam: float = 1.0, delta: float = 1e6):
+        self.state = AlpState()
+        _check(lib().chunkattn_alp_init(ctypes.byref(self.state), float(lam), float(delta)))
+
+    def predict(self, x) -> float:
+        import numpy as np
+
+        xv = np.ascontiguousarray(x, dtype=np.float64)
+        return lib().chunkattn_alp_predict(ctypes.byref(self.state), xv.ctypes.data)
+
+    def update(self, x, measured: float) -> float:
+        import numpy as np
+
+        xv = np.ascontiguousarray(x, dtype=np.float64)
+        err = ctypes.c_double()
+        _check(lib().chunkattn_alp_update(ctypes.byref(self.state), xv.ctypes.data, float(measured), ctypes.byref(err)))
+        return err.value
+
+    @property
+    def theta(self):
+        return list(self.state.theta)
 
 
 def chunkattn_sched_drain_pack(n_chunks: int, t: float, tau_next) -> tuple[int, float]:

@@ -238,6 +238,47 @@ ca_status chunkattn_sched_simulate(int32_t kind, int32_t n_chunks, const double*
 int32_t chunkattn_sched_drain_pack(int32_t n_chunks, double t, int32_t n_next, const double* tau_next,
                                    double* window_left);
 
+/*
+ * Online attention-latency predictor (host only).  "Revisiting Pipeline
+ * Parallelism for LLM Serving" paper notes §2.3 (ALP): the attention time of
+ * a batch is linear in three features summed over its sequences — past
+ * context x new prefill tokens, new tokens squared, and the context of each
+ * decode request — with coefficients adapted online by recursive least
+ * squares with a forgetting factor.  For the kernel alone a constant term
+ * replaces the notes' offline token-linear part:
+ *   x = [1, sum(L_past * L_pre) / 1e6, sum(L_pre^2) / 1e6, sum(L_dec) / 1e3]
+ * where a sequence with q_len > 1 is a prefill chunk (L_pre = q_len,
+ * L_past = kv_len - q_len) and one with q_len == 1 a decode (L_dec = kv_len).
+ */
+#define CA_ALP_FEATURES 4
+typedef struct {
+  double theta[CA_ALP_FEATURES];                     /* coefficients, time unit of the measurements */
+  double info[CA_ALP_FEATURES * CA_ALP_FEATURES];    /* weighted normal matrix R (inverse covariance), row-major */
+  double rhs[CA_ALP_FEATURES];                       /* weighted right-hand side b */
+  double lambda;                                     /* forgetting factor, 0 < lambda <= 1 */
+  int64_t n_obs;                                     /* updates so far */
+} ca_alp_state;
+
+/* Feature vector x[CA_ALP_FEATURES] of a batch (host arrays q_lens, kv_lens of
+ * num_seqs sequences, kv_len >= q_len >= 0).  CA_OK or CA_EINVAL. */
+ca_status chunkattn_alp_features(int32_t num_seqs, const int32_t* q_lens, const int32_t* kv_lens, double* x);
+
+/* Start a recursive least-squares fit: theta = 0, R = I / delta (covariance delta * I), b = 0.
+ * CA_OK or CA_EINVAL. */
+ca_status chunkattn_alp_init(ca_alp_state* state, double lambda, double delta);
+
+/* Predicted time theta . x (NaN for NULL arguments). */
+double chunkattn_alp_predict(const ca_alp_state* state, const double* x);
+
+/* One recursive least-squares step with a measured time, in information form:
+ * R = lambda R + x x', b = lambda b + x measured, theta = R^-1 b (Cholesky) —
+ * the estimate of the gain form g = P x / (lambda + x' P x), theta += g e,
+ * P = (P - g x' P) / lambda with P = R^-1, without its loss of precision.
+ * *prior_error (optional) receives measured - theta . x before the step.
+ * CA_OK, CA_EINVAL, or CA_ERANGE if R stopped being positive definite.
+ * The state belongs to the caller; calls on one state must not overlap. */
+ca_status chunkattn_alp_update(ca_alp_state* state, const double* x, double measured, double* prior_error);
+
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* chunkattn_last_error(void);
 
