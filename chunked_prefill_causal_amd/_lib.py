@@ -21,13 +21,16 @@ CA_OK, CA_EINVAL, CA_EUNSUPPORTED, CA_ERANGE, CA_EWORKSPACE, CA_EHIP = 0, -1, -2
 CA_F32, CA_BF16 = 0, 1
 CA_KV_CONTIGUOUS, CA_KV_PAGED = 0, 1
 CA_SCHED_CPP, CA_SCHED_VPP, CA_SCHED_VPP_ASYNC = 0, 1, 2
+CA_MLA_BF16, CA_MLA_FP8 = 0, 1
 BLOCK_SIZE = 64
+MLA_LATENT, MLA_ROPE = 512, 64
 
 EXPORTED = ("ca_prefill_opts_init", "chunk_prefill_attn", "chunkattn_prefill_workspace_size",
             "chunkattn_prefill_auto_splits", "chunk_attn_varlen", "chunkattn_varlen_workspace_size",
             "chunkattn_kv_append", "chunkattn_sched_simulate", "chunkattn_sched_drain_pack",
             "chunkattn_alp_features", "chunkattn_alp_init", "chunkattn_alp_predict", "chunkattn_alp_update",
-            "chunkattn_last_error", "chunkattn_version")
+            "chunkattn_mla_block_bytes", "chunkattn_mla_decode_workspace_size", "chunkattn_mla_kv_append",
+            "chunk_mla_decode", "chunkattn_last_error", "chunkattn_version")
 
 
 class ChunkAttnError(RuntimeError):
@@ -93,6 +96,14 @@ def lib() -> ctypes.CDLL:
     L.chunkattn_alp_predict.restype = f64
     L.chunkattn_alp_update.argtypes = [ctypes.POINTER(AlpState), vp, f64, vp]
     L.chunkattn_alp_update.restype = ctypes.c_int
+    L.chunkattn_mla_block_bytes.argtypes = [i32]
+    L.chunkattn_mla_block_bytes.restype = sz
+    L.chunkattn_mla_decode_workspace_size.argtypes = [vp, i32, i32, i32]
+    L.chunkattn_mla_decode_workspace_size.restype = sz
+    L.chunkattn_mla_kv_append.argtypes = [vp, vp, i64, i64, i32, vp, i32, i32, vp, vp]
+    L.chunkattn_mla_kv_append.restype = ctypes.c_int
+    L.chunk_mla_decode.argtypes = [vp, vp, i32, vp, i32, i32, vp, vp, i32, i32, f32, vp, vp, vp, sz, vp]
+    L.chunk_mla_decode.restype = ctypes.c_int
     L.chunkattn_last_error.argtypes = []
     L.chunkattn_last_error.restype = ctypes.c_char_p
     L.chunkattn_version.argtypes = []
@@ -333,3 +344,51 @@ def chunkattn_kv_append(k_new, v_new, start_pos: int, block_table, k_pool, v_poo
                                      _ptr(block_table), block_table.numel(),
                                      k_pool.shape[0] if num_blocks is None else num_blocks,
                                      _ptr(k_pool), _ptr(v_pool), _stream(stream)))
+
+
+def chunkattn_mla_block_bytes(fmt: int) -> int:
+    return lib().chunkattn_mla_block_bytes(fmt)
+
+
+def mla_pool(num_blocks: int, fmt: int, device="cuda"):
+    """Allocate (uninitialised) a paged MLA latent pool of ``num_blocks`` 64-token blocks, as bytes."""
+    nbytes = chunkattn_mla_block_bytes(fmt)
+    if nbytes == 0:
+        raise ValueError(f"unknown MLA cache format {fmt}")
+    return torch.empty((num_blocks, nbytes), dtype=torch.uint8, device=device)
+
+
+def chunkattn_mla_kv_append(latent, rope, start_pos: int, block_table, pool, fmt: int, *,
+                            num_blocks: int | None = None, stream=None) -> None:
+    """Write ``latent [n, 512]`` / ``rope [n, 64]`` (bf16) at positions start_pos.. of one sequence."""
+    n = latent.shape[0]
+    _check(lib().chunkattn_mla_kv_append(_ptr(latent), _ptr(rope), start_pos, n, fmt, _ptr(block_table),
+                                         block_table.numel(), pool.shape[0] if num_blocks is None else num_blocks,
+                                         _ptr(pool), _stream(stream)))
+
+
+def chunkattn_mla_decode_workspace_size(kv_lens, heads: int, fmt: int) -> int:
+    kv = _host_i32(kv_lens)
+    return lib().chunkattn_mla_decode_workspace_size(kv.data_ptr(), kv.numel(), heads, fmt)
+
+
+def chunk_mla_decode(q, pool, fmt: int, block_tables, kv_lens, scale: float, *, num_blocks: int | None = None,
+                     out=None, return_lse: bool = False, lse=None, workspace=None, kv_lens_dev=None, stream=None):
+    """Absorbed MLA decode: ``q [num_seqs, heads, 576]`` bf16 against the latent pool; returns
+    ``out [num_seqs, heads, 512]`` bf16 (and ``lse [heads, num_seqs]`` fp32)."""
+    n, heads, _ = q.shape
+    kv = _host_i32(kv_lens)
+    if kv_lens_dev is None:
+        kv_lens_dev = kv.to(q.device)
+    if out is None:
+        out = torch.empty((n, heads, MLA_LATENT), dtype=torch.bfloat16, device=q.device)
+    if return_lse and lse is None:
+        lse = torch.empty((heads, n), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        need = lib().chunkattn_mla_decode_workspace_size(kv.data_ptr(), n, heads, fmt)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(lib().chunk_mla_decode(
+        _ptr(q), _ptr(pool), fmt, _ptr(block_tables), block_tables.shape[1],
+        pool.shape[0] if num_blocks is None else num_blocks, _ptr(kv_lens_dev), kv.data_ptr(), n, heads,
+        float(scale), _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return (out, lse) if return_lse else out

@@ -146,6 +146,50 @@ void set_error(const char* fmt, ...) {
 void clear_error() { g_err[0] = '\0'; }
 }  // namespace chunkattn
 
+namespace {
+
+// MLA latent decode plan: keys per split (a multiple of the 32-key step) so
+// that about four rounds of waves fill the chip (2 bf16 / 3 fp8 waves per CU
+// fit their double-buffered LDS), and the largest split count of any sequence.
+struct MlaPlan {
+  int split_tokens = 0, max_splits = 0;
+  size_t o_bytes = 0, bytes = 0;
+};
+MlaPlan plan_mla(const int32_t* kv_lens, int num_seqs, int heads, bool fp8) {
+  MlaPlan p;
+  int64_t units = 0;
+  for (int s = 0; s < num_seqs; ++s) units += (int64_t)(kv_lens[s] + kMlaStepKeys - 1) / kMlaStepKeys;
+  units *= heads / 16;
+  const int64_t target = (int64_t)kNumCUs * (fp8 ? 3 : 2) * 4;
+  int64_t steps = (units + target - 1) / target;
+  steps = steps < 4 ? 4 : (steps > 4096 ? 4096 : steps);
+  p.split_tokens = (int)(steps * kMlaStepKeys);
+  for (int s = 0; s < num_seqs; ++s) {
+    const int n = (kv_lens[s] + p.split_tokens - 1) / p.split_tokens;
+    p.max_splits = n > p.max_splits ? n : p.max_splits;
+  }
+  const size_t slots = (size_t)num_seqs * heads * p.max_splits;
+  p.o_bytes = align_up(slots * kMlaLatent * sizeof(float), 256);
+  p.bytes = p.o_bytes + slots * 2 * sizeof(float);
+  return p;
+}
+
+ca_status check_mla(const int32_t* kv_lens, int num_seqs, int heads, int max_blocks, int format) {
+  if (format != CA_MLA_BF16 && format != CA_MLA_FP8) return fail(CA_EINVAL, "unknown MLA cache format %d", format);
+  if (num_seqs < 0 || num_seqs > 65535) return fail(CA_EINVAL, "num_seqs must be in [0, 65535]");
+  if (heads <= 0 || heads % 16 || heads > 1024)
+    return fail(CA_EUNSUPPORTED, "heads must be a positive multiple of 16 up to 1024, got %d", heads);
+  if (num_seqs > 0 && !kv_lens) return fail(CA_EINVAL, "kv_lens_host is required");
+  for (int s = 0; s < num_seqs; ++s) {
+    if (kv_lens[s] < 1) return fail(CA_EINVAL, "sequence %d: kv_len %d < 1", s, kv_lens[s]);
+    if ((int64_t)kv_lens[s] > (int64_t)max_blocks * kBlock)
+      return fail(CA_ERANGE, "sequence %d: kv_len %d exceeds %d blocks", s, kv_lens[s], max_blocks);
+  }
+  return CA_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 void ca_prefill_opts_init(ca_prefill_opts* o) {
@@ -404,6 +448,75 @@ ca_status chunkattn_kv_append(const void* k_new, const void* v_new, int64_t star
   hipError_t e = launch_kv_append((DType)dtype, head_dim, head_dim_v, k_new, v_new, start_pos, n_tokens, kv_heads,
                                   block_table, num_blocks, k_pool, v_pool, (hipStream_t)stream);
   return hip_status(e, "kv_append launch");
+}
+
+size_t chunkattn_mla_block_bytes(int32_t format) {
+  return format == CA_MLA_BF16 ? (size_t)kMlaBf16Block : (format == CA_MLA_FP8 ? (size_t)kMlaFp8Block : 0);
+}
+
+size_t chunkattn_mla_decode_workspace_size(const int32_t* kv_lens_host, int32_t num_seqs, int32_t heads,
+                                           int32_t format) {
+  if (check_mla(kv_lens_host, num_seqs, heads, 1 << 24, format) != CA_OK || num_seqs == 0) return 0;
+  return plan_mla(kv_lens_host, num_seqs, heads, format == CA_MLA_FP8).bytes;
+}
+
+ca_status chunkattn_mla_kv_append(const void* latent, const void* rope, int64_t start_pos, int64_t n_tokens,
+                                  int32_t format, const int32_t* block_table, int32_t block_table_len,
+                                  int32_t num_blocks, void* pool, void* stream) {
+  if (format != CA_MLA_BF16 && format != CA_MLA_FP8) return fail(CA_EINVAL, "unknown MLA cache format %d", format);
+  if (start_pos < 0 || n_tokens < 0) return fail(CA_EINVAL, "start_pos and n_tokens must be >= 0");
+  if (n_tokens == 0) return ok();
+  if (!latent || !rope || !block_table || !pool) return fail(CA_EINVAL, "null pointer argument");
+  if (!aligned(latent, 16) || !aligned(rope, 16) || !aligned(pool, 16) || !aligned(block_table, 4))
+    return fail(CA_EINVAL, "misaligned pointer argument");
+  if (num_blocks <= 0) return fail(CA_EINVAL, "num_blocks must be > 0");
+  if (start_pos + n_tokens > (int64_t)block_table_len * kBlock)
+    return fail(CA_ERANGE, "block table covers %lld tokens, need %lld", (long long)block_table_len * kBlock,
+                (long long)(start_pos + n_tokens));
+  MlaAppendArgs a;
+  a.latent = (const uint16_t*)latent;
+  a.rope = (const uint16_t*)rope;
+  a.block_table = block_table;
+  a.pool = (unsigned char*)pool;
+  a.start_pos = start_pos;
+  a.n_tokens = n_tokens;
+  a.num_blocks = num_blocks;
+  return hip_status(launch_mla_append(format == CA_MLA_FP8, a, (hipStream_t)stream), "MLA append launch");
+}
+
+ca_status chunk_mla_decode(const void* q, const void* pool, int32_t format, const int32_t* block_tables,
+                           int32_t max_blocks, int32_t num_blocks, const int32_t* kv_lens_dev,
+                           const int32_t* kv_lens_host, int32_t num_seqs, int32_t heads, float scale, void* out,
+                           float* lse_out, void* workspace, size_t workspace_bytes, void* stream) {
+  if (max_blocks <= 0 || num_blocks <= 0) return fail(CA_EINVAL, "max_blocks and num_blocks must be > 0");
+  if (ca_status st = check_mla(kv_lens_host, num_seqs, heads, max_blocks, format)) return st;
+  if (!(scale > 0.f) || !std::isfinite(scale)) return fail(CA_EINVAL, "scale must be finite and > 0");
+  if (num_seqs == 0) return ok();
+  if (!q || !pool || !block_tables || !kv_lens_dev || !out) return fail(CA_EINVAL, "null pointer argument");
+  if (!aligned(q, 16) || !aligned(pool, 16) || !aligned(out, 16) || !aligned(block_tables, 4) ||
+      !aligned(kv_lens_dev, 4) || (lse_out && !aligned(lse_out, 4)))
+    return fail(CA_EINVAL, "misaligned pointer argument");
+  const MlaPlan p = plan_mla(kv_lens_host, num_seqs, heads, format == CA_MLA_FP8);
+  if (!workspace || workspace_bytes < p.bytes)
+    return fail(CA_EWORKSPACE, "workspace of %zu bytes needed, %zu given", p.bytes, workspace_bytes);
+  if (!aligned(workspace, 256)) return fail(CA_EINVAL, "workspace must be 256-byte aligned");
+  MlaArgs a;
+  a.q = (const uint16_t*)q;
+  a.pool = (const unsigned char*)pool;
+  a.block_tables = block_tables;
+  a.kv_lens = kv_lens_dev;
+  a.ws_o = (float*)workspace;
+  a.ws_ml = (float*)((char*)workspace + p.o_bytes);
+  a.out = (uint16_t*)out;
+  a.lse = lse_out;
+  a.num_seqs = num_seqs;
+  a.max_blocks = max_blocks;
+  a.num_blocks = num_blocks;
+  a.heads = heads;
+  a.max_splits = p.max_splits;
+  a.split_tokens = p.split_tokens;
+  a.scale_log2 = scale * kLog2e;
+  return hip_status(launch_mla_decode(format == CA_MLA_FP8, a, (hipStream_t)stream), "MLA decode launch");
 }
 
 }  // extern "C"

@@ -85,6 +85,39 @@ hipError_t launch_decode(int D, int DV, const DecodeArgs& a, int max_splits, hip
 hipError_t launch_decode_merge(int DV, const DecodeArgs& a, hipStream_t stream);
 bool decode_supported(int D, int DV);
 
+// MLA latent (absorbed) decode over a paged latent cache (one record of 512
+// latent + 64 rotary values per token, shared by every query head).
+constexpr int kMlaLatent = 512, kMlaRope = 64, kMlaRecord = 576, kMlaStepKeys = 32;
+// Block bytes (64 tokens): bf16 [72 runs][64][16 B]; fp8 codes [32 runs][64][16 B] +
+// scales [64][4 fp32] + rotary [8 runs][64][16 B].
+constexpr int64_t kMlaBf16Block = 72 * 64 * 16;
+constexpr int64_t kMlaFp8Block = 32 * 64 * 16 + 64 * 16 + 8 * 64 * 16;
+
+struct MlaArgs {
+  const uint16_t* q;             // [num_seqs, heads, 576] bf16
+  const unsigned char* pool;     // [num_blocks][block bytes]
+  const int32_t* block_tables;   // [num_seqs, max_blocks]
+  const int32_t* kv_lens;        // [num_seqs]
+  float* ws_o;                   // [num_seqs * heads * max_splits][512] unnormalised partials
+  float* ws_ml;                  // [...][2]: max (log2 units) and sum
+  uint16_t* out;                 // [num_seqs, heads, 512] bf16
+  float* lse;                    // [heads, num_seqs] or null
+  int32_t num_seqs, max_blocks, num_blocks, heads, max_splits, split_tokens;
+  float scale_log2;
+};
+
+struct MlaAppendArgs {
+  const uint16_t* latent;        // [n_tokens, 512] bf16
+  const uint16_t* rope;          // [n_tokens, 64] bf16
+  const int32_t* block_table;
+  unsigned char* pool;
+  int64_t start_pos, n_tokens;
+  int32_t num_blocks;
+};
+
+hipError_t launch_mla_decode(bool fp8, const MlaArgs& a, hipStream_t stream);
+hipError_t launch_mla_append(bool fp8, const MlaAppendArgs& a, hipStream_t stream);
+
 hipError_t launch_kv_append(DType dt, int D, int DV, const void* k_new, const void* v_new,
                             int64_t start_pos, int64_t n_tokens, int kv_heads,
                             const int32_t* block_table, int num_blocks, void* k_pool, void* v_pool,

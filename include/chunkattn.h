@@ -279,6 +279,62 @@ double chunkattn_alp_predict(const ca_alp_state* state, const double* x);
  * The state belongs to the caller; calls on one state must not overlap. */
 ca_status chunkattn_alp_update(ca_alp_state* state, const double* x, double measured, double* prior_error);
 
+/*
+ * MLA latent (absorbed) attention over a paged latent cache.
+ * "02 · 并行策略与 PP 切分 — GLM5.3 CyberSec W4A16" deployment notes §1, §4: an
+ * MLA layer caches one latent record per token shared by every query head,
+ * 1152 B in bf16 or 656 B in the fp8 latent format (the VPP review's models,
+ * DeepSeek-V3.1 and GLM-5.x, use MLA, §6.1).  A record is 512 latent + 64
+ * rotary values.  Cache blocks hold 64 tokens, one shared head:
+ *   CA_MLA_BF16: [72 runs][64 tokens][8 bf16]                      73728 B per block
+ *   CA_MLA_FP8 : [32 runs][64 tokens][16 e4m3] latent codes,
+ *                [64 tokens][4 fp32] scales (one per 128 latent values),
+ *                [8 runs][64 tokens][8 bf16] rotary                41984 B per block (= 64 x 656)
+ * Run r holds values 8r..8r+7 (bf16) or 16r..16r+15 (codes) of every token.
+ * fp8 codes are OCP e4m3 (bias 7, largest normal 448): a group's scale is
+ * amax / 448 in fp32 (1 for an all-zero group) and a value's code is its fp32
+ * quotient by the scale clamped to +-448, rounded to the nearest code.
+ */
+typedef enum { CA_MLA_BF16 = 0, CA_MLA_FP8 = 1 } ca_mla_format;
+
+/* Bytes of one 64-token cache block of the format (0 for an unknown format). */
+size_t chunkattn_mla_block_bytes(int32_t format);
+
+/*
+ * chunkattn_mla_kv_append — write n_tokens records of one sequence at
+ * logical positions [start_pos, start_pos + n_tokens) of its block table.
+ *   latent [n_tokens, 512] bf16, rope [n_tokens, 64] bf16 (device, 16-byte aligned).
+ *   block_table [block_table_len] device int32; pool [num_blocks * block bytes] device.
+ * bf16 copies bits; fp8 quantises each 128-value latent group.  Block ids are
+ * clamped to [0, num_blocks).  CA_OK, CA_EINVAL, CA_ERANGE or CA_EHIP.
+ */
+ca_status chunkattn_mla_kv_append(const void* latent, const void* rope, int64_t start_pos, int64_t n_tokens,
+                                  int32_t format, const int32_t* block_table, int32_t block_table_len,
+                                  int32_t num_blocks, void* pool, void* stream);
+
+/* Workspace bytes chunk_mla_decode needs for these context lengths (host array); 0 for invalid arguments. */
+size_t chunkattn_mla_decode_workspace_size(const int32_t* kv_lens_host, int32_t num_seqs, int32_t heads,
+                                           int32_t format);
+
+/*
+ * chunk_mla_decode — one decode token per sequence attends to its whole
+ * latent cache (the query sits at position kv_len - 1, VPP review §2.1: decode
+ * reads the entire cache).
+ *   q    [num_seqs, heads, 576] bf16: per head, the latent-space projection of
+ *        the no-rope query (512) then its rotary part (64).
+ *   out  [num_seqs, heads, 512] bf16: the attention output in latent space.
+ *   lse_out optional [heads, num_seqs] fp32, natural log of the softmax denominator.
+ *   block_tables [num_seqs, max_blocks_per_seq] device; kv_lens on device and host (>= 1).
+ *   heads: a positive multiple of 16 (one wave serves 16 heads).
+ *   workspace: >= chunkattn_mla_decode_workspace_size bytes, 256-byte aligned (split partials).
+ * Keys past kv_len never reach an output.  CA_OK, CA_EINVAL, CA_EUNSUPPORTED,
+ * CA_ERANGE, CA_EWORKSPACE or CA_EHIP; validation precedes any HIP call.
+ */
+ca_status chunk_mla_decode(const void* q, const void* pool, int32_t format, const int32_t* block_tables,
+                           int32_t max_blocks_per_seq, int32_t num_blocks, const int32_t* kv_lens_dev,
+                           const int32_t* kv_lens_host, int32_t num_seqs, int32_t heads, float scale, void* out,
+                           float* lse_out, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* chunkattn_last_error(void);
 

@@ -10,8 +10,9 @@ Eq. (1) (scaled dot-product attention), the causal rule stated beside it in
 earlier chunk plus itself).  The arithmetic lives in ``attn_oracle.c`` (plain
 C, IEEE fp64, two passes); this module only marshals numpy arrays.
 
-Inputs are numpy arrays of float32, or uint16 holding bfloat16 bit patterns
-(widened exactly to fp64 inside the C code).  Layouts are logical:
+Inputs are numpy arrays of float32, float64 (used for values that fp32 cannot
+hold exactly, such as dequantized fp8), or uint16 holding bfloat16 bit
+patterns (widened exactly to fp64 inside the C code).  Layouts are logical:
 ``q [chunk_len, Hq, d]``, ``k [kv_len, Hkv, d]``, ``v [kv_len, Hkv, dv]``.
 
 Every function here is pinned by the CPU tests (closed forms, invariants,
@@ -31,7 +32,7 @@ _SRC = os.path.join(_HERE, "attn_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
-F32, BF16 = 0, 1
+F32, BF16, F64 = 0, 1, 2
 
 
 def build() -> str:
@@ -74,7 +75,9 @@ def _dtype_code(*arrays) -> int:
         return F32
     if kinds == {np.dtype(np.uint16)}:
         return BF16
-    raise TypeError(f"oracle inputs must all be float32 or all uint16 (bf16 bits), got {kinds}")
+    if kinds == {np.dtype(np.float64)}:
+        return F64
+    raise TypeError(f"oracle inputs must all be float32, all float64 or all uint16 (bf16 bits), got {kinds}")
 
 
 def attend_rows(q, k, v, past_len: int, scale: float, tok, head,

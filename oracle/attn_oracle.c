@@ -41,10 +41,11 @@
 #include <string.h>
 #include <omp.h>
 
-enum { ORC_F32 = 0, ORC_BF16 = 1 };
+enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_F64 = 2 };
 
 static double orc_load(const void* base, int dtype, int64_t idx) {
   if (dtype == ORC_F32) return (double)((const float*)base)[idx];
+  if (dtype == ORC_F64) return ((const double*)base)[idx];
   uint32_t bits = ((uint32_t)((const uint16_t*)base)[idx]) << 16;
   float f;
   memcpy(&f, &bits, sizeof f);

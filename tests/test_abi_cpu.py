@@ -148,3 +148,61 @@ def test_kv_append_rejections():
     assert f(dt=5) == L.CA_EINVAL
     assert f(start=60, n=10) == L.CA_ERANGE
     assert f(n=0) == L.CA_OK
+
+
+def test_mla_block_bytes_follow_the_per_token_record():
+    # 64 tokens per block of 1152 B (bf16) and 656 B (fp8 latent) records
+    assert L.chunkattn_mla_block_bytes(L.CA_MLA_BF16) == 64 * 1152
+    assert L.chunkattn_mla_block_bytes(L.CA_MLA_FP8) == 64 * 656
+    assert L.chunkattn_mla_block_bytes(2) == 0
+    assert L.chunkattn_mla_decode_workspace_size([100, 5000], 16, L.CA_MLA_FP8) > 2 * 16 * 512 * 4
+    assert L.chunkattn_mla_decode_workspace_size([100], 15, L.CA_MLA_BF16) == 0
+    assert L.chunkattn_mla_decode_workspace_size([0], 16, L.CA_MLA_BF16) == 0
+    assert L.chunkattn_mla_decode_workspace_size([10], 16, 4) == 0
+
+
+def mla_decode(q=FAKE, fmt=L.CA_MLA_BF16, kv=(10, 300), heads=16, max_blocks=8, num_blocks=8, scale=0.1,
+               out=FAKE, ws=FAKE, ws_bytes=1 << 30, lse=None):
+    kv_a = (ctypes.c_int32 * len(kv))(*kv)
+    return L.lib().chunk_mla_decode(q, FAKE, fmt, FAKE, max_blocks, num_blocks, FAKE, ctypes.addressof(kv_a),
+                                    len(kv), heads, scale, out, lse, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(fmt=2), L.CA_EINVAL),
+    (dict(heads=8), L.CA_EUNSUPPORTED),
+    (dict(heads=2048), L.CA_EUNSUPPORTED),
+    (dict(kv=(0, 5)), L.CA_EINVAL),
+    (dict(kv=(10, 600)), L.CA_ERANGE),                   # 600 tokens > 8 blocks of 64
+    (dict(scale=0.0), L.CA_EINVAL),
+    (dict(scale=float("nan")), L.CA_EINVAL),
+    (dict(q=None), L.CA_EINVAL),
+    (dict(q=MISALIGNED), L.CA_EINVAL),
+    (dict(lse=FAKE + 2), L.CA_EINVAL),
+    (dict(ws=None), L.CA_EWORKSPACE),
+    (dict(ws_bytes=1024), L.CA_EWORKSPACE),
+    (dict(ws=FAKE + 16), L.CA_EINVAL),
+    (dict(max_blocks=0), L.CA_EINVAL),
+    (dict(num_blocks=0), L.CA_EINVAL),
+])
+def test_mla_decode_rejections(kwargs, status):
+    assert mla_decode(**kwargs) == status
+    assert L.lib().chunkattn_last_error().decode()
+
+
+def test_mla_decode_empty_batch_succeeds():
+    assert mla_decode(q=None, out=None, kv=(), ws=None) == L.CA_OK
+
+
+def test_mla_append_rejections():
+    lib = L.lib()
+    f = lambda **kw: lib.chunkattn_mla_kv_append(kw.get("lat", FAKE), FAKE, kw.get("start", 0), kw.get("n", 10),
+                                                 kw.get("fmt", L.CA_MLA_FP8), FAKE, kw.get("tl", 1),
+                                                 kw.get("nb", 4), FAKE, None)
+    assert f(fmt=3) == L.CA_EINVAL
+    assert f(start=-1) == L.CA_EINVAL
+    assert f(lat=None) == L.CA_EINVAL
+    assert f(lat=MISALIGNED) == L.CA_EINVAL
+    assert f(nb=0) == L.CA_EINVAL
+    assert f(start=60, n=10) == L.CA_ERANGE
+    assert f(n=0, lat=None) == L.CA_OK

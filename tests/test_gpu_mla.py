@@ -1,0 +1,268 @@
+"""GPU parity of MLA latent (absorbed) decode and of the latent cache write,
+against the fp64 oracle (oracle/mla.py).
+
+"02 · 并行策略与 PP 切分 — GLM5.3 CyberSec W4A16" deployment notes §1, §4:
+one latent record per token shared by every query head, 1152 B in bf16 or
+656 B in the fp8 latent format.
+
+* The cache write is compared byte for byte with the layout the header states,
+  packed here on the host; fp8 codes and scales must equal the oracle's
+  quantisation exactly, and bytes the write does not own must be untouched.
+* Decode runs on pools packed on the host (so it does not lean on the write
+  kernel), poisoned with 0xFF (NaN in bf16, in e4m3 and in the fp32 scales)
+  outside the records that exist: no output may see them.  Every output value
+  and LSE is compared with the oracle.
+* The decode-batch workload (256 requests, contexts uniform in [1024, 32768],
+  16 query heads) is filled by the write kernel and checked on sampled
+  sequences, in the launch configuration the benchmark times.
+Softmax scale 1/sqrt(192), the expanded head's 128 no-rope + 64 rope values.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from chunked_prefill_causal_amd import _lib as L
+from chunked_prefill_causal_amd import inputs
+from oracle import mla
+
+from gpu_common import BF16_TOL, LSE_TOL, log, max_err, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+FMTS = {"bf16": L.CA_MLA_BF16, "fp8": L.CA_MLA_FP8}
+SCALE = 1.0 / math.sqrt(192)
+POISON = 0xFF
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _gpu():
+    require_gpu()
+
+
+def bits(t: torch.Tensor) -> np.ndarray:
+    return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def byte_offsets(fmt: str, table: np.ndarray, positions: np.ndarray):
+    """Flat pool byte offsets of each position's (latent or codes, scales, rotary) bytes."""
+    bb = L.chunkattn_mla_block_bytes(FMTS[fmt])
+    base = table[positions // 64].astype(np.int64) * bb + (positions % 64) * 16
+    if fmt == "bf16":                      # [72 runs][64 tokens][16 B]: record byte j in run j // 16
+        j = np.arange(1152)
+        rec = base[:, None] + (j // 16) * 1024 + j % 16
+        return rec[:, :1024], None, rec[:, 1024:]
+    j = np.arange(512)                     # codes [32 runs][64][16 B], scales [64][16 B], rotary [8][64][16 B]
+    codes = base[:, None] + (j // 16) * 1024 + j % 16
+    scales = base[:, None] + 32768 + np.arange(16)
+    j = np.arange(128)
+    rope = base[:, None] + 33792 + (j // 16) * 1024 + j % 16
+    return codes, scales, rope
+
+
+def pack(pool: np.ndarray, fmt: str, table: np.ndarray, lat_bits, rope_bits, start: int = 0) -> None:
+    """Write records of positions start.. into a flat host pool, as the header lays them out."""
+    n = lat_bits.shape[0]
+    lat_off, sc_off, rope_off = byte_offsets(fmt, table, np.arange(start, start + n))
+    pool[rope_off] = rope_bits.view(np.uint8).reshape(n, 128)
+    if fmt == "bf16":
+        pool[lat_off] = lat_bits.view(np.uint8).reshape(n, 1024)
+    else:
+        codes, scales = mla.quantize_latent(inputs_f32(lat_bits))
+        pool[lat_off] = codes
+        pool[sc_off] = scales.view(np.uint8).reshape(n, 16)
+
+
+def inputs_f32(b: np.ndarray) -> np.ndarray:
+    return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+def new_pool(fmt, num_blocks, fill):
+    return torch.full((num_blocks, L.chunkattn_mla_block_bytes(FMTS[fmt])), fill, dtype=torch.uint8, device="cuda")
+
+
+# ------------------------------------------------------------- cache write
+def special_latents(n, seed):
+    """Seeded latents with the quantiser's corner cases in the first rows."""
+    lat = inputs.normal((n, 512), seed, "f32").numpy() * np.float32(2.0)
+    lat[0, 128:256] = 0.0                                   # all-zero group: scale 1
+    lat[1, 256:384] = -0.0                                  # all negative zero: codes 0x80
+    lat[2, 0:128] *= np.float32(1e-30)                      # tiny group
+    lat[2, 5] = np.float32(3e-28)
+    lat[3, :] *= np.float32(1e30)                           # huge values
+    lat[4, 0:128] = 1.0                                     # amax 448 -> scale 1; exact midpoints
+    lat[4, 0] = 448.0
+    lat[4, 1:8] = [1.0625, 1.1875, 432.0, 3 * 2.0 ** -10, 2.0 ** -10, -1.0625, -432.0]
+    lat[5, 384:512] = np.linspace(-7, 7, 128, dtype=np.float32)
+    lat[6, 0:128] = 0.0                                     # scale 1; subnormal codes and their midpoints
+    lat[6, 0] = 448.0
+    lat[6, 1:12] = np.array([1, 1.5, 2, 2.5, 3, 5, 6.5, 7, 7.5, -1.5, -0.5], dtype=np.float32) * 2.0 ** -9
+    t = torch.from_numpy(lat).to(torch.bfloat16)
+    return t
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_append_layout_bitexact(fmt):
+    start, n, cap = 37, 230, 300
+    needed = math.ceil(cap / 64)
+    nb = inputs.pool_size(needed)
+    table = inputs.block_table(needed, 31, nb)
+    lat = special_latents(n, 40)
+    rope = inputs.normal((n, 64), 41, "bf16")
+    log(f"mla append fmt={fmt} start={start} n={n} blocks={nb}")
+    pool = new_pool(fmt, nb, 0xAB)
+    L.chunkattn_mla_kv_append(lat.cuda(), rope.cuda(), start, torch.from_numpy(table).cuda(), pool, FMTS[fmt])
+    got = pool.cpu().numpy().reshape(-1)
+    want = np.full(got.shape, 0xAB, dtype=np.uint8)
+    pack(want, fmt, table, bits(lat), bits(rope), start)
+    bad = np.flatnonzero(got != want)
+    assert bad.size == 0, f"{bad.size} bytes differ, first at {bad[:8]}: got {got[bad[:8]]} want {want[bad[:8]]}"
+
+
+def test_append_two_calls_fill_one_sequence():
+    """A prefill chunk then one decode token: the second call lands after the first."""
+    table = inputs.block_table(3, 32, 5)
+    t_d = torch.from_numpy(table).cuda()
+    lat = inputs.normal((129, 512), 42, "bf16")
+    rope = inputs.normal((129, 64), 43, "bf16")
+    for fmt in ("bf16", "fp8"):
+        log(f"mla append two calls fmt={fmt}")
+        pool = new_pool(fmt, 5, 0)
+        L.chunkattn_mla_kv_append(lat[:128].cuda(), rope[:128].cuda(), 0, t_d, pool, FMTS[fmt])
+        L.chunkattn_mla_kv_append(lat[128:].cuda(), rope[128:].cuda(), 128, t_d, pool, FMTS[fmt])
+        want = np.zeros(pool.numel(), dtype=np.uint8)
+        pack(want, fmt, table, bits(lat), bits(rope))
+        assert np.array_equal(pool.cpu().numpy().reshape(-1), want)
+
+
+# ------------------------------------------------------------------ decode
+def build_batch(fmt, kv_lens, heads, seed):
+    n = len(kv_lens)
+    needed = [math.ceil(k / 64) for k in kv_lens]
+    nb = inputs.pool_size(sum(needed))
+    perm = inputs.block_table(sum(needed), seed, nb)
+    tables = np.zeros((n, max(needed)), dtype=np.int32)
+    host = np.full(nb * L.chunkattn_mla_block_bytes(FMTS[fmt]), POISON, dtype=np.uint8)
+    seqs, off = [], 0
+    for s, kv in enumerate(kv_lens):
+        tables[s, : needed[s]] = perm[off: off + needed[s]]
+        off += needed[s]
+        lat = bits(inputs.normal((kv, 512), seed + 7 * s + 1, "bf16"))
+        rope = bits(inputs.normal((kv, 64), seed + 7 * s + 2, "bf16"))
+        pack(host, fmt, tables[s], lat, rope)
+        seqs.append((lat, rope))
+    q = inputs.normal((n, heads, 576), seed + 5, "bf16")
+    pool = torch.from_numpy(host.reshape(nb, -1)).cuda()
+    return pool, torch.from_numpy(tables).cuda(), q, seqs
+
+
+def check_decode(fmt, kv_lens, heads, seed, sample=None):
+    pool, tables, q, seqs = build_batch(fmt, kv_lens, heads, seed)
+    log(f"mla decode fmt={fmt} heads={heads} kv={list(kv_lens)[:12]} seed={seed}")
+    out, lse = L.chunk_mla_decode(q.cuda(), pool, FMTS[fmt], tables, kv_lens, SCALE, return_lse=True)
+    torch.cuda.synchronize()
+    out, lse = out.cpu(), lse.cpu()
+    qb = bits(q)
+    worst = worst_lse = 0.0
+    for s in (range(len(kv_lens)) if sample is None else sample):
+        ref, ref_lse = mla.decode(qb[s], mla.records(*seqs[s], fmt), SCALE)
+        worst = max(worst, max_err(out[s], ref))
+        worst_lse = max(worst_lse, max_err(lse[:, s], ref_lse))
+    log(f"  max abs err {worst:.3e}  lse {worst_lse:.3e}")
+    assert worst <= BF16_TOL and worst_lse <= LSE_TOL
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_decode_ragged_contexts(fmt):
+    # every step-tail length class: 1 key, one short of / exactly / one past 32 and 64, long
+    check_decode(fmt, [1, 31, 32, 33, 63, 64, 65, 100, 1000, 4097], 16, 100)
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+@pytest.mark.parametrize("heads", [32, 128])
+def test_decode_more_heads(fmt, heads):
+    check_decode(fmt, [7, 129, 2000, 3333], heads, 200 + heads)
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_decode_many_splits(fmt):
+    # one long context among short ones: the plan gives it many splits
+    check_decode(fmt, [40000, 5, 70, 300], 16, 300)
+
+
+def test_decode_rejects_unsupported_heads_on_device():
+    q = torch.zeros((1, 8, 576), dtype=torch.bfloat16, device="cuda")
+    pool = new_pool("bf16", 1, 0)
+    with pytest.raises(L.ChunkAttnError):
+        L.chunk_mla_decode(q, pool, L.CA_MLA_BF16, torch.zeros((1, 1), dtype=torch.int32, device="cuda"), [10], SCALE)
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_decode_after_append_end_to_end(fmt):
+    """Records written by the cache-write kernel (prefix, then one decode token) and read by decode."""
+    kv = [700, 65, 1]
+    needed = [math.ceil(k / 64) for k in kv]
+    nb = inputs.pool_size(sum(needed))
+    perm = inputs.block_table(sum(needed), 400, nb)
+    tables = np.zeros((3, max(needed)), dtype=np.int32)
+    pool = new_pool(fmt, nb, POISON)
+    recs, off = [], 0
+    for s, n in enumerate(kv):
+        tables[s, : needed[s]] = perm[off: off + needed[s]]
+        off += needed[s]
+        lat = inputs.normal((n, 512), 410 + s, "bf16")
+        rope = inputs.normal((n, 64), 420 + s, "bf16")
+        t_d = torch.from_numpy(tables[s]).cuda()
+        log(f"mla append+decode fmt={fmt} seq={s} n={n}")
+        if n > 1:
+            L.chunkattn_mla_kv_append(lat[:-1].cuda(), rope[:-1].cuda(), 0, t_d, pool, FMTS[fmt])
+        L.chunkattn_mla_kv_append(lat[-1:].cuda(), rope[-1:].cuda(), n - 1, t_d, pool, FMTS[fmt])
+        recs.append(mla.records(bits(lat), bits(rope), fmt))
+    q = inputs.normal((3, 16, 576), 430, "bf16")
+    out, lse = L.chunk_mla_decode(q.cuda(), pool, FMTS[fmt], torch.from_numpy(tables).cuda(), kv, SCALE,
+                                  return_lse=True)
+    out, lse = out.cpu(), lse.cpu()
+    for s in range(3):
+        ref, ref_lse = mla.decode(bits(q)[s], recs[s], SCALE)
+        assert max_err(out[s], ref) <= BF16_TOL
+        assert max_err(lse[:, s], ref_lse) <= LSE_TOL
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_decode_batch_workload_sampled(fmt):
+    """256 decode requests, contexts uniform in [1024, 32768], 16 heads: the benchmark's launch."""
+    kv = inputs.context_lengths(256, 1024, 32768, 77)
+    needed = [math.ceil(int(k) / 64) for k in kv]
+    nb = inputs.pool_size(sum(needed))
+    perm = inputs.block_table(sum(needed), 78, nb)
+    tables = np.zeros((256, max(needed)), dtype=np.int32)
+    off = 0
+    for s in range(256):
+        tables[s, : needed[s]] = perm[off: off + needed[s]]
+        off += needed[s]
+    tables_d = torch.from_numpy(tables).cuda()
+    pool = new_pool(fmt, nb, POISON)
+    log(f"mla workload fmt={fmt}: filling {int(kv.sum())} tokens")
+    gen = torch.Generator(device="cuda")
+    sample = sorted({0, 255, int(np.argmax(kv)), int(np.argmin(kv)), 17, 130})
+    kept = {}
+    for s in range(256):
+        gen.manual_seed(1000 + s)
+        lat = torch.randn((int(kv[s]), 512), generator=gen, device="cuda").to(torch.bfloat16)
+        rope = torch.randn((int(kv[s]), 64), generator=gen, device="cuda").to(torch.bfloat16)
+        L.chunkattn_mla_kv_append(lat, rope, 0, tables_d[s], pool, FMTS[fmt])
+        if s in sample:
+            kept[s] = (bits(lat.cpu()), bits(rope.cpu()))
+    q = inputs.normal((256, 16, 576), 79, "bf16")
+    log(f"mla workload fmt={fmt}: decode")
+    out, lse = L.chunk_mla_decode(q.cuda(), pool, FMTS[fmt], tables_d, kv, SCALE, return_lse=True)
+    out, lse = out.cpu(), lse.cpu()
+    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
+    worst = worst_lse = 0.0
+    for s in sample:
+        ref, ref_lse = mla.decode(bits(q)[s], mla.records(*kept[s], fmt), SCALE)
+        worst = max(worst, max_err(out[s], ref))
+        worst_lse = max(worst_lse, max_err(lse[:, s], ref_lse))
+    log(f"  sampled {sample}: max abs err {worst:.3e} lse {worst_lse:.3e}")
+    assert worst <= BF16_TOL and worst_lse <= LSE_TOL
