@@ -67,6 +67,8 @@ def parse():
     p.add_argument("--reps", type=int, default=10, help="repetitions for the decode-only / prefill-only timings")
     p.add_argument("--copy-calibration", action="store_true",
                    help="after the timed region, copy 1 GiB device to device (a known-size kernel for counter scaling)")
+    p.add_argument("--mla-only", action="store_true",
+                   help="time only the MLA latent decode batches (prints their JSON object)")
     p.add_argument("--summarize-profile", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
                    help="write the traffic summary from rocprofv3 output of this script (no GPU needed)")
     return p.parse_args()
@@ -240,6 +242,69 @@ class MixedBatch:
                                    kv_lens_dev=self.kv_dev)
 
 
+class MlaDecode:
+    """256 absorbed MLA decodes over a paged latent cache of one format (bf16 or fp8).
+
+    Records are written by the library's cache-write kernel (fp8: quantised
+    there); the pool is poisoned with 0xFF first.  ``bytes`` is what the
+    decode must move at least: every cached record once (1152 B bf16, 656 B
+    fp8 per token), the queries and outputs, and the block-table entries.
+    """
+
+    def __init__(self, L, inputs, torch, fmt):
+        w = inputs.WORKLOADS["mla_decode"]
+        self.w, self.fmt = w, fmt
+        kv = inputs.context_lengths(w.decode_requests, w.decode_ctx[0], w.decode_ctx[1], w.seed)
+        tables, pool_blocks = inputs.batch_block_tables(kv, w.seed + 1)
+        self.tables = torch.from_numpy(tables).cuda()
+        self.pool = L.mla_pool(pool_blocks, fmt)
+        self.pool.fill_(0xFF)
+        gen = torch.Generator(device="cuda")
+        for s, n in enumerate(kv.tolist()):
+            gen.manual_seed(inputs.mla_record_seed(w, s))
+            lat = torch.randn((n, L.MLA_LATENT), generator=gen, device="cuda").to(torch.bfloat16)
+            rope = torch.randn((n, L.MLA_ROPE), generator=gen, device="cuda").to(torch.bfloat16)
+            L.chunkattn_mla_kv_append(lat, rope, 0, self.tables[s], self.pool, fmt)
+        self.q = inputs.normal_device((w.decode_requests, w.heads, w.head_dim), w.seed + 2, "bf16")
+        self.kv_host = torch.from_numpy(kv)
+        self.kv_dev = self.kv_host.cuda()
+        self.out = torch.empty((w.decode_requests, w.heads, w.head_dim_v), dtype=torch.bfloat16, device="cuda")
+        need = L.chunkattn_mla_decode_workspace_size(kv, w.heads, fmt)
+        self.ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+        self.tokens = int(kv.sum())
+        self.bytes_per_token = L.chunkattn_mla_block_bytes(fmt) // 64
+        self.bytes = (self.tokens * self.bytes_per_token + (self.q.numel() + self.out.numel()) * 2
+                      + sum(math.ceil(int(k) / 64) for k in kv) * 4)
+
+    def run(self, L):
+        return L.chunk_mla_decode(self.q, self.pool, self.fmt, self.tables, self.kv_host, self.w.scale,
+                                  out=self.out, workspace=self.ws, kv_lens_dev=self.kv_dev)
+
+
+def mla_decode_summary(L, inputs, torch, timed, reps, warmup):
+    """Both latent formats of the MLA decode batch: op time, HBM fraction, requests/s."""
+    res = {}
+    for name, fmt in (("bf16", L.CA_MLA_BF16), ("fp8", L.CA_MLA_FP8)):
+        m = MlaDecode(L, inputs, torch, fmt)
+        for _ in range(max(1, warmup)):
+            m.run(L)
+        torch.cuda.synchronize()
+        ms = timed(lambda: m.run(L), reps)
+        gbps = m.bytes / (ms / 1e3) / 1e9
+        res[name] = {"ms": round(ms, 4), "requests_per_s": round(m.w.decode_requests / (ms / 1e3), 1),
+                     "cached_tokens": m.tokens, "bytes_per_token": m.bytes_per_token,
+                     "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS,
+                                  "unit": "GB/s", "frac": round(gbps / PEAK_HBM_GBPS, 4),
+                                  "algorithmic_bytes": m.bytes}}
+        log(f"MLA decode {name}: {ms:.3f} ms, {gbps:.0f} GB/s ({gbps / PEAK_HBM_GBPS:.1%} of HBM)")
+        del m
+        torch.cuda.empty_cache()
+    res["fp8_speedup"] = round(res["bf16"]["ms"] / res["fp8"]["ms"], 3)
+    res["workload"] = ("256 decodes, ctx U[1024,32768], 16 q heads over one shared 576-value latent record per "
+                       "token, paged KV (64); decode + split merge, inputs resident in HBM")
+    return res
+
+
 def median(xs):
     s = sorted(xs)
     return s[len(s) // 2] if len(s) % 2 else 0.5 * (s[len(s) // 2 - 1] + s[len(s) // 2])
@@ -402,6 +467,22 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     L.lib()
     torch.cuda.set_device(0)
+
+    def timed(fn, reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ts = []
+        for _ in range(reps):
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return median(ts)
+
+    if args.mla_only:
+        print(json.dumps({"mla_decode": mla_decode_summary(L, inputs, torch, timed, args.reps, args.warmup)}),
+              flush=True)
+        return
     log("generating inputs in HBM")
     loop = PrefillLoop(L, inputs, torch)
     mixed = MixedBatch(L, inputs, torch)
@@ -452,17 +533,6 @@ def main():
         f"({prefill_tflops:.1f} TFLOP/s); mixed {median(mixed_ms):.3f} ms")
 
     # the two halves of the mixed batch on their own (for the decode HBM roofline)
-    def timed(fn, reps):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        ts = []
-        for _ in range(reps):
-            e0.record()
-            fn()
-            e1.record()
-            torch.cuda.synchronize()
-            ts.append(e0.elapsed_time(e1))
-        return median(ts)
-
     dec_ms = timed(lambda: dec_only.run(L), args.reps)
     pre_ms = timed(lambda: pre_only.run(L), args.reps)
     dec_gbps = dec_only.decode_bytes / (dec_ms / 1e3) / 1e9
@@ -476,6 +546,10 @@ def main():
         torch.cuda.synchronize()
         del src, dst
         log("calibration copy of 1 GiB done")
+
+    log("timing the MLA latent decode batches")
+    del dec_only, pre_only
+    mla = mla_decode_summary(L, inputs, torch, timed, args.reps, args.warmup)
 
     log("timing the latency-predictor grid")
     alp = latency_predictor(L, loop, torch)
@@ -540,6 +614,7 @@ def main():
                                 "unit": "GB/s", "frac": round(dec_gbps / PEAK_HBM_GBPS, 4),
                                 "algorithmic_bytes": mixed.decode_bytes},
         },
+        "mla_decode": mla,
         "schedule_sim": sched,
         "latency_predictor": alp,
         "cpu_baseline": cpu,

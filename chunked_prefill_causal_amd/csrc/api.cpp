@@ -151,26 +151,31 @@ namespace {
 // MLA latent decode plan: keys per split (a multiple of the 32-key step) so
 // that about four rounds of waves fill the chip (2 bf16 / 3 fp8 waves per CU
 // fit their double-buffered LDS), and the largest split count of any sequence.
+// MLA decode plan.  The 32-key steps of all sequences, laid end to end, are
+// cut into `units` equal ranges: a multiple of the workgroups the chip holds at
+// once (2 per CU for bf16, 3 for fp8, shared by the head blocks), rounded to 8
+// so units spread evenly over the XCDs, with at most kMlaMaxUnitSteps steps
+// each.  Workspace: per-sequence step prefix sums, each unit's first sequence,
+// then per head and slot (num_seqs + units slots) the partial (m, l) and O.
 struct MlaPlan {
-  int split_tokens = 0, max_splits = 0;
-  size_t o_bytes = 0, bytes = 0;
+  int64_t steps = 0;
+  int64_t units = 0, slots = 0;
+  size_t unit_off = 0, ml_off = 0, o_off = 0, bytes = 0;
 };
 MlaPlan plan_mla(const int32_t* kv_lens, int num_seqs, int heads, bool fp8) {
   MlaPlan p;
-  int64_t units = 0;
-  for (int s = 0; s < num_seqs; ++s) units += (int64_t)(kv_lens[s] + kMlaStepKeys - 1) / kMlaStepKeys;
-  units *= heads / 16;
-  const int64_t target = (int64_t)kNumCUs * (fp8 ? 3 : 2) * 4;
-  int64_t steps = (units + target - 1) / target;
-  steps = steps < 4 ? 4 : (steps > 4096 ? 4096 : steps);
-  p.split_tokens = (int)(steps * kMlaStepKeys);
-  for (int s = 0; s < num_seqs; ++s) {
-    const int n = (kv_lens[s] + p.split_tokens - 1) / p.split_tokens;
-    p.max_splits = n > p.max_splits ? n : p.max_splits;
-  }
-  const size_t slots = (size_t)num_seqs * heads * p.max_splits;
-  p.o_bytes = align_up(slots * kMlaLatent * sizeof(float), 256);
-  p.bytes = p.o_bytes + slots * 2 * sizeof(float);
+  for (int s = 0; s < num_seqs; ++s) p.steps += (kv_lens[s] + kMlaStepKeys - 1) / kMlaStepKeys;
+  const int nhb = heads / 16;
+  int per_hb = kNumCUs * (fp8 ? 3 : 2) / nhb;
+  per_hb = per_hb >= 8 ? per_hb / 8 * 8 : 8;
+  const int64_t cap = (int64_t)per_hb * kMlaMaxUnitSteps;
+  p.units = (p.steps + cap - 1) / cap * per_hb;
+  if (p.units > p.steps) p.units = p.steps;
+  p.slots = num_seqs + p.units;
+  p.unit_off = align_up((size_t)(num_seqs + 1) * sizeof(int64_t), 256);
+  p.ml_off = p.unit_off + align_up((size_t)p.units * sizeof(int32_t), 256);
+  p.o_off = p.ml_off + align_up((size_t)heads * p.slots * 2 * sizeof(float), 256);
+  p.bytes = p.o_off + (size_t)heads * p.slots * kMlaLatent * sizeof(float);
   return p;
 }
 
@@ -497,6 +502,9 @@ ca_status chunk_mla_decode(const void* q, const void* pool, int32_t format, cons
       !aligned(kv_lens_dev, 4) || (lse_out && !aligned(lse_out, 4)))
     return fail(CA_EINVAL, "misaligned pointer argument");
   const MlaPlan p = plan_mla(kv_lens_host, num_seqs, heads, format == CA_MLA_FP8);
+  // keeps unit * steps products in int64 and the launch grid in int32
+  if (p.steps > (int64_t)1 << 31 || p.units * (heads / 16) > 0x7fffffffLL)
+    return fail(CA_ERANGE, "the batch holds %lld key steps, too many for one call", (long long)p.steps);
   if (!workspace || workspace_bytes < p.bytes)
     return fail(CA_EWORKSPACE, "workspace of %zu bytes needed, %zu given", p.bytes, workspace_bytes);
   if (!aligned(workspace, 256)) return fail(CA_EINVAL, "workspace must be 256-byte aligned");
@@ -505,16 +513,18 @@ ca_status chunk_mla_decode(const void* q, const void* pool, int32_t format, cons
   a.pool = (const unsigned char*)pool;
   a.block_tables = block_tables;
   a.kv_lens = kv_lens_dev;
-  a.ws_o = (float*)workspace;
-  a.ws_ml = (float*)((char*)workspace + p.o_bytes);
+  a.seq_steps = (int64_t*)workspace;
+  a.unit_seq = (int32_t*)((char*)workspace + p.unit_off);
+  a.ws_ml = (float*)((char*)workspace + p.ml_off);
+  a.ws_o = (float*)((char*)workspace + p.o_off);
   a.out = (uint16_t*)out;
   a.lse = lse_out;
   a.num_seqs = num_seqs;
   a.max_blocks = max_blocks;
   a.num_blocks = num_blocks;
   a.heads = heads;
-  a.max_splits = p.max_splits;
-  a.split_tokens = p.split_tokens;
+  a.units = (int32_t)p.units;
+  a.slots = (int32_t)p.slots;
   a.scale_log2 = scale * kLog2e;
   return hip_status(launch_mla_decode(format == CA_MLA_FP8, a, (hipStream_t)stream), "MLA decode launch");
 }

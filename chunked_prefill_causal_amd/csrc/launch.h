@@ -88,21 +88,29 @@ bool decode_supported(int D, int DV);
 // MLA latent (absorbed) decode over a paged latent cache (one record of 512
 // latent + 64 rotary values per token, shared by every query head).
 constexpr int kMlaLatent = 512, kMlaRope = 64, kMlaRecord = 576, kMlaStepKeys = 32;
+// A decode work unit holds at most this many steps, so a segment spans at most
+// 64 cache blocks (the kernel keeps their ids one per lane).
+constexpr int kMlaMaxUnitSteps = 127;
 // Block bytes (64 tokens): bf16 [72 runs][64][16 B]; fp8 codes [32 runs][64][16 B] +
 // scales [64][4 fp32] + rotary [8 runs][64][16 B].
 constexpr int64_t kMlaBf16Block = 72 * 64 * 16;
 constexpr int64_t kMlaFp8Block = 32 * 64 * 16 + 64 * 16 + 8 * 64 * 16;
 
+// MLA decode work plan: the 32-key steps of all sequences, laid end to end,
+// are cut into `units` equal ranges; a unit's piece of one sequence (a
+// segment) writes one partial, into slot s + unit of each head.
 struct MlaArgs {
   const uint16_t* q;             // [num_seqs, heads, 576] bf16
   const unsigned char* pool;     // [num_blocks][block bytes]
   const int32_t* block_tables;   // [num_seqs, max_blocks]
   const int32_t* kv_lens;        // [num_seqs]
-  float* ws_o;                   // [num_seqs * heads * max_splits][512] unnormalised partials
-  float* ws_ml;                  // [...][2]: max (log2 units) and sum
+  int64_t* seq_steps;            // [num_seqs + 1] steps before each sequence (plan kernel output)
+  int32_t* unit_seq;             // [units] sequence holding each unit's first step (plan kernel output)
+  float* ws_o;                   // [heads][slots][512] unnormalised partials
+  float* ws_ml;                  // [heads][slots][2]: max (log2 units) and sum
   uint16_t* out;                 // [num_seqs, heads, 512] bf16
   float* lse;                    // [heads, num_seqs] or null
-  int32_t num_seqs, max_blocks, num_blocks, heads, max_splits, split_tokens;
+  int32_t num_seqs, max_blocks, num_blocks, heads, units, slots;
   float scale_log2;
 };
 

@@ -9,22 +9,29 @@
 // head q (576 values) is attention with keys = records and values = their
 // 512-value latents; the output stays in latent space.
 //
-// Kernel shape (one wave per (sequence, 16-head block, key split)):
-//  * 32 keys per step, double-buffered in LDS by direct-to-LDS loads.
-//  * S^T = K Q^T on v_mfma_f32_16x16x32_bf16: two 16-key row blocks x 18
-//    feature steps; a lane holds keys 4g..4g+3 and 16+4g..16+4g+3 (g = lane/16)
-//    of head lane%16 — exactly the B operand P^T of the PV product over those
-//    8 keys, so P needs no shuffle.
-//  * O^T = V^T P^T on the same MFMA, 32 blocks of 16 latent values.  The V^T
-//    operand (8 keys of one feature per lane) comes from the token-major tile
-//    through transposing LDS reads: two ds_read_b64_tr_b16 (bf16) or one
-//    ds_read_b64_tr_b8 (fp8 codes).
+// Kernel shape (two waves per (work unit, 16-head block)):
+//  * 32 keys per step, double-buffered in LDS by direct-to-LDS loads.  Wave w
+//    owns latent values 256w.. and rotary values 32w..: it loads only those
+//    runs, so neither wave waits for the other's loads.
+//  * Partial S^T = K Q^T over the wave's 288 values on
+//    v_mfma_f32_16x16x32_bf16: two 16-key row blocks x 9 feature steps.  A lane
+//    holds keys 4g..4g+3 and 16+4g..16+4g+3 (g = lane/16) of head lane%16 —
+//    exactly the B operand P^T of the PV product over those 8 keys, so P needs
+//    no shuffle.  The waves swap their 2 KiB of partial scores through LDS and
+//    both run the same online softmax.
+//  * O^T = V^T P^T on the same MFMA, 16 blocks of 16 latent values per wave.
+//    The V^T operand (8 keys of one value per lane) comes from the token-major
+//    tile through transposing LDS reads: two ds_read_b64_tr_b16 (bf16) or one
+//    ds_read_b64_tr_b8 (fp8 codes).  LDS reads run several MFMAs ahead.
 //  * fp8: codes are widened exactly (unit scale) by v_cvt_scalef32_pk_bf16_fp8,
 //    one instruction per pair.  Scores are accumulated per 128-value group and
 //    each key's fp32 group scale is applied to its partial score; for PV each
 //    key's scale is folded into P, group by group.
-//  * Unnormalised partials (O, max, sum) per split; mla_merge_kernel combines
-//    them in split order.
+//  * Work plan: the 32-key steps of all sequences, end to end, are cut into
+//    equal units (mla_plan_kernel finds where each starts), so every
+//    workgroup streams the same number of bytes whatever the length mix.
+//    Each segment (a unit's piece of one sequence) leaves an unnormalised
+//    partial (O, max, sum); mla_merge_kernel combines them in unit order.
 #include "device_common.h"
 #include "launch.h"
 
@@ -66,235 +73,358 @@ __device__ __forceinline__ u32x4_t widen8(uint32_t lo, uint32_t hi, float scale)
   return r;
 }
 
+// Waits for this wave's LDS operations and meets the other wave; loads in
+// flight keep flying.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 template <bool FP8>
 struct MlaCfg {
-  // LDS bytes of one 32-key step: bf16 [72 runs][32][16 B]; fp8 codes [32 runs][32][16 B],
-  // scales [32][16 B] (+512 B the second half-wave of the scale load writes), rotary [8 runs][32][16 B].
+  // LDS bytes of one 32-key step.  bf16: [72 runs][32 tokens][16 B].  fp8: codes
+  // [32 runs][32][16 B]; per wave a copy of the 32 keys' scales [32][16 B] plus the
+  // 512 B the upper half-wave of that load writes; rotary [8 runs][32][16 B].
   static constexpr int kCodes = 0;
   static constexpr int kScales = 32 * 32 * 16;
-  static constexpr int kRope = FP8 ? kScales + 1024 : 64 * 32 * 16;
+  static constexpr int kRope = FP8 ? kScales + 2 * 1024 : 64 * 32 * 16;
   static constexpr int kStage = FP8 ? kRope + 8 * 32 * 16 : 72 * 32 * 16;
-  static constexpr int kLoads = FP8 ? 16 + 1 + 4 : 36;     // direct loads per step
+  static constexpr int kLoads = FP8 ? 8 + 1 + 2 : 16 + 2;     // direct loads per wave per step
+  static constexpr int kXchg = 2 * kStage;                     // partial scores: [2 waves][64 lanes][8 fp32]
+  static constexpr int kLds = kXchg + 2 * 64 * 32;
   static constexpr int64_t kBlock = FP8 ? kMlaFp8Block : kMlaBf16Block;
-  static constexpr int64_t kBlkScales = 32 * 64 * 16;       // fp8 block: scales, then rotary
+  static constexpr int64_t kBlkScales = 32 * 64 * 16;          // fp8 block: scales, then rotary
   static constexpr int64_t kBlkRope = FP8 ? kBlkScales + 64 * 16 : 64 * 64 * 16;
 };
 
 }  // namespace
 
+// Two waves per (work unit, 16-head block).  Wave w owns latent
+// values 256w .. 256w+255 and rotary values 32w .. 32w+31: it loads only those
+// runs, forms the partial scores over them, and after the two waves swap
+// partials through LDS (both then hold identical scores and run the same
+// softmax) it accumulates its half of the output.
 template <bool FP8>
-__global__ __launch_bounds__(64) void mla_decode_kernel(const MlaArgs a) {
+__global__ __launch_bounds__(128) void mla_decode_kernel(const MlaArgs a) {
   using C = MlaCfg<FP8>;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * C::kStage];
-  const int lane = threadIdx.x, g = lane >> 4, c = lane & 15;
-  const int split = blockIdx.x, hb = blockIdx.y, s = blockIdx.z;
-  const int kv_len = a.kv_lens[s];
-  const int key_lo = split * a.split_tokens;
-  if (kv_len <= 0 || key_lo >= kv_len) return;
-  const int key_hi = min(kv_len, key_lo + a.split_tokens);
-  const int n_steps = (key_hi - key_lo + kMlaStepKeys - 1) / kMlaStepKeys;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[C::kLds];
+  const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // Workgroup -> (unit, head block).  Workgroups go round-robin to the 8 XCDs;
+  // with a unit count divisible by 8 the head blocks of one unit land on one
+  // XCD back to back and share its L2 copy of the unit's cache blocks.
+  const int nhb = a.heads / 16;
+  int unit, hb;
+  if ((a.units & 7) == 0) {
+    const int id = blockIdx.x;
+    unit = (id / (8 * nhb)) * 8 + (id & 7);
+    hb = (id >> 3) % nhb;
+  } else {
+    unit = blockIdx.x % a.units;
+    hb = blockIdx.x / a.units;
+  }
   const int head = hb * 16 + c;
   const float cs = a.scale_log2;
-
-  // Q^T as B operands: 18 feature steps of 8 values (features 32i + 8g ..).
-  u32x4_t qb[18];
-  {
-    const uint16_t* qrow = a.q + ((int64_t)s * a.heads + head) * kMlaRecord;
-#pragma unroll
-    for (int i = 0; i < 18; ++i) qb[i] = *(const u32x4_t*)(qrow + 32 * i + 8 * g);
-  }
-
-  const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks;
+  const int64_t total = a.seq_steps[a.num_seqs];
+  const int64_t u_hi = (int64_t)(unit + 1) * total / a.units;
+  int64_t x = (int64_t)unit * total / a.units;
+  int s = a.unit_seq[unit];
   const uint32_t smem_base = lds_addr(smem);
-  // step t covers keys key_lo + 32t .. +31: half (key / 32) & 1 of block key / 64
-  auto issue = [&](int t, int st) {
-    const int key0 = key_lo + kMlaStepKeys * t;
-    const int blk = clamp_block(bt[key0 >> 6], a.num_blocks);
-    const unsigned char* b = a.pool + (int64_t)blk * C::kBlock + ((key0 >> 5) & 1) * 32 * 16;
-    const uint32_t lds = smem_base + st * C::kStage;
-    const int run = lane >> 5, tok = lane & 31;
-    if constexpr (FP8) {
-#pragma unroll
-      for (int n = 0; n < 16; ++n) dma16(b + (2 * n + run) * 1024 + tok * 16, lds + C::kCodes + n * 1024);
-      dma16(b + C::kBlkScales + tok * 16, lds + C::kScales);
-#pragma unroll
-      for (int n = 0; n < 4; ++n) dma16(b + C::kBlkRope + (2 * n + run) * 1024 + tok * 16, lds + C::kRope + n * 1024);
-    } else {
-#pragma unroll
-      for (int n = 0; n < 36; ++n) dma16(b + (2 * n + run) * 1024 + tok * 16, lds + n * 1024);
-    }
-  };
 
-  f32x4_t o[32];
-#pragma unroll
-  for (int b = 0; b < 32; ++b) o[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
+  // one segment per sequence the unit touches
+  for (; x < u_hi; ++s) {
+    const int64_t p0 = a.seq_steps[s];
+    const int64_t seg_end = min(u_hi, a.seq_steps[s + 1]);
+    const int kv_len = a.kv_lens[s];
+    const int key_lo = (int)(x - p0) * kMlaStepKeys;
+    const int key_hi = min(kv_len, (int)(seg_end - p0) * kMlaStepKeys);
+    x = seg_end;
+    const int n_steps = (key_hi - key_lo + kMlaStepKeys - 1) / kMlaStepKeys;
 
-  issue(0, 0);
-  for (int t = 0; t < n_steps; ++t) {
-    const int st = t & 1;
-    if (t + 1 < n_steps) {
-      issue(t + 1, st ^ 1);
-      wait_vmem<C::kLoads>();
-    } else {
-      wait_vmem<0>();
+    // Q^T as B operands of this wave's 9 feature steps (32 values each): latent
+    // steps 8w .. 8w+7, then rotary step 16 + w; lane group g holds values 8g ..
+    u32x4_t qb[9];
+    {
+      const uint16_t* qrow = a.q + ((int64_t)s * a.heads + head) * kMlaRecord + 8 * g;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) qb[j] = *(const u32x4_t*)(qrow + 32 * (8 * w + j));
+      qb[8] = *(const u32x4_t*)(qrow + 32 * (16 + w));
     }
-    unsigned char* stage = smem + st * C::kStage;
-    const int key0 = key_lo + kMlaStepKeys * t;
-    const int valid = key_hi - key0;                 // keys of this step that count (1..32)
-    if (valid < kMlaStepKeys) {
-      // Keys past the split's end (past the sequence) may hold anything: give
-      // them zero values (and unit scales) so 0 * junk cannot reach O.
+    // The segment's block ids, lane l holding the (l+1)-th (a segment spans at
+    // most 64 blocks): the step loop then makes no load the compiler tracks,
+    // so none of its waits can stall on the direct loads in flight.
+    const int blk0 = key_lo >> 6;
+    const int n_blk = ((key_hi - 1) >> 6) - blk0 + 1;
+    const int bt_lane = lane < n_blk ? a.block_tables[(int64_t)s * a.max_blocks + blk0 + lane] : 0;
+#pragma unroll
+    for (int j = 0; j < 9; ++j) asm volatile("" ::"v"(qb[j]));
+    asm volatile("" ::"v"(bt_lane));
+
+    // step t covers keys key_lo + 32t .. +31: half (key / 32) & 1 of block key / 64.
+    // Load n moves runs 2n and 2n+1 (32 tokens each); the wave issues only its own.
+    auto issue = [&](int t, int st) {
+      const int key0 = key_lo + kMlaStepKeys * t;
+      const int blk = clamp_block(__builtin_amdgcn_readlane(bt_lane, (key0 >> 6) - blk0), a.num_blocks);
+      const unsigned char* b = a.pool + (int64_t)blk * C::kBlock + ((key0 >> 5) & 1) * 32 * 16 + (lane >> 5) * 1024 +
+                               (lane & 31) * 16;
+      const uint32_t lds = smem_base + st * C::kStage;
       if constexpr (FP8) {
-        for (int e = lane; e < 32 * 32; e += 64) {
-          const int run = e >> 5, tok = e & 31;
-          if (tok >= valid) *(u32x4_t*)(stage + C::kCodes + run * 512 + tok * 16) = u32x4_t{0u, 0u, 0u, 0u};
-        }
-        if (lane < 32 && lane >= valid)
-          *(f32x4_t*)(stage + C::kScales + lane * 16) = f32x4_t{1.f, 1.f, 1.f, 1.f};
+#pragma unroll
+        for (int n = 8 * w; n < 8 * w + 8; ++n) dma16(b + 2 * n * 1024, lds + C::kCodes + n * 1024);
+        dma16(b - (lane >> 5) * 1024 + C::kBlkScales, lds + C::kScales + w * 1024);
+#pragma unroll
+        for (int n = 2 * w; n < 2 * w + 2; ++n) dma16(b + C::kBlkRope + 2 * n * 1024, lds + C::kRope + n * 1024);
       } else {
-        for (int e = lane; e < 64 * 32; e += 64) {
-          const int run = e >> 5, tok = e & 31;
-          if (tok >= valid) *(u32x4_t*)(stage + run * 512 + tok * 16) = u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int n = 16 * w; n < 16 * w + 16; ++n) dma16(b + 2 * n * 1024, lds + n * 1024);
+#pragma unroll
+        for (int n = 32 + 2 * w; n < 34 + 2 * w; ++n) dma16(b + 2 * n * 1024, lds + n * 1024);
+      }
+    };
+
+    f32x4_t o[16];
+#pragma unroll
+    for (int b = 0; b < 16; ++b) o[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY, l_run = 0.f;
+    // this lane's keys as a score row: kappa(g, j) = 4g + j (j < 4), 16 + 4g + (j - 4)
+    auto kappa = [&](int j) { return j < 4 ? 4 * g + j : 16 + 4 * g + (j - 4); };
+
+    issue(0, 0);
+    for (int t = 0; t < n_steps; ++t) {
+      const int st = t & 1;
+      if (t + 1 < n_steps) {
+        issue(t + 1, st ^ 1);
+        wait_vmem<C::kLoads>();
+      } else {
+        wait_vmem<0>();
+      }
+      unsigned char* stage = smem + st * C::kStage;
+      const int key0 = key_lo + kMlaStepKeys * t;
+      const int valid = key_hi - key0;                 // keys of this step that count (1..32)
+      if (valid < kMlaStepKeys) {
+        // Keys past the sequence's end may hold anything: give this wave's latent
+        // runs zeros (and its scales ones) there, so 0 * junk cannot reach O.
+        if constexpr (FP8) {
+          for (int e = lane; e < 16 * 32; e += 64) {
+            const int run = 16 * w + (e >> 5), tok = e & 31;
+            if (tok >= valid) *(u32x4_t*)(stage + C::kCodes + run * 512 + tok * 16) = u32x4_t{0u, 0u, 0u, 0u};
+          }
+          if (lane < 32 && lane >= valid)
+            *(f32x4_t*)(stage + C::kScales + w * 1024 + lane * 16) = f32x4_t{1.f, 1.f, 1.f, 1.f};
+        } else {
+          for (int e = lane; e < 32 * 32; e += 64) {
+            const int run = 32 * w + (e >> 5), tok = e & 31;
+            if (tok >= valid) *(u32x4_t*)(stage + run * 512 + tok * 16) = u32x4_t{0u, 0u, 0u, 0u};
+          }
         }
       }
-    }
 
-    // ---- S^T = K Q^T: row blocks of keys 0-15 and 16-31 ----
-    // A lane's S^T rows are keys 4g+r (s0) and 16+4g+r (s1), r = 0..3: kappa(g, j) below.
-    f32x4_t s0 = f32x4_t{0.f, 0.f, 0.f, 0.f}, s1 = s0;
-    float vs[8][4];                                  // fp8: scale of key kappa(g, j), 128-value group q
-    if constexpr (FP8) {
+      // ---- partial S^T = K Q^T over this wave's values; row blocks keys 0-15 and 16-31 ----
+      // fp8: scale of key kappa(j) for latent group 2w + q
+      float vs[8][2];
+      if constexpr (FP8) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int key = j < 4 ? 4 * g + j : 16 + 4 * g + (j - 4);
-        const f32x4_t sc = *(const f32x4_t*)(stage + C::kScales + key * 16);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) vs[j][q] = sc[q];
-      }
-      // rotary part (bf16), then each latent group's codes widened exactly (scale 1)
-      // with the group's partial scores scaled per key in fp32
-#pragma unroll
-      for (int i = 16; i < 18; ++i) {
-        const int off = C::kRope + (4 * (i - 16) + g) * 512;
-        s0 = mfma16(*(const u32x4_t*)(stage + off + c * 16), qb[i], s0);
-        s1 = mfma16(*(const u32x4_t*)(stage + off + (16 + c) * 16), qb[i], s1);
-      }
-#pragma unroll
-      for (int gr = 0; gr < 4; ++gr) {
-        f32x4_t t0 = f32x4_t{0.f, 0.f, 0.f, 0.f}, t1 = t0;
-#pragma unroll
-        for (int i = 4 * gr; i < 4 * gr + 4; ++i) {
-          const int off = C::kCodes + (2 * i + (g >> 1)) * 512 + (g & 1) * 8;
-          const u32x2_t c0 = *(const u32x2_t*)(stage + off + c * 16);
-          const u32x2_t c1 = *(const u32x2_t*)(stage + off + (16 + c) * 16);
-          t0 = mfma16(widen8(c0[0], c0[1], 1.0f), qb[i], t0);
-          t1 = mfma16(widen8(c1[0], c1[1], 1.0f), qb[i], t1);
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          s0[r] = __builtin_fmaf(t0[r], vs[r][gr], s0[r]);
-          s1[r] = __builtin_fmaf(t1[r], vs[4 + r][gr], s1[r]);
+        for (int j = 0; j < 8; ++j) {
+          const u32x2_t sc = *(const u32x2_t*)(stage + C::kScales + w * 1024 + kappa(j) * 16 + 8 * w);
+          vs[j][0] = __uint_as_float(sc[0]);
+          vs[j][1] = __uint_as_float(sc[1]);
         }
       }
-    } else {
+      // op k: k = 0, 1 rotary (row block k); k >= 2 latent step (k - 2) / 2, row block k & 1
+      const unsigned char* kr = stage + C::kRope + (4 * w + g) * 512 + c * 16;
+      const unsigned char* kl = FP8 ? stage + C::kCodes + (16 * w + (g >> 1)) * 512 + (g & 1) * 8 + c * 16
+                                    : stage + (32 * w + g) * 512 + c * 16;
+      constexpr int kQ = 18, kAq = 8;
+      auto qk_read = [&](int k) -> u32x4_t {
+        if (k < 2) return *(const u32x4_t*)(kr + k * 256);
+        const int j = (k - 2) >> 1, row = k & 1;
+        if constexpr (FP8) {
+          const u32x2_t v = *(const u32x2_t*)(kl + j * 1024 + row * 256);
+          return u32x4_t{v[0], v[1], 0u, 0u};
+        } else {
+          return *(const u32x4_t*)(kl + j * 2048 + row * 256);
+        }
+      };
+      u32x4_t rd[kQ];
 #pragma unroll
-      for (int i = 0; i < 18; ++i) {
-        const int off = (4 * i + g) * 512;
-        s0 = mfma16(*(const u32x4_t*)(stage + off + c * 16), qb[i], s0);
-        s1 = mfma16(*(const u32x4_t*)(stage + off + (16 + c) * 16), qb[i], s1);
+      for (int k = 0; k < kAq; ++k) rd[k] = qk_read(k);
+      f32x4_t s0 = f32x4_t{0.f, 0.f, 0.f, 0.f}, s1 = s0, t0 = s0, t1 = s0;
+#pragma unroll
+      for (int k = 0; k < kQ; ++k) {
+        const int row = k & 1;
+        if (k < 2) {
+          if (row) s1 = mfma16(rd[k], qb[8], s1);
+          else s0 = mfma16(rd[k], qb[8], s0);
+        } else {
+          const int j = (k - 2) >> 1;
+          if constexpr (FP8) {
+            // codes widen exactly (unit scale); the group's partial gets the key scales in fp32
+            const u32x4_t kv = widen8(rd[k][0], rd[k][1], 1.0f);
+            if (row) t1 = mfma16(kv, qb[j], t1);
+            else t0 = mfma16(kv, qb[j], t0);
+            if (row && (j & 3) == 3) {
+              const int q = j >> 2;
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                s0[r] = __builtin_fmaf(t0[r], vs[r][q], s0[r]);
+                s1[r] = __builtin_fmaf(t1[r], vs[4 + r][q], s1[r]);
+              }
+              t0 = f32x4_t{0.f, 0.f, 0.f, 0.f};
+              t1 = t0;
+            }
+          } else {
+            if (row) s1 = mfma16(rd[k], qb[j], s1);
+            else s0 = mfma16(rd[k], qb[j], s0);
+          }
+        }
+        if (k + kAq < kQ) rd[k + kAq] = qk_read(k + kAq);
+        __builtin_amdgcn_sched_barrier(0);            // keep the reads kAq operations ahead
       }
-    }
 
-    // ---- online softmax over this step's keys (head c; keys 4g+r and 16+4g+r) ----
-    float mx = -INFINITY;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      if (4 * g + r >= valid) s0[r] = -INFINITY;
-      if (16 + 4 * g + r >= valid) s1[r] = -INFINITY;
-      mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
-    }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const bool grow = mx * cs > m_run * cs + kLazyRescale;
-    if (__any(grow)) {
-      const float m_new = grow ? mx : m_run;
-      const float alpha = grow ? fast_exp2((m_run - m_new) * cs) : 1.f;
-      l_run *= alpha;
-#pragma unroll
-      for (int b = 0; b < 32; ++b) o[b] *= alpha;
-      m_run = m_new;
-    }
-    const float mb = m_run == -INFINITY ? 0.f : m_run * cs;
-    float p[8];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      p[r] = fast_exp2(__builtin_fmaf(s0[r], cs, -mb));
-      p[4 + r] = fast_exp2(__builtin_fmaf(s1[r], cs, -mb));
-    }
-    l_run += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+      // ---- swap partial scores with the other wave (same lane = same keys and head) ----
+      float* x_own = (float*)(smem + C::kXchg + w * 2048 + lane * 32);
+      const float* x_other = (const float*)(smem + C::kXchg + (1 - w) * 2048 + lane * 32);
+      lds_barrier();                                   // the other wave has read the previous partials
+      *(f32x4_t*)x_own = s0;
+      *(f32x4_t*)(x_own + 4) = s1;
+      lds_barrier();
+      s0 += *(const f32x4_t*)x_other;                  // fp32 addition commutes: both waves get the same sums
+      s1 += *(const f32x4_t*)(x_other + 4);
 
-    // ---- O^T += V^T P^T over the 8 keys this lane's P covers ----
-    if constexpr (FP8) {
-      // each key's scale for 128-value group gr is folded into P
-      // transposing read: this lane (as a source) points at key kappa(g, c/2), features 8(c%2)..
-      const int src_r = c >> 1;
-      const int src_key = src_r < 4 ? 4 * g + src_r : 16 + 4 * g + (src_r - 4);
-      const int tr_off = C::kCodes + src_key * 16 + (c & 1) * 8;
+      // ---- online softmax over this step's keys (head c; keys kappa(0..7)) ----
+      float mx = -INFINITY;
 #pragma unroll
-      for (int gr = 0; gr < 4; ++gr) {
+      for (int r = 0; r < 4; ++r) {
+        if (4 * g + r >= valid) s0[r] = -INFINITY;
+        if (16 + 4 * g + r >= valid) s1[r] = -INFINITY;
+        mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const bool grow = mx * cs > m_run * cs + kLazyRescale;
+      if (__any(grow)) {
+        const float m_new = grow ? mx : m_run;
+        const float alpha = grow ? fast_exp2((m_run - m_new) * cs) : 1.f;
+        l_run *= alpha;
+#pragma unroll
+        for (int b = 0; b < 16; ++b) o[b] *= alpha;
+        m_run = m_new;
+      }
+      const float mb = m_run == -INFINITY ? 0.f : m_run * cs;
+      float p[8];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        p[r] = fast_exp2(__builtin_fmaf(s0[r], cs, -mb));
+        p[4 + r] = fast_exp2(__builtin_fmaf(s1[r], cs, -mb));
+      }
+      l_run += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+
+      // ---- O^T += V^T P^T over the 8 keys this lane's P covers; this wave's 16 value blocks ----
+      constexpr int kP = 16, kAp = 6;
+      if constexpr (FP8) {
+        // transposing read: this lane (as a source) points at key kappa(c / 2), codes 8(c % 2) ..
+        const int src_r = c >> 1;
+        const int src_key = src_r < 4 ? 4 * g + src_r : 16 + 4 * g + (src_r - 4);
+        const unsigned char* vb = stage + C::kCodes + (16 * w) * 512 + src_key * 16 + (c & 1) * 8;
+        auto pv_read = [&](int bb) -> v2i32_t {
+          return __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i32*)(vb + bb * 512));
+        };
+        v2i32_t rv[kP];
+#pragma unroll
+        for (int k = 0; k < kAp; ++k) rv[k] = pv_read(k);
+        u32x4_t pb[2];                                 // P with each key's group scale folded in
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) pb[q][i] = pack_bf16(p[2 * i] * vs[2 * i][q], p[2 * i + 1] * vs[2 * i + 1][q]);
+#pragma unroll
+        for (int bb = 0; bb < kP; ++bb) {
+          const u32x4_t va = widen8((uint32_t)rv[bb][0], (uint32_t)rv[bb][1], 1.0f);
+          o[bb] = mfma16(va, pb[bb >> 3], o[bb]);
+          if (bb + kAp < kP) rv[bb + kAp] = pv_read(bb + kAp);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      } else {
+        // two transposing reads: keys 4g + (c/4) and 16 + 4g + (c/4); values 4(c%4) ..
+        const unsigned char* vb = stage + (32 * w) * 512 + (4 * g + (c >> 2)) * 16 + (c & 1) * 8 + ((c & 3) >> 1) * 512;
+        auto pv_read = [&](int bb) -> u32x4_t {
+          const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vb + bb * 1024));
+          const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vb + bb * 1024 + 256));
+          const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo), h2 = __builtin_bit_cast(u32x2_t, hi);
+          return u32x4_t{l2[0], l2[1], h2[0], h2[1]};
+        };
+        u32x4_t rv[kP];
+#pragma unroll
+        for (int k = 0; k < kAp; ++k) rv[k] = pv_read(k);
         u32x4_t pb;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) pb[q] = pack_bf16(p[2 * q] * vs[2 * q][gr], p[2 * q + 1] * vs[2 * q + 1][gr]);
+        for (int i = 0; i < 4; ++i) pb[i] = pack_bf16(p[2 * i], p[2 * i + 1]);
 #pragma unroll
-        for (int bb = 0; bb < 8; ++bb) {
-          const int b = 8 * gr + bb;                  // latent values 16b .. 16b+15 live in code run b
-          const v2i32_t codes = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i32*)(stage + tr_off + b * 512));
-          const u32x4_t va = widen8((uint32_t)codes[0], (uint32_t)codes[1], 1.0f);
-          o[b] = mfma16(va, pb, o[b]);
+        for (int bb = 0; bb < kP; ++bb) {
+          o[bb] = mfma16(rv[bb], pb, o[bb]);
+          if (bb + kAp < kP) rv[bb + kAp] = pv_read(bb + kAp);
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
-    } else {
-      u32x4_t pb;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) pb[q] = pack_bf16(p[2 * q], p[2 * q + 1]);
-      // two transposing reads: keys 4g + (c/4) and 16 + 4g + (c/4); features 4(c%4)..
-      const int tr0 = (4 * g + (c >> 2)) * 16 + (c & 1) * 8 + ((c & 3) >> 1) * 512;
-      const int tr1 = tr0 + 16 * 16;
-#pragma unroll
-      for (int b = 0; b < 32; ++b) {
-        const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(stage + tr0 + 2 * b * 512));
-        const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(stage + tr1 + 2 * b * 512));
-        const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo), h2 = __builtin_bit_cast(u32x2_t, hi);
-        o[b] = mfma16(u32x4_t{l2[0], l2[1], h2[0], h2[1]}, pb, o[b]);
-      }
     }
-  }
 
-  // ---- partial of this split ----
-  float l_tot = l_run + __shfl_xor(l_run, 16);
-  l_tot += __shfl_xor(l_tot, 32);
-  const int64_t slot = ((int64_t)s * a.heads + head) * a.max_splits + split;
-  float* wo = a.ws_o + slot * kMlaLatent;
+    // ---- partial of this segment: wave w writes latent values 256w .. 256w+255 ----
+    float l_tot = l_run + __shfl_xor(l_run, 16);
+    l_tot += __shfl_xor(l_tot, 32);
+    const int64_t slot = (int64_t)head * a.slots + s + unit;
+    float* wo = a.ws_o + slot * kMlaLatent + 256 * w;
 #pragma unroll
-  for (int b = 0; b < 32; ++b) *(f32x4_t*)(wo + 16 * b + 4 * g) = o[b];
-  if (g == 0) *(float2*)(a.ws_ml + slot * 2) = make_float2(m_run == -INFINITY ? -INFINITY : m_run * cs, l_tot);
+    for (int b = 0; b < 16; ++b) *(f32x4_t*)(wo + 16 * b + 4 * g) = o[b];
+    if (w == 0 && g == 0)
+      *(float2*)(a.ws_ml + slot * 2) = make_float2(m_run == -INFINITY ? -INFINITY : m_run * cs, l_tot);
+  }
 }
 
-// One workgroup per (sequence, head): combine the splits in order, normalise, store bf16 and the LSE.
+// One workgroup of 1024 threads: steps per sequence (ceil(kv / 32)), their
+// exclusive prefix sums, and the sequence where each unit's step range starts.
+__global__ __launch_bounds__(1024) void mla_plan_kernel(const MlaArgs a) {
+  __shared__ int64_t part[1024];
+  const int t = threadIdx.x;
+  const int per = (a.num_seqs + 1023) / 1024;
+  const int s0 = min(a.num_seqs, t * per), s1 = min(a.num_seqs, s0 + per);
+  int64_t sum = 0;
+  for (int s = s0; s < s1; ++s) sum += (a.kv_lens[s] + kMlaStepKeys - 1) / kMlaStepKeys;
+  part[t] = sum;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {     // inclusive scan
+    const int64_t v = t >= off ? part[t - off] : 0;
+    __syncthreads();
+    part[t] += v;
+    __syncthreads();
+  }
+  const int64_t total = part[1023];
+  int64_t run = t > 0 ? part[t - 1] : 0;
+  for (int s = s0; s < s1; ++s) {
+    a.seq_steps[s] = run;
+    const int64_t next = run + (a.kv_lens[s] + kMlaStepKeys - 1) / kMlaStepKeys;
+    // units whose first step (unit * total / units) lies in [run, next)
+    const int64_t g_lo = (run * a.units + total - 1) / total, g_hi = (next * a.units + total - 1) / total;
+    for (int64_t u = g_lo; u < g_hi; ++u) a.unit_seq[u] = s;
+    run = next;
+  }
+  if (t == 0) a.seq_steps[a.num_seqs] = total;
+}
+
+// One workgroup per (sequence, head): combine the sequence's segment partials
+// in unit order, normalise, store bf16 and the LSE.
 __global__ __launch_bounds__(128) void mla_merge_kernel(const MlaArgs a) {
   const int s = blockIdx.x / a.heads, h = blockIdx.x % a.heads;
-  const int kv_len = a.kv_lens[s];
-  const int nsplit = min(a.max_splits, (kv_len + a.split_tokens - 1) / a.split_tokens);
-  const int64_t slot0 = ((int64_t)s * a.heads + h) * a.max_splits;
+  const int64_t total = a.seq_steps[a.num_seqs];
+  const int64_t p0 = a.seq_steps[s], p1 = a.seq_steps[s + 1];
+  // unit holding step x: ((x + 1) * units - 1) / total
+  const int u0 = (int)(((p0 + 1) * a.units - 1) / total), u1 = (int)((p1 * a.units - 1) / total);
+  const int64_t slot0 = (int64_t)h * a.slots + s + u0;
+  const int n = u1 - u0 + 1;
   float M, L;
-  merge_weights(a.ws_ml + slot0 * 2, nsplit, 1, M, L);
+  merge_weights(a.ws_ml + slot0 * 2, n, 1, M, L);
   const int t = threadIdx.x;
   f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  for (int sp = 0; sp < nsplit; ++sp) {
-    const float m = a.ws_ml[(slot0 + sp) * 2];
+  for (int i = 0; i < n; ++i) {
+    const float m = a.ws_ml[(slot0 + i) * 2];
     if (m == -INFINITY) continue;
-    acc += *(const f32x4_t*)(a.ws_o + (slot0 + sp) * kMlaLatent + 4 * t) * fast_exp2(m - M);
+    acc += *(const f32x4_t*)(a.ws_o + (slot0 + i) * kMlaLatent + 4 * t) * fast_exp2(m - M);
   }
   acc *= 1.f / L;
   uint16_t* orow = a.out + ((int64_t)s * a.heads + h) * kMlaLatent + 4 * t;
@@ -350,10 +480,13 @@ __global__ __launch_bounds__(64) void mla_append_kernel(const MlaAppendArgs a) {
 }
 
 hipError_t launch_mla_decode(bool fp8, const MlaArgs& a, hipStream_t stream) {
-  const dim3 grid(a.max_splits, a.heads / 16, a.num_seqs);
-  if (fp8) hipLaunchKernelGGL(mla_decode_kernel<true>, grid, dim3(64), 0, stream, a);
-  else hipLaunchKernelGGL(mla_decode_kernel<false>, grid, dim3(64), 0, stream, a);
+  hipLaunchKernelGGL(mla_plan_kernel, dim3(1), dim3(1024), 0, stream, a);
   hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 grid(a.units * (a.heads / 16));
+  if (fp8) hipLaunchKernelGGL(mla_decode_kernel<true>, grid, dim3(128), 0, stream, a);
+  else hipLaunchKernelGGL(mla_decode_kernel<false>, grid, dim3(128), 0, stream, a);
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(mla_merge_kernel, dim3(a.num_seqs * a.heads), dim3(128), 0, stream, a);
   return hipGetLastError();

@@ -24,6 +24,10 @@ Recipe (fixed here, stated once):
   * block table: a pool of ceil(1.25 * needed) blocks; the table is a seeded
     draw of ``needed`` distinct block ids.
   * decode context lengths: integers uniform on [lo, hi], both ends included.
+  * MLA decode batch: per sequence, latents [kv, 512] then rotary parts
+    [kv, 64] drawn N(0, 1) on the device from one seeded generator, rounded to
+    bf16; queries [requests, heads, 576] N(0, 1) bf16 (GLM5.3 PP-split
+    deployment notes §1, §4: one shared latent record per token).
   * sampled rows: every chunk's first and last token, tokens on both sides of
     every 64- and 128-token tile boundary (a bounded subset when there are
     many), and a seeded uniform fill; heads uniform.
@@ -60,6 +64,7 @@ class Workload:
     decode_requests: int = 0
     decode_ctx: tuple = (0, 0)
     prefill_past: int = 0
+    scale_dim: int = 0         # softmax scale 1/sqrt(scale_dim); 0: 1/sqrt(head_dim)
 
     @property
     def n_chunks(self) -> int:
@@ -67,7 +72,7 @@ class Workload:
 
     @property
     def scale(self) -> float:
-        return 1.0 / math.sqrt(self.head_dim)
+        return 1.0 / math.sqrt(self.scale_dim or self.head_dim)
 
 
 WORKLOADS = {
@@ -88,6 +93,13 @@ WORKLOADS = {
         "32 q heads / 8 KV heads, d=128, bf16, paged KV (64)",
         65536 + 2048, 2048, 32, 8, 128, 128, "bf16", "paged", seed=505,
         decode_requests=256, decode_ctx=(1024, 32768), prefill_past=65536),
+    # absorbed MLA decode: one 576-value record (512 latent + 64 rotary) per token shared by all
+    # heads; the softmax scale is the expanded head's, 1/sqrt(128 + 64)
+    "mla_decode": Workload(
+        "mla_decode", "256 MLA decodes, ctx ~ U[1024, 32768], 16 q heads over one shared 512+64 latent record "
+        "per token (bf16 or fp8 latent cache), paged KV (64)",
+        0, 0, 16, 1, 576, 512, "bf16", "paged", seed=606,
+        decode_requests=256, decode_ctx=(1024, 32768), scale_dim=192),
 }
 
 
@@ -162,6 +174,24 @@ def context_lengths(n: int, lo: int, hi: int, seed: int) -> np.ndarray:
     """Seeded integers uniform on [lo, hi] (both ends included), int32."""
     rng = np.random.default_rng(seed)
     return rng.integers(lo, hi, size=n, endpoint=True).astype(np.int32)
+
+
+def batch_block_tables(kv_lens, seed: int):
+    """Disjoint seeded blocks for every sequence of a batch: ([n, max_blocks] int32, pool_blocks)."""
+    needed = [max(1, math.ceil(int(k) / BLOCK_SIZE)) for k in kv_lens]
+    pool_blocks = pool_size(sum(needed))
+    perm = block_table(sum(needed), seed, pool_blocks)
+    tables = np.zeros((len(needed), max(needed) if needed else 1), dtype=np.int32)
+    off = 0
+    for s, nb in enumerate(needed):
+        tables[s, :nb] = perm[off: off + nb]
+        off += nb
+    return tables, pool_blocks
+
+
+def mla_record_seed(w: Workload, s: int) -> int:
+    """Seed of sequence s's latent records (device draws: latents, then rotary parts)."""
+    return w.seed * 1000 + 10 + s
 
 
 def sample_rows(chunk_len: int, heads: int, n: int, seed: int):

@@ -231,37 +231,33 @@ def test_decode_after_append_end_to_end(fmt):
 
 @pytest.mark.parametrize("fmt", ["bf16", "fp8"])
 def test_decode_batch_workload_sampled(fmt):
-    """256 decode requests, contexts uniform in [1024, 32768], 16 heads: the benchmark's launch."""
-    kv = inputs.context_lengths(256, 1024, 32768, 77)
-    needed = [math.ceil(int(k) / 64) for k in kv]
-    nb = inputs.pool_size(sum(needed))
-    perm = inputs.block_table(sum(needed), 78, nb)
-    tables = np.zeros((256, max(needed)), dtype=np.int32)
-    off = 0
-    for s in range(256):
-        tables[s, : needed[s]] = perm[off: off + needed[s]]
-        off += needed[s]
+    """The benchmark's MLA decode batch (same seeds, tables and launch): sampled sequences vs the oracle."""
+    w = inputs.WORKLOADS["mla_decode"]
+    kv = inputs.context_lengths(w.decode_requests, w.decode_ctx[0], w.decode_ctx[1], w.seed)
+    tables, nb = inputs.batch_block_tables(kv, w.seed + 1)
     tables_d = torch.from_numpy(tables).cuda()
     pool = new_pool(fmt, nb, POISON)
     log(f"mla workload fmt={fmt}: filling {int(kv.sum())} tokens")
     gen = torch.Generator(device="cuda")
-    sample = sorted({0, 255, int(np.argmax(kv)), int(np.argmin(kv)), 17, 130})
+    n = w.decode_requests
+    sample = sorted({0, n - 1, int(np.argmax(kv)), int(np.argmin(kv)), 17, 130})
     kept = {}
-    for s in range(256):
-        gen.manual_seed(1000 + s)
+    for s in range(n):
+        gen.manual_seed(inputs.mla_record_seed(w, s))
         lat = torch.randn((int(kv[s]), 512), generator=gen, device="cuda").to(torch.bfloat16)
         rope = torch.randn((int(kv[s]), 64), generator=gen, device="cuda").to(torch.bfloat16)
         L.chunkattn_mla_kv_append(lat, rope, 0, tables_d[s], pool, FMTS[fmt])
         if s in sample:
             kept[s] = (bits(lat.cpu()), bits(rope.cpu()))
-    q = inputs.normal((256, 16, 576), 79, "bf16")
+    q = inputs.normal_device((n, w.heads, w.head_dim), w.seed + 2, "bf16")
+    assert w.scale == SCALE
     log(f"mla workload fmt={fmt}: decode")
-    out, lse = L.chunk_mla_decode(q.cuda(), pool, FMTS[fmt], tables_d, kv, SCALE, return_lse=True)
-    out, lse = out.cpu(), lse.cpu()
+    out, lse = L.chunk_mla_decode(q, pool, FMTS[fmt], tables_d, kv, w.scale, return_lse=True)
+    out, lse, qb = out.cpu(), lse.cpu(), bits(q.cpu())
     assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
     worst = worst_lse = 0.0
     for s in sample:
-        ref, ref_lse = mla.decode(bits(q)[s], mla.records(*kept[s], fmt), SCALE)
+        ref, ref_lse = mla.decode(qb[s], mla.records(*kept[s], fmt), SCALE)
         worst = max(worst, max_err(out[s], ref))
         worst_lse = max(worst_lse, max_err(lse[:, s], ref_lse))
     log(f"  sampled {sample}: max abs err {worst:.3e} lse {worst_lse:.3e}")
