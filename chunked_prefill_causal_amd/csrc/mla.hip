@@ -77,6 +77,26 @@ __device__ __forceinline__ u32x4_t widen8(uint32_t lo, uint32_t hi, float scale)
 // flight keep flying.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// Max / sum of x over lanes l and l^16 (then l^32) on the vector ALU:
+// v_permlane16_swap / v_permlane32_swap hand each lane its partner's value.
+// Both lanes of a pair add in the same order, so they hold identical sums.
+__device__ __forceinline__ float xor16_max(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor16_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 template <bool FP8>
 struct MlaCfg {
   // LDS bytes of one 32-key step.  bf16: [72 runs][32 tokens][16 B].  fp8: codes
@@ -86,9 +106,17 @@ struct MlaCfg {
   static constexpr int kScales = 32 * 32 * 16;
   static constexpr int kRope = FP8 ? kScales + 2 * 1024 : 64 * 32 * 16;
   static constexpr int kStage = FP8 ? kRope + 8 * 32 * 16 : 72 * 32 * 16;
+  // ring depth: kStages - 1 steps in flight per wave while one is consumed.
+  // fp8 steps are small, so three of them (two workgroups per CU) keep more
+  // bytes in flight than two (three workgroups per CU) would.
+  static constexpr int kStages = FP8 ? 3 : 2;
   static constexpr int kLoads = FP8 ? 8 + 1 + 2 : 16 + 2;     // direct loads per wave per step
-  static constexpr int kXchg = 2 * kStage;                     // partial scores: [2 waves][64 lanes][8 fp32]
-  static constexpr int kLds = kXchg + 2 * 64 * 32;
+  // partial scores: [kXSlots][2 waves][64 lanes][8 fp32].  With two slots (by
+  // step parity) one barrier per step suffices; bf16 keeps one slot and a
+  // second barrier so that two workgroups still fit in a CU's LDS.
+  static constexpr int kXSlots = FP8 ? 2 : 1;
+  static constexpr int kXchg = kStages * kStage;
+  static constexpr int kLds = kXchg + kXSlots * 2 * 64 * 32;
   static constexpr int64_t kBlock = FP8 ? kMlaFp8Block : kMlaBf16Block;
   static constexpr int64_t kBlkScales = 32 * 64 * 16;          // fp8 block: scales, then rotary
   static constexpr int64_t kBlkRope = FP8 ? kBlkScales + 64 * 16 : 64 * 64 * 16;
@@ -186,15 +214,18 @@ __global__ __launch_bounds__(128) void mla_decode_kernel(const MlaArgs a) {
     // this lane's keys as a score row: kappa(g, j) = 4g + j (j < 4), 16 + 4g + (j - 4)
     auto kappa = [&](int j) { return j < 4 ? 4 * g + j : 16 + 4 * g + (j - 4); };
 
-    issue(0, 0);
+#pragma unroll
+    for (int i = 0; i < C::kStages - 1; ++i)
+      if (i < n_steps) issue(i, i);
+    int st = 0;                                        // stage of step t: t % kStages
     for (int t = 0; t < n_steps; ++t) {
-      const int st = t & 1;
-      if (t + 1 < n_steps) {
-        issue(t + 1, st ^ 1);
-        wait_vmem<C::kLoads>();
-      } else {
-        wait_vmem<0>();
-      }
+      // refill the stage step t-1 used, then wait for step t's loads only
+      const int t_next = t + C::kStages - 1;
+      if (t_next < n_steps) issue(t_next, st == 0 ? C::kStages - 1 : st - 1);
+      const int ahead = min(C::kStages - 1, n_steps - 1 - t);   // steps issued after t
+      if (C::kStages > 2 && ahead >= 2) wait_vmem<2 * C::kLoads>();
+      else if (ahead >= 1) wait_vmem<C::kLoads>();
+      else wait_vmem<0>();
       unsigned char* stage = smem + st * C::kStage;
       const int key0 = key_lo + kMlaStepKeys * t;
       const int valid = key_hi - key0;                 // keys of this step that count (1..32)
@@ -279,9 +310,11 @@ __global__ __launch_bounds__(128) void mla_decode_kernel(const MlaArgs a) {
       }
 
       // ---- swap partial scores with the other wave (same lane = same keys and head) ----
-      float* x_own = (float*)(smem + C::kXchg + w * 2048 + lane * 32);
-      const float* x_other = (const float*)(smem + C::kXchg + (1 - w) * 2048 + lane * 32);
-      lds_barrier();                                   // the other wave has read the previous partials
+      const int xs = C::kXSlots == 2 ? (t & 1) * 4096 : 0;
+      float* x_own = (float*)(smem + C::kXchg + xs + w * 2048 + lane * 32);
+      const float* x_other = (const float*)(smem + C::kXchg + xs + (1 - w) * 2048 + lane * 32);
+      // one slot: the other wave must have read the previous partials
+      if (C::kXSlots == 1) lds_barrier();
       *(f32x4_t*)x_own = s0;
       *(f32x4_t*)(x_own + 4) = s1;
       lds_barrier();
@@ -296,8 +329,7 @@ __global__ __launch_bounds__(128) void mla_decode_kernel(const MlaArgs a) {
         if (16 + 4 * g + r >= valid) s1[r] = -INFINITY;
         mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = xor32_max(xor16_max(mx));
       const bool grow = mx * cs > m_run * cs + kLazyRescale;
       if (__any(grow)) {
         const float m_new = grow ? mx : m_run;
@@ -363,11 +395,11 @@ __global__ __launch_bounds__(128) void mla_decode_kernel(const MlaArgs a) {
           __builtin_amdgcn_sched_barrier(0);
         }
       }
+      st = st + 1 == C::kStages ? 0 : st + 1;
     }
 
     // ---- partial of this segment: wave w writes latent values 256w .. 256w+255 ----
-    float l_tot = l_run + __shfl_xor(l_run, 16);
-    l_tot += __shfl_xor(l_tot, 32);
+    const float l_tot = xor32_sum(xor16_sum(l_run));
     const int64_t slot = (int64_t)head * a.slots + s + unit;
     float* wo = a.ws_o + slot * kMlaLatent + 256 * w;
 #pragma unroll
