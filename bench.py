@@ -69,8 +69,10 @@ def parse():
                    help="after the timed region, copy 1 GiB device to device (a known-size kernel for counter scaling)")
     p.add_argument("--mla-only", action="store_true",
                    help="time only the MLA latent decode batches (prints their JSON object)")
-    p.add_argument("--summarize-profile", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
-                   help="write the traffic summary from rocprofv3 output of this script (no GPU needed)")
+    p.add_argument("--chunk-reps", type=int, default=20, help="repetitions per chunk for the latency distribution")
+    p.add_argument("--summarize-profile", nargs="+", metavar="DIR",
+                   help="TRACE_DIR FETCH_DIR WRITE_DIR [MFMA_DIR]: write the profile summary from rocprofv3 "
+                        "output of this script (no GPU needed)")
     return p.parse_args()
 
 
@@ -108,18 +110,38 @@ def _csv_rows(directory, suffix):
     raise FileNotFoundError(f"no *{suffix} under {directory}")
 
 
-def _counter_per_dispatch(directory, counter):
-    vals, names = {}, {}
+def _counter_per_dispatch(directory, counter, reduce=sum):
+    """Per dispatch: the counter reduced over its instances, the kernel name and the grid size."""
+    parts, names, grids = {}, {}, {}
     for r in _csv_rows(directory, "counter_collection.csv"):
         if r["Counter_Name"] != counter:
             continue
         d = int(r["Dispatch_Id"])
-        vals[d] = vals.get(d, 0.0) + float(r["Counter_Value"])
+        parts.setdefault(d, []).append(float(r["Counter_Value"]))
         names[d] = r["Kernel_Name"]
-    return vals, names
+        grids[d] = int(r["Grid_Size"])
+    return {d: reduce(v) for d, v in parts.items()}, names, grids
 
 
-def summarize_profile(trace_dir, fetch_dir, write_dir):
+def mixed_decode_kv_lens(inputs):
+    w = inputs.WORKLOADS["mixed"]
+    return inputs.context_lengths(w.decode_requests, w.decode_ctx[0], w.decode_ctx[1], w.seed + 7).tolist()
+
+
+def gqa_decode_bytes(kv_lens, heads, kv_heads, d, dv):
+    """Least bytes a GQA decode batch moves: K and V of every cached token once per KV head, plus q and out."""
+    return sum(kv * kv_heads * (d + dv) * 2 for kv in kv_lens) + len(kv_lens) * heads * (d + dv) * 2
+
+
+def mla_decode_read_bytes(inputs, bytes_per_token):
+    """Bytes an MLA decode batch must read: every cached record once, the queries, the block-table entries."""
+    w = inputs.WORKLOADS["mla_decode"]
+    kv = inputs.context_lengths(w.decode_requests, w.decode_ctx[0], w.decode_ctx[1], w.seed)
+    return (int(kv.sum()) * bytes_per_token + w.decode_requests * w.heads * w.head_dim * 2
+            + sum(math.ceil(int(k) / 64) for k in kv) * 4)
+
+
+def summarize_profile(trace_dir, fetch_dir, write_dir, mfma_dir=None):
     """Markdown summary of the bench command's kernel trace and its FETCH_SIZE / WRITE_SIZE passes."""
     stats = _csv_rows(trace_dir, "kernel_stats.csv")
     trace = _csv_rows(trace_dir, "kernel_trace.csv")
@@ -137,11 +159,12 @@ def summarize_profile(trace_dir, fetch_dir, write_dir):
               f"{sum(durs) / len(durs):.4f} ms."]
     out = {"kernel_sha256": kernel_source_hash()}
     for counter, directory in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
-        vals, names = _counter_per_dispatch(directory, counter)
+        vals, names, _ = _counter_per_dispatch(directory, counter)
         calib = [d for d in vals if "copyBuffer" in names[d] or "copy" in names[d].lower()]
         cal = max(calib, key=lambda d: vals[d])
         factor = CALIB_BYTES / (vals[cal] * 1024)
-        dom = sorted(d for d in vals if any(n in names[d] for n in DOMINANT_NAMES))
+        # the counter passes run one step without warmup: its chunk loop is the first 8 launches
+        dom = sorted(d for d in vals if any(n in names[d] for n in DOMINANT_NAMES))[:8]
         per = [vals[d] * 1024 * factor for d in dom]
         out[counter] = {"calibration_kib": vals[cal], "factor": round(factor, 4), "dispatches": len(dom),
                         "bytes_per_launch": sum(per) / len(per), "bytes_by_chunk": [round(x) for x in per]}
@@ -149,8 +172,64 @@ def summarize_profile(trace_dir, fetch_dir, write_dir):
                   f"{vals[cal]:.0f} KiB, so bytes = KiB x 1024 x {factor:.4f}.  Dominant kernel, by launch: "
                   + ", ".join(f"{x / 1e9:.2f} GB" for x in per) + f" (mean {sum(per) / len(per) / 1e9:.3f} GB)."]
     out["bytes_per_launch"] = out["FETCH_SIZE"]["bytes_per_launch"] + out["WRITE_SIZE"]["bytes_per_launch"]
+    lines += decode_fetch_check(fetch_dir, out["FETCH_SIZE"]["factor"])
+    if mfma_dir:
+        lines += mfma_counter_summary(mfma_dir)
     lines += ["", f"<!-- traffic {json.dumps(out)} -->"]
     return "\n".join(lines) + "\n"
+
+
+def decode_fetch_check(fetch_dir, factor):
+    """HBM-side reads of the decode kernels against the byte model (FETCH_SIZE, same calibration)."""
+    sys.path.insert(0, ROOT)
+    from chunked_prefill_causal_amd import inputs
+
+    vals, names, grids = _counter_per_dispatch(fetch_dir, "FETCH_SIZE")
+    w = inputs.WORKLOADS["mixed"]
+    checks = [("decode_kernel<128, 128>", "GQA decode, 256 requests (decode-only batch)",
+               gqa_decode_bytes(mixed_decode_kv_lens(inputs), w.heads, w.kv_heads, w.head_dim, w.head_dim_v)),
+              ("mla_decode_kernel<false>", "MLA decode, bf16 latent cache", mla_decode_read_bytes(inputs, 1152)),
+              ("mla_decode_kernel<true>", "MLA decode, fp8 latent cache", mla_decode_read_bytes(inputs, 656))]
+    lines = ["", "Decode kernels, FETCH_SIZE (same calibration) against the bytes the batch must read:", "",
+             "| Kernel | Batch | Dispatches | Counted GB | Model GB | Counted / model |", "|---|---|---|---|---|---|"]
+    for kname, label, model in checks:
+        ds = [d for d in vals if kname in names[d]]
+        if not ds:
+            continue
+        if kname.startswith("decode_kernel"):     # the decode-only batch: the most frequent grid
+            common = max(set(grids[d] for d in ds), key=lambda g: sum(grids[d] == g for d in ds))
+            ds = [d for d in ds if grids[d] == common]
+        got = sum(vals[d] for d in ds) / len(ds) * 1024 * factor
+        lines.append(f"| `{kname}` | {label} | {len(ds)} | {got / 1e9:.3f} | {model / 1e9:.3f} | {got / model:.3f} |")
+    return lines
+
+
+def mfma_counter_summary(mfma_dir):
+    """Executed bf16 MFMA flops and matrix-pipe busy cycles of the chunk-loop launches (one counter pass)."""
+    sys.path.insert(0, ROOT)
+    from chunked_prefill_causal_amd import inputs
+
+    mops, names, _ = _counter_per_dispatch(mfma_dir, "SQ_INSTS_VALU_MFMA_MOPS_BF16")
+    busy, _, _ = _counter_per_dispatch(mfma_dir, "SQ_VALU_MFMA_BUSY_CYCLES")
+    dur = {}
+    for r in _csv_rows(mfma_dir, "counter_collection.csv"):
+        dur[int(r["Dispatch_Id"])] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+    dom = sorted(d for d in mops if any(n in names[d] for n in DOMINANT_NAMES))[:8]
+    w = inputs.WORKLOADS["gqa_128k"]
+    simds, clock = 1024, 2.4e9
+    lines = ["", "Chunk-loop launches, one pass of SQ_INSTS_VALU_MFMA_MOPS_BF16 and SQ_VALU_MFMA_BUSY_CYCLES. Executed "
+             "flops = MOPS x 512. The busy counter is the matrix-pipe cycles summed over the 1024 SIMDs (32 per "
+             "32x32x16 MFMA); busy % = busy cycles per SIMD / (launch duration under counting x 2.4 GHz), the "
+             "same nominal clock as the 2516.6 TFLOP/s peak.", "",
+             "| Chunk | Executed MFMA TFLOP | Causal-effective TFLOP | Executed / effective | Duration (ms) | "
+             "Busy cycles per SIMD (M) | Busy % at 2.4 GHz |", "|---|---|---|---|---|---|---|"]
+    for k, d in enumerate(dom):
+        eff = w.heads * causal_pairs(k * w.chunk_len, w.chunk_len) * 2 * (w.head_dim + w.head_dim_v)
+        ex = mops[d] * 512
+        per_simd = busy.get(d, 0.0) / simds
+        lines.append(f"| {k} | {ex / 1e12:.2f} | {eff / 1e12:.2f} | {ex / eff:.3f} | {dur[d] * 1e3:.3f} | "
+                     f"{per_simd / 1e6:.2f} | {100 * per_simd / (dur[d] * clock):.1f} |")
+    return lines
 
 
 class PrefillLoop:
@@ -233,7 +312,7 @@ class MixedBatch:
         self.prefill_flops = sum(hq * causal_pairs(p, c) * 2 * (d + dv) for p, c in pref)
         self.decode_flops = sum(hq * kv * 2 * (d + dv) for kv in decs)
         # bytes the decode part must move: K and V of every cached token once per KV head, plus q and out
-        self.decode_bytes = sum(kv * hkv * (d + dv) * 2 for kv in decs) + len(decs) * hq * (d + dv) * 2
+        self.decode_bytes = gqa_decode_bytes(decs, hq, hkv, d, dv)
         self.flops = self.prefill_flops + self.decode_flops
 
     def run(self, L):
@@ -303,6 +382,39 @@ def mla_decode_summary(L, inputs, torch, timed, reps, warmup):
     res["workload"] = ("256 decodes, ctx U[1024,32768], 16 q heads over one shared 576-value latent record per "
                        "token, paged KV (64); decode + split merge, inputs resident in HBM")
     return res
+
+
+def chunk_latency_stats(L, loop, torch, reps):
+    """Each chunk `reps` times (median, p10, p90); then each once cold, after a 512 MiB write evicts the
+    caches."""
+    n = loop.w.n_chunks
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    warm = []
+    for c in range(n):
+        ts = []
+        for _ in range(reps):
+            e0.record()
+            loop.run_chunk(L, c)
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        ts.sort()
+        at = lambda q: ts[min(len(ts) - 1, int(round(q * (len(ts) - 1))))]
+        warm.append((median(ts), at(0.1), at(0.9)))
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    cold = []
+    for c in range(n):
+        flush.fill_(c & 0xFF)
+        torch.cuda.synchronize()
+        e0.record()
+        loop.run_chunk(L, c)
+        e1.record()
+        torch.cuda.synchronize()
+        cold.append(e0.elapsed_time(e1))
+    del flush
+    return {"reps": reps, "median_ms": [round(x[0], 3) for x in warm], "p10_ms": [round(x[1], 3) for x in warm],
+            "p90_ms": [round(x[2], 3) for x in warm], "cold_ms": [round(x, 3) for x in cold],
+            "cold_note": "one call per chunk right after writing a 512 MiB buffer (L2 and MALL evicted)"}
 
 
 def median(xs):
@@ -443,7 +555,11 @@ def cpu_baseline(args, loop, torch):
             cpu_model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), "")
     except OSError:
         pass
-    return {"value": total_flops / total_s / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+    rate = total_flops / total_s
+    return {"value": rate / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "rows": rows, "seconds": round(total_s, 2), "rows_per_s": round(rows / total_s, 1),
+            "fp64_gflops": round(rate / 1e9, 2),
+            "extrapolated_full_chunk_loop_s": round(sum(loop.flops) / rate, 1),
             "sample": f"{args.cpu_rows} seeded (token, head) rows per chunk of the 131072-token prompt, all 8 "
                       f"chunks ({rows} rows, {total_flops:.3e} causal-effective flops in fp64, "
                       f"{total_s:.1f} s); CPU {cpu_model}",
@@ -453,6 +569,8 @@ def cpu_baseline(args, loop, torch):
 def main():
     args = parse()
     if args.summarize_profile:
+        if len(args.summarize_profile) not in (3, 4):
+            sys.exit("--summarize-profile takes TRACE_DIR FETCH_DIR WRITE_DIR [MFMA_DIR]")
         sys.stdout.write(summarize_profile(*args.summarize_profile))
         return
     if args.gpus != 1:
@@ -531,6 +649,8 @@ def main():
     prefill_tflops = sum(loop.flops) / (sum(per_chunk) / 1e3) / 1e12
     log(f"step {ms_per_step:.2f} ms, {value:.1f} TFLOP/s; chunk loop {sum(per_chunk):.2f} ms "
         f"({prefill_tflops:.1f} TFLOP/s); mixed {median(mixed_ms):.3f} ms")
+    log(f"per-chunk latency distribution ({args.chunk_reps} repetitions each) and a cold pass")
+    chunk_stats = chunk_latency_stats(L, loop, torch, args.chunk_reps)
 
     # the two halves of the mixed batch on their own (for the decode HBM roofline)
     dec_ms = timed(lambda: dec_only.run(L), args.reps)
@@ -563,6 +683,7 @@ def main():
     if not args.no_cpu_baseline:
         log("timing the fp64 oracle on a bounded sample")
         cpu = cpu_baseline(args, loop, torch)
+        cpu["gpu_over_cpu_chunk_loop"] = round(prefill_tflops / cpu["value"], 1)
 
     w = loop.w
     traffic, traffic_note = recorded_traffic()
@@ -588,6 +709,7 @@ def main():
             "decode_requests": mixed.w.decode_requests, "step_causal_flops": step_flops,
         },
         "per_chunk_ms": [round(x, 3) for x in per_chunk],
+        "per_chunk_latency": chunk_stats,
         "per_chunk_fit": {"a_ms": round(a, 4), "b_ms_per_chunk": round(b, 4), "r2": round(r2, 5),
                           "b_over_a": round(b / a, 3) if a else None},
         "prefill_chunk_loop": {"ms": round(sum(per_chunk), 3), "tflops": round(prefill_tflops, 1)},
