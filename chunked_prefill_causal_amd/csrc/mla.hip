@@ -112,8 +112,8 @@ struct MlaCfg {
   static constexpr int kStages = FP8 ? 3 : 2;
   static constexpr int kLoads = FP8 ? 8 + 1 + 2 : 16 + 2;     // direct loads per wave per step
   // partial scores: [kXSlots][2 waves][64 lanes][8 fp32].  With two slots (by
-  // step parity) one barrier per step suffices; bf16 keeps one slot and a
-  // second barrier so that two workgroups still fit in a CU's LDS.
+  // step parity) one barrier per step suffices.  bf16 keeps one slot and a
+  // second barrier: its loads bound it, and two slots measured no faster.
   static constexpr int kXSlots = FP8 ? 2 : 1;
   static constexpr int kXchg = kStages * kStage;
   static constexpr int kLds = kXchg + kXSlots * 2 * 64 * 32;

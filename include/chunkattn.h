@@ -325,10 +325,15 @@ size_t chunkattn_mla_decode_workspace_size(const int32_t* kv_lens_host, int32_t 
  *   out  [num_seqs, heads, 512] bf16: the attention output in latent space.
  *   lse_out optional [heads, num_seqs] fp32, natural log of the softmax denominator.
  *   block_tables [num_seqs, max_blocks_per_seq] device; kv_lens on device and host (>= 1).
- *   heads: a positive multiple of 16 (one wave serves 16 heads).
- *   workspace: >= chunkattn_mla_decode_workspace_size bytes, 256-byte aligned (split partials).
+ *   heads: a positive multiple of 16, at most 1024 (a workgroup serves 16 heads).
+ *   num_seqs: 0 .. 65535; the device kv_lens must equal the host ones (the host
+ *        copy sizes the work plan, the device copy drives the kernels).
+ *   workspace: >= chunkattn_mla_decode_workspace_size bytes, 256-byte aligned:
+ *        the work plan (per-sequence step offsets, work-unit starts) and the
+ *        unnormalised partial results, combined in a fixed order (deterministic).
  * Keys past kv_len never reach an output.  CA_OK, CA_EINVAL, CA_EUNSUPPORTED,
- * CA_ERANGE, CA_EWORKSPACE or CA_EHIP; validation precedes any HIP call.
+ * CA_ERANGE (also for a batch of more than 2^31 32-key steps), CA_EWORKSPACE or
+ * CA_EHIP; validation precedes any HIP call.
  */
 ca_status chunk_mla_decode(const void* q, const void* pool, int32_t format, const int32_t* block_tables,
                            int32_t max_blocks_per_seq, int32_t num_blocks, const int32_t* kv_lens_dev,
