@@ -102,7 +102,7 @@ def lib() -> ctypes.CDLL:
     L.chunkattn_mla_decode_workspace_size.restype = sz
     L.chunkattn_mla_kv_append.argtypes = [vp, vp, i64, i64, i32, vp, i32, i32, vp, vp]
     L.chunkattn_mla_kv_append.restype = ctypes.c_int
-    L.chunk_mla_decode.argtypes = [vp, vp, i32, vp, i32, i32, vp, vp, i32, i32, f32, vp, vp, vp, sz, vp]
+    L.chunk_mla_decode.argtypes = [vp, vp, i32, vp, i32, i32, vp, vp, i32, i32, f32, vp, i32, vp, vp, sz, vp]
     L.chunk_mla_decode.restype = ctypes.c_int
     L.chunkattn_last_error.argtypes = []
     L.chunkattn_last_error.restype = ctypes.c_char_p
@@ -373,15 +373,17 @@ def chunkattn_mla_decode_workspace_size(kv_lens, heads: int, fmt: int) -> int:
 
 
 def chunk_mla_decode(q, pool, fmt: int, block_tables, kv_lens, scale: float, *, num_blocks: int | None = None,
-                     out=None, return_lse: bool = False, lse=None, workspace=None, kv_lens_dev=None, stream=None):
+                     out=None, out_dtype=torch.bfloat16, return_lse: bool = False, lse=None, workspace=None,
+                     kv_lens_dev=None, stream=None):
     """Absorbed MLA decode: ``q [num_seqs, heads, 576]`` bf16 against the latent pool; returns
-    ``out [num_seqs, heads, 512]`` bf16 (and ``lse [heads, num_seqs]`` fp32)."""
+    ``out [num_seqs, heads, 512]`` in ``out_dtype`` (bf16 or fp32; that of ``out`` when given) and
+    ``lse [heads, num_seqs]`` fp32."""
     n, heads, _ = q.shape
     kv = _host_i32(kv_lens)
     if kv_lens_dev is None:
         kv_lens_dev = kv.to(q.device)
     if out is None:
-        out = torch.empty((n, heads, MLA_LATENT), dtype=torch.bfloat16, device=q.device)
+        out = torch.empty((n, heads, MLA_LATENT), dtype=out_dtype, device=q.device)
     if return_lse and lse is None:
         lse = torch.empty((heads, n), dtype=torch.float32, device=q.device)
     if workspace is None:
@@ -390,5 +392,6 @@ def chunk_mla_decode(q, pool, fmt: int, block_tables, kv_lens, scale: float, *, 
     _check(lib().chunk_mla_decode(
         _ptr(q), _ptr(pool), fmt, _ptr(block_tables), block_tables.shape[1],
         pool.shape[0] if num_blocks is None else num_blocks, _ptr(kv_lens_dev), kv.data_ptr(), n, heads,
-        float(scale), _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(), _stream(stream)))
+        float(scale), _ptr(out), _dtype_code(out.dtype), _ptr(lse), _ptr(workspace), workspace.numel(),
+        _stream(stream)))
     return (out, lse) if return_lse else out

@@ -493,8 +493,9 @@ ca_status chunkattn_mla_kv_append(const void* latent, const void* rope, int64_t 
 ca_status chunk_mla_decode(const void* q, const void* pool, int32_t format, const int32_t* block_tables,
                            int32_t max_blocks, int32_t num_blocks, const int32_t* kv_lens_dev,
                            const int32_t* kv_lens_host, int32_t num_seqs, int32_t heads, float scale, void* out,
-                           float* lse_out, void* workspace, size_t workspace_bytes, void* stream) {
+                           int32_t out_dtype, float* lse_out, void* workspace, size_t workspace_bytes, void* stream) {
   if (max_blocks <= 0 || num_blocks <= 0) return fail(CA_EINVAL, "max_blocks and num_blocks must be > 0");
+  if (out_dtype != CA_BF16 && out_dtype != CA_F32) return fail(CA_EINVAL, "out_dtype must be CA_BF16 or CA_F32");
   if (ca_status st = check_mla(kv_lens_host, num_seqs, heads, max_blocks, format)) return st;
   if (!(scale > 0.f) || !std::isfinite(scale)) return fail(CA_EINVAL, "scale must be finite and > 0");
   if (num_seqs == 0) return ok();
@@ -518,7 +519,8 @@ ca_status chunk_mla_decode(const void* q, const void* pool, int32_t format, cons
   a.unit_seq = (int32_t*)((char*)workspace + p.unit_off);
   a.ws_ml = (float*)((char*)workspace + p.ml_off);
   a.ws_o = (float*)((char*)workspace + p.o_off);
-  a.out = (uint16_t*)out;
+  a.out = out;
+  a.out_f32 = out_dtype == CA_F32 ? 1 : 0;
   a.lse = lse_out;
   a.num_seqs = num_seqs;
   a.max_blocks = max_blocks;

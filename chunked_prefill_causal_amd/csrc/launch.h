@@ -108,9 +108,10 @@ struct MlaArgs {
   int32_t* unit_seq;             // [units] sequence holding each unit's first step (plan kernel output)
   float* ws_o;                   // [heads][slots][512] unnormalised partials
   float* ws_ml;                  // [heads][slots][2]: max (log2 units) and sum
-  uint16_t* out;                 // [num_seqs, heads, 512] bf16
+  void* out;                     // [num_seqs, heads, 512] bf16 or fp32
   float* lse;                    // [heads, num_seqs] or null
   int32_t num_seqs, max_blocks, num_blocks, heads, units, slots;
+  int32_t out_f32;               // 1: fp32 output, 0: bf16
   float scale_log2;
 };
 

@@ -440,7 +440,7 @@ __global__ __launch_bounds__(1024) void mla_plan_kernel(const MlaArgs a) {
 }
 
 // One workgroup per (sequence, head): combine the sequence's segment partials
-// in unit order, normalise, store bf16 and the LSE.
+// in unit order, normalise, store bf16 (RNE) or fp32 and the LSE.
 __global__ __launch_bounds__(128) void mla_merge_kernel(const MlaArgs a) {
   const int s = blockIdx.x / a.heads, h = blockIdx.x % a.heads;
   const int64_t total = a.seq_steps[a.num_seqs];
@@ -459,8 +459,9 @@ __global__ __launch_bounds__(128) void mla_merge_kernel(const MlaArgs a) {
     acc += *(const f32x4_t*)(a.ws_o + (slot0 + i) * kMlaLatent + 4 * t) * fast_exp2(m - M);
   }
   acc *= 1.f / L;
-  uint16_t* orow = a.out + ((int64_t)s * a.heads + h) * kMlaLatent + 4 * t;
-  *(u32x2_t*)orow = u32x2_t{pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3])};
+  const int64_t o_off = ((int64_t)s * a.heads + h) * kMlaLatent + 4 * t;
+  if (a.out_f32) *(f32x4_t*)((float*)a.out + o_off) = acc;
+  else *(u32x2_t*)((uint16_t*)a.out + o_off) = u32x2_t{pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3])};
   if (a.lse && t == 0) a.lse[(int64_t)h * a.num_seqs + s] = (M + __log2f(L)) * kLn2;
 }
 

@@ -322,7 +322,8 @@ size_t chunkattn_mla_decode_workspace_size(const int32_t* kv_lens_host, int32_t 
  * reads the entire cache).
  *   q    [num_seqs, heads, 576] bf16: per head, the latent-space projection of
  *        the no-rope query (512) then its rotary part (64).
- *   out  [num_seqs, heads, 512] bf16: the attention output in latent space.
+ *   out  [num_seqs, heads, 512] in out_dtype (CA_BF16, rounded to nearest even, or
+ *        CA_F32): the attention output in latent space.
  *   lse_out optional [heads, num_seqs] fp32, natural log of the softmax denominator.
  *   block_tables [num_seqs, max_blocks_per_seq] device; kv_lens on device and host (>= 1).
  *   heads: a positive multiple of 16, at most 1024 (a workgroup serves 16 heads).
@@ -338,7 +339,7 @@ size_t chunkattn_mla_decode_workspace_size(const int32_t* kv_lens_host, int32_t 
 ca_status chunk_mla_decode(const void* q, const void* pool, int32_t format, const int32_t* block_tables,
                            int32_t max_blocks_per_seq, int32_t num_blocks, const int32_t* kv_lens_dev,
                            const int32_t* kv_lens_host, int32_t num_seqs, int32_t heads, float scale, void* out,
-                           float* lse_out, void* workspace, size_t workspace_bytes, void* stream);
+                           int32_t out_dtype, float* lse_out, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* chunkattn_last_error(void);

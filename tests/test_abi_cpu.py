@@ -162,10 +162,10 @@ def test_mla_block_bytes_follow_the_per_token_record():
 
 
 def mla_decode(q=FAKE, fmt=L.CA_MLA_BF16, kv=(10, 300), heads=16, max_blocks=8, num_blocks=8, scale=0.1,
-               out=FAKE, ws=FAKE, ws_bytes=1 << 30, lse=None):
+               out=FAKE, out_dtype=L.CA_BF16, ws=FAKE, ws_bytes=1 << 30, lse=None):
     kv_a = (ctypes.c_int32 * len(kv))(*kv)
     return L.lib().chunk_mla_decode(q, FAKE, fmt, FAKE, max_blocks, num_blocks, FAKE, ctypes.addressof(kv_a),
-                                    len(kv), heads, scale, out, lse, ws, ws_bytes, None)
+                                    len(kv), heads, scale, out, out_dtype, lse, ws, ws_bytes, None)
 
 
 @pytest.mark.parametrize("kwargs,status", [
@@ -184,6 +184,7 @@ def mla_decode(q=FAKE, fmt=L.CA_MLA_BF16, kv=(10, 300), heads=16, max_blocks=8, 
     (dict(ws=FAKE + 16), L.CA_EINVAL),
     (dict(max_blocks=0), L.CA_EINVAL),
     (dict(num_blocks=0), L.CA_EINVAL),
+    (dict(out_dtype=5), L.CA_EINVAL),
 ])
 def test_mla_decode_rejections(kwargs, status):
     assert mla_decode(**kwargs) == status

@@ -157,20 +157,36 @@ def build_batch(fmt, kv_lens, heads, seed):
     return pool, torch.from_numpy(tables).cuda(), q, seqs
 
 
-def check_decode(fmt, kv_lens, heads, seed, sample=None):
+def bf16_half_ulp(x) -> np.ndarray:
+    """Half the bf16 spacing at |x|: the most one round-to-nearest-even store can change x."""
+    e = np.floor(np.log2(np.maximum(np.abs(np.asarray(x, dtype=np.float64)), 2.0 ** -126)))
+    return 2.0 ** (e - 8)
+
+
+def check_decode(fmt, kv_lens, heads, seed, sample=None, out_dtype=torch.bfloat16):
+    """Every output against the oracle: fp32 output within the bar; bf16 output within the bar plus what its
+    one rounding store may add (half a bf16 spacing, up to 0.0156 for |o| in [4, 8))."""
     pool, tables, q, seqs = build_batch(fmt, kv_lens, heads, seed)
-    log(f"mla decode fmt={fmt} heads={heads} kv={list(kv_lens)[:12]} seed={seed}")
-    out, lse = L.chunk_mla_decode(q.cuda(), pool, FMTS[fmt], tables, kv_lens, SCALE, return_lse=True)
+    log(f"mla decode fmt={fmt} heads={heads} out={out_dtype} kv={list(kv_lens)[:12]} n={len(kv_lens)} seed={seed}")
+    out, lse = L.chunk_mla_decode(q.cuda(), pool, FMTS[fmt], tables, kv_lens, SCALE, return_lse=True,
+                                  out_dtype=out_dtype)
     torch.cuda.synchronize()
-    out, lse = out.cpu(), lse.cpu()
+    out, lse = out.float().cpu().numpy().astype(np.float64), lse.cpu()
+    assert np.all(np.isfinite(out)), "non-finite GPU output"
     qb = bits(q)
-    worst = worst_lse = 0.0
+    worst = worst_excess = worst_lse = 0.0
     for s in (range(len(kv_lens)) if sample is None else sample):
         ref, ref_lse = mla.decode(qb[s], mla.records(*seqs[s], fmt), SCALE)
-        worst = max(worst, max_err(out[s], ref))
+        err = np.abs(out[s] - ref)
+        # the pre-store value rounds to out within its own binade, which |ref| or |out| bounds from above
+        store = bf16_half_ulp(np.maximum(np.abs(ref), np.abs(out[s]))) if out_dtype == torch.bfloat16 else 0.0
+        worst = max(worst, float(err.max()))
+        worst_excess = max(worst_excess, float((err - store).max()))
         worst_lse = max(worst_lse, max_err(lse[:, s], ref_lse))
-    log(f"  max abs err {worst:.3e}  lse {worst_lse:.3e}")
-    assert worst <= BF16_TOL and worst_lse <= LSE_TOL
+    log(f"  max abs err {worst:.3e} (beyond the store's rounding {worst_excess:.3e})  lse {worst_lse:.3e}")
+    assert worst_excess <= BF16_TOL and worst_lse <= LSE_TOL
+    if out_dtype == torch.float32:
+        assert worst <= BF16_TOL
 
 
 @pytest.mark.parametrize("fmt", ["bf16", "fp8"])
@@ -189,6 +205,19 @@ def test_decode_more_heads(fmt, heads):
 def test_decode_many_splits(fmt):
     # one long context among short ones: the plan gives it many splits
     check_decode(fmt, [40000, 5, 70, 300], 16, 300)
+
+
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32], ids=["bf16out", "f32out"])
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_decode_thousands_of_short_sequences(fmt, out_dtype):
+    # 3000 sequences: the plan kernel's threads each own several sequences, and
+    # a work unit spans many short sequences (one partial per segment).  Short
+    # contexts give outputs up to |o| ~ 5, where one bf16 store alone may err
+    # by 0.0156: fp32 output shows the kernel itself within the bar.
+    rng = np.random.default_rng(500)
+    kv = rng.integers(1, 200, size=3000).tolist()
+    kv[0], kv[1], kv[-1] = 1, 33, 64
+    check_decode(fmt, kv, 16, 500, out_dtype=out_dtype)
 
 
 def test_decode_rejects_unsupported_heads_on_device():
