@@ -202,6 +202,12 @@ def test_decode_more_heads(fmt, heads):
 
 
 @pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_decode_most_heads(fmt):
+    # 1024 heads = 64 head blocks: the plan keeps its minimum of 8 units per head block
+    check_decode(fmt, [1, 77, 300], 1024, 250)
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
 def test_decode_many_splits(fmt):
     # one long context among short ones: the plan gives it many splits
     check_decode(fmt, [40000, 5, 70, 300], 16, 300)
