@@ -120,23 +120,34 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeArgs a) {
   for (int b = 0; b < NB; ++b) o[b] = f32x16_t{};
   float m_run = -INFINITY, l_run = 0.f;
 
-  for (int j = key_lo / kBlock; j * kBlock < key_hi; ++j) {
+  // K and V of a tile each have one register set.  K of tile j+1 is requested as
+  // soon as QK of tile j has consumed K, V of tile j+1 as soon as PV of tile j
+  // has consumed V, so a tile's worth of loads is in flight while the wave
+  // computes (one wave per SIMD fits these registers).
+  u32x4_t ka[2][NQ];
+  u32x4_t va[4][NB];
+  auto load_k = [&](int j) {
     const int64_t tile = (int64_t)clamp_block(bt[j], a.num_blocks) * a.kv_heads + g;
     const uint16_t* kt = (const uint16_t*)a.k + tile * (D * kBlock);
-    const uint16_t* vt = (const uint16_t*)a.v + tile * (DV * kBlock);
-    u32x4_t ka[2][NQ];
 #pragma unroll
     for (int kb2 = 0; kb2 < 2; ++kb2) {
       const int krow = 32 * kb2 + dec_key_of_row(col);
 #pragma unroll
       for (int k = 0; k < NQ; ++k) ka[kb2][k] = *(const u32x4_t*)(kt + ((2 * k + hl) * kBlock + krow) * 8);
     }
-    u32x4_t va[4][NB];
+  };
+  auto load_v = [&](int j) {
+    const int64_t tile = (int64_t)clamp_block(bt[j], a.num_blocks) * a.kv_heads + g;
+    const uint16_t* vt = (const uint16_t*)a.v + tile * (DV * kBlock);
 #pragma unroll
     for (int st = 0; st < 4; ++st)
 #pragma unroll
       for (int b = 0; b < NB; ++b) va[st][b] = *(const u32x4_t*)(vt + ((2 * st + hl) * DV + 32 * b + col) * 8);
-
+  };
+  const int j_first = key_lo / kBlock, j_end = (key_hi + kBlock - 1) / kBlock;
+  load_k(j_first);
+  load_v(j_first);
+  for (int j = j_first; j < j_end; ++j) {
     f32x16_t sc[2];
 #pragma unroll
     for (int kb2 = 0; kb2 < 2; ++kb2) {
@@ -144,6 +155,7 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeArgs a) {
 #pragma unroll
       for (int k = 0; k < NQ; ++k) sc[kb2] = mfma_bf16(ka[kb2][k], qreg[k], sc[kb2]);
     }
+    if (j + 1 < j_end) load_k(j + 1);
     const int key0 = j * kBlock;
     if (key0 + kBlock - 1 > first_pos) {
 #pragma unroll
@@ -151,15 +163,6 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r)
           if (key0 + dec_key_of_reg(kb2, r, hl) > pos) sc[kb2][r] = -INFINITY;
-    }
-    if (key0 + kBlock > kvl) {   // values past the sequence end are zeroed (0 * NaN guard)
-#pragma unroll
-      for (int st = 0; st < 4; ++st)
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (key0 + 16 * st + 8 * hl + e >= kvl)
-#pragma unroll
-            for (int b = 0; b < NB; ++b) va[st][b][e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
     }
     float mx = sc[0][0];
 #pragma unroll
@@ -191,6 +194,15 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeArgs a) {
         pk[kb2 * 8 + rr] = pack_bf16(p0, p1);
       }
     l_run += psum;
+    if (key0 + kBlock > kvl) {   // values past the sequence end are zeroed (0 * NaN guard)
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (key0 + 16 * st + 8 * hl + e >= kvl)
+#pragma unroll
+            for (int b = 0; b < NB; ++b) va[st][b][e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
+    }
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
       const int base = (st >> 1) * 8 + 4 * (st & 1);
@@ -198,6 +210,7 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeArgs a) {
 #pragma unroll
       for (int b = 0; b < NB; ++b) o[b] = mfma_bf16(va[st][b], pb, o[b]);
     }
+    if (j + 1 < j_end) load_v(j + 1);
   }
 
   const float l_tot = half_sum(l_run);
