@@ -147,6 +147,43 @@ def test_split_kv_vs_oracle(splits):
     assert e <= BF16_TOL and el <= LSE_TOL
 
 
+SPLIT_CASES = [
+    # (chunk_len, past_len, heads, kv_heads, d, dv, layout, dtype, out_dtype, splits)
+    (33, 3000, 16, 16, 64, 64, "paged", "bf16", "bf16", 3),
+    (80, 2100, 8, 4, 192, 128, "paged", "bf16", "bf16", 2),
+    (50, 1500, 6, 2, 192, 128, "contiguous", "bf16", "bf16", 4),
+    (100, 2500, 16, 4, 128, 128, "paged", "bf16", "f32", 5),
+    (40, 1200, 8, 8, 64, 64, "contiguous", "f32", "f32", 3),
+]
+
+
+@pytest.mark.parametrize("c,past,hq,hkv,d,dv,layout,dtype,odtype,splits", SPLIT_CASES)
+def test_split_kv_dims_layouts_dtypes(c, past, hq, hkv, d, dv, layout, dtype, odtype, splits):
+    """Forced key splits for every head-dim pair, both cache layouts and every dtype pair."""
+    seed = 3000 + c + d + splits
+    n = past + c
+    k, v = seq_kv(n, hkv, d, dv, dtype, seed)
+    q = inputs.normal((c, hq, d), seed + 1, dtype)
+    scale = 1.0 / math.sqrt(d)
+    log(f"split case c={c} past={past} heads={hq}/{hkv} d={d}/{dv} {layout} {dtype}->{odtype} splits={splits}")
+    kw = dict(return_lse=True, num_splits=splits, out_dtype=torch_dtype(odtype))
+    if layout == "paged":
+        pool, table = single_seq_pool(k, v, seed + 2)
+        out, lse = L.chunk_prefill_attn(q.cuda(), pool.k, pool.v, past, scale, kv_layout="paged",
+                                        block_table=table, **kw)
+    else:
+        cap = n + 9   # capacity beyond kv_len holds NaN that must never be read
+        kc = torch.full((cap, hkv, d), float("nan"), dtype=torch_dtype(dtype))
+        vc = torch.full((cap, hkv, dv), float("nan"), dtype=torch_dtype(dtype))
+        kc[:n], vc[:n] = k, v
+        out, lse = L.chunk_prefill_attn(q.cuda(), kc.cuda(), vc.cuda(), past, scale, **kw)
+    ref, ref_lse = oracle_chunk(q, k, v, past, scale)
+    e, el = max_err(out, ref), max_err(lse, ref_lse)
+    log(f"  max err {e:.3e}  lse err {el:.2e}")
+    assert out.dtype == torch_dtype(odtype)
+    assert e <= (F32_TOL if dtype == "f32" else BF16_TOL) and el <= LSE_TOL
+
+
 # ------------------------------------------------------------- invariants ----
 
 def _paged_run(q, pool, table, past, d, **kw):

@@ -76,6 +76,14 @@ def test_decode_only_ragged_contexts():
     check_batch([1] * 24, kv, 32, 8, 128, 128, 5100)
 
 
+def test_decode_contexts_at_tile_and_split_edges():
+    """Contexts at, one below and one above 64-key tiles and 256-key splits (the split length
+    a small batch gets), so a split may hold a single key or end exactly on a tile."""
+    kv = [1, 63, 64, 65, 127, 128, 255, 256, 257, 511, 512, 513, 768, 769, 1023, 1024]
+    check_batch([1] * len(kv), kv, 32, 8, 128, 128, 5150)
+    check_batch([1] * len(kv), kv, 16, 16, 64, 64, 5160)
+
+
 def test_short_multi_token_rows_take_decode_path():
     """q_len * group <= 32 rides the split-KV path with a causal mask inside the group."""
     check_batch([2, 8, 3, 40], [900, 2100, 3, 600], 16, 4, 128, 128, 5200)
