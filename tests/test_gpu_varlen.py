@@ -104,3 +104,21 @@ def test_lse_and_out_rows_untouched_outside_batch_rows():
     out = torch.full((4, 8, 128), 7.0, dtype=torch.bfloat16, device="cuda")
     L.chunk_attn_varlen(q_all.cuda(), pool.k, pool.v, tables, cu, [100, 200], 0.1, out=out[:2])
     assert torch.all(out[2:] == 7.0)
+
+
+@pytest.mark.parametrize("seed", [7001, 7002, 7003, 7004])
+def test_random_mixed_batches(seed):
+    """Seeded random batches: 4-12 sequences mixing prefill chunks (q_len up to 300) with decode
+    requests (q_len 1-4), contexts 1..4000 with q_len <= kv_len, a random GQA ratio and head-dim pair."""
+    rng = np.random.default_rng(seed)
+    hq, hkv = [(32, 8), (16, 16), (8, 1), (12, 4)][seed % 4]
+    d, dv = [(128, 128), (64, 64), (192, 128), (128, 128)][(seed // 2) % 4]
+    n = int(rng.integers(4, 13))
+    q_lens, kv_lens = [], []
+    for _ in range(n):
+        kv = int(rng.integers(1, 4001))
+        q = int(rng.integers(1, 5)) if rng.random() < 0.6 else int(rng.integers(5, 301))
+        q_lens.append(min(q, kv))
+        kv_lens.append(kv)
+    log(f"random batch seed {seed}: heads {hq}/{hkv}, d {d}/{dv}, q_lens {q_lens}, kv_lens {kv_lens}")
+    check_batch(q_lens, kv_lens, hq, hkv, d, dv, seed)
