@@ -218,8 +218,8 @@ def mfma_counter_summary(mfma_dir):
     w = inputs.WORKLOADS["gqa_128k"]
     simds, clock = 1024, 2.4e9
     lines = ["", "Chunk-loop launches, one pass of SQ_INSTS_VALU_MFMA_MOPS_BF16 and SQ_VALU_MFMA_BUSY_CYCLES. Executed "
-             "flops = MOPS x 512. The busy counter is the matrix-pipe cycles summed over the 1024 SIMDs (32 per "
-             "32x32x16 MFMA); busy % = busy cycles per SIMD / (launch duration under counting x 2.4 GHz), the "
+             "flops = MOPS x 512. The busy counter is the matrix-pipe cycles summed over the 1024 SIMDs (16 per "
+             "16x16x32 bf16 MFMA); busy % = busy cycles per SIMD / (launch duration under counting x 2.4 GHz), the "
              "same nominal clock as the 2516.6 TFLOP/s peak.", "",
              "| Chunk | Executed MFMA TFLOP | Causal-effective TFLOP | Executed / effective | Duration (ms) | "
              "Busy cycles per SIMD (M) | Busy % at 2.4 GHz |", "|---|---|---|---|---|---|---|"]

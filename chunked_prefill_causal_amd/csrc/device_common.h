@@ -6,6 +6,9 @@
 //    D[8*(r/4) + 4*(l/32) + r%4][l%32].
 //  * v_mfma_f32_32x32x2_f32: lane l supplies A[l%32][l/32] and B[l/32][l%32];
 //    same accumulator map.
+//  * v_mfma_f32_16x16x32_bf16: lane l supplies A[l%16][8*(l/16) + i] and
+//    B[8*(l/16) + i][l%16]; accumulator register r of lane l is
+//    D[4*(l/16) + r][l%16].
 // Only the pairing of A and B slots matters for a contraction, so each kernel
 // is free to choose which key or feature a slot stands for, as long as both
 // operands agree.
@@ -73,15 +76,6 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_floa
 __device__ __forceinline__ int clamp_block(int32_t id, int32_t num_blocks) {
   return id < 0 ? 0 : (id >= num_blocks ? num_blocks - 1 : id);
 }
-
-// Accumulator row m of a 32-key half of an S^T = K Q^T tile stands for key
-// key_of_row(m): quads 4..7 and 8..11 of every 16 are swapped.  Then the bf16
-// P fragment a lane holds (registers 8s..8s+7 of the accumulator, keys
-// 16s + 8*(lane/32) + 0..7) is exactly the B operand of O^T = V^T P^T over 8
-// consecutive keys, read with one 16-byte load of the V tile.
-__device__ __forceinline__ int bf16_key_of_row(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
-// Key offset inside a 64-key tile of accumulator register r of half kb2 (bf16 layout).
-__device__ __forceinline__ int bf16_key_of_reg(int kb2, int r, int hl) { return 32 * kb2 + 16 * (r >> 3) + 8 * hl + (r & 7); }
 
 // Row merge of split partials stored in log2 units: ml = {m*log2e*scale, l}.
 // Partials whose m is -inf (no visible key) carry no weight and their O is

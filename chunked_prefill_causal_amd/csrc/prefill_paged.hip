@@ -10,7 +10,7 @@
 //  * Tiles move HBM/L2 -> LDS by direct-to-LDS loads (global_load_lds_dwordx4):
 //    no staging registers, no LDS write instructions.  Four LDS stages (three
 //    at d = 192) give each load two tile-times to land; one barrier per tile.
-//    Only the four leading waves issue them, one load after every fourth MFMA
+//    Only the four leading waves issue them, one load after every eighth MFMA
 //    of their matrix phase.  Measured on MI355X, the direct-to-LDS path drains
 //    ~40 B/clk per CU, so a tile issued as a burst holds the issuing wave at
 //    issue for several hundred cycles; that delayed the leading waves' matrix
@@ -22,11 +22,27 @@
 //    operations are these loads (block-table entries come through the scalar
 //    unit, one tile ahead), so "s_waitcnt vmcnt(N)" with N = loads of the
 //    newer tile is exact (the trailing waves have none outstanding and pass).
-//  * The per-wave matrix work is the same as prefill_kernel's: S^T = K Q^T
-//    and O^T = V^T P^T on v_mfma_f32_32x32x16_bf16, one query row per lane
-//    pair, rescale skipped when no row's maximum grew.  The two waves that
-//    share a SIMD run the same tiles half an interval apart (ping-pong), so
-//    one feeds the matrix cores while the other computes its softmax.
+//  * Per wave, S^T = K Q^T and O^T = V^T P^T run on v_mfma_f32_16x16x32_bf16:
+//    the wave's 32 query rows are two 16-row blocks, and every 1 KiB K or V
+//    operand read from LDS feeds one MFMA per block, so LDS bytes per flop
+//    are those of v_mfma_f32_32x32x16_bf16.  On random bf16 data the chip is
+//    power-bound; measured on MI355X, this loop holds a ~17% higher shader
+//    clock with the 16x16x32 shape than with 32x32x16 but needs more issue
+//    cycles (twice the MFMA instructions, 4-lane row reductions).  With the
+//    softmax kept to the minimum of vector ops it comes out 2-3% faster.
+//    A lane holds query 16*blk + lane%16 and, in lane group g = lane/16, keys
+//    8g..8g+7 of every 32-key step: the K tile's LDS slots are ordered by the
+//    loads themselves (key_of_slot) so that the accumulator registers of two
+//    QK blocks are exactly the bf16 P^T operand of the PV step over those 8
+//    keys, which one 16-byte read of the V tile matches.  Row maxima and sums
+//    combine the 4 lanes of a query with v_permlane16/32_swap.
+//  * Per row the softmax keeps, beside the running max m, the exp offset
+//    -m*scale and the threshold a new max must pass (lazy rescale); both
+//    change only when m does, so a tile costs one fma + exp per logit, the
+//    max3 chains, the pack to bf16 and the fp32 sum.
+//  * The two waves that share a SIMD run the same tiles half an interval
+//    apart (ping-pong), so one feeds the matrix cores while the other
+//    computes its softmax; the rescale is skipped when no row's maximum grew.
 //  * Values of keys past the sequence end are zeroed in LDS once the tile
 //    holding the sequence end has landed, logits past a row's position are
 //    masked with a select, so NaN in unused pool slots never reaches an output.
@@ -46,18 +62,23 @@ struct PagedCfg {
   static constexpr int KPT = KBytes / 16 / kLoaders;   // direct loads per loading thread per tile
   static constexpr int VPT = VBytes / 16 / kLoaders;
   static constexpr int LPT = KPT + VPT;
-  static constexpr int NQ = D / 16;
-  static constexpr int NB = DV / 32;
+  static constexpr int QS = D / 32;                    // 32-feature steps of QK
+  static constexpr int NDB = DV / 16;                  // 16-value blocks of O
+  static constexpr int KF = 4 * QS;                    // K operands per tile: 4 key blocks x QS
+  static constexpr int VF = 2 * NDB;                   // V operands per tile: 2 key steps x NDB
   static_assert(KBytes % (16 * kLoaders) == 0 && VBytes % (16 * kLoaders) == 0, "tile split");
+  static_assert(VF <= KF, "PV operands interleave with QK operands");
 };
 
 __device__ __forceinline__ uint32_t lds_address(const void* p) {
   return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) void*)p);
 }
 
-// 16 bytes per lane from global memory straight into LDS at m0 + 16 * lane.
-__device__ __forceinline__ void load_to_lds16(const void* g, uint32_t lds_wave_base) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_wave_base), "v"(g) : "memory", "m0");
+// 16 bytes per lane from global memory (uniform base + this lane's 32-bit
+// offset) straight into LDS at m0 + 16 * lane.
+__device__ __forceinline__ void load_to_lds16(const void* base, uint32_t lane_off, uint32_t lds_wave_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_wave_base), "v"(lane_off), "s"(base)
+               : "memory", "m0");
 }
 
 template <int N>
@@ -69,6 +90,53 @@ __device__ __forceinline__ void workgroup_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+__device__ __forceinline__ f32x4_t mfma16(u32x4_t a, u32x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
+                                                 0, 0, 0);
+}
+
+// Combine x over the four lanes l, l^16, l^32, l^48 that hold one query row.
+__device__ __forceinline__ float max_raw(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ float max3_raw(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+// Row maxima of both query blocks at once: x0, x1 are this lane's partial
+// maxima of blocks 0 and 1.  permlane16_swap(x0, x1) hands lane group g the
+// pair (x0 of group g&~1, x1 of group g&~1) or its odd partners, so one max
+// leaves group 0 / 2 with block 0 over groups {0,1} / {2,3} and group 1 / 3
+// with block 1; permlane32_swap folds the two halves, and a last
+// permlane16_swap gives every lane both totals.
+__device__ __forceinline__ void quad_max2(float& x0, float& x1) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x0), __float_as_uint(x1), false, false);
+  const float c = max_raw(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  const auto u = __builtin_amdgcn_permlane32_swap(__float_as_uint(c), __float_as_uint(c), false, false);
+  const float d = max_raw(__uint_as_float(u[0]), __uint_as_float(u[1]));
+  const auto v = __builtin_amdgcn_permlane16_swap(__float_as_uint(d), __float_as_uint(d), false, false);
+  x0 = __uint_as_float(v[0]);
+  x1 = __uint_as_float(v[1]);
+}
+__device__ __forceinline__ float quad_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return half_sum(__uint_as_float(r[0]) + __uint_as_float(r[1]));
+}
+
+// LDS slot s of a 64-key K chunk holds key key_of_slot(s).  Slot 16b + m is
+// row m of QK key block b, which stands for key 32(b>>1) + 8(m>>2) + 4(b&1) + (m&3):
+// lane group g then finds keys 8g..8g+3 of a 32-key step in block 2*step and
+// keys 8g+4..8g+7 in block 2*step+1.
+__device__ __forceinline__ int key_of_slot(int s) {
+  const int b = s >> 4, m = s & 15;
+  return 32 * (b >> 1) + 8 * (m >> 2) + 4 * (b & 1) + (m & 3);
+}
+// Key offset (before the lane group's 8g) of register r of QK block b.
+__host__ __device__ constexpr int key_of_reg(int b, int r) { return 32 * (b >> 1) + 4 * (b & 1) + r; }
+
 template <typename EO, int D, int DV, bool kVarlen>
 __global__ __launch_bounds__(512, 1) void prefill_paged_kernel(const PrefillArgs a) {
   using C = PagedCfg<D, DV>;
@@ -77,8 +145,8 @@ __global__ __launch_bounds__(512, 1) void prefill_paged_kernel(const PrefillArgs
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int hl = lane >> 5, col = lane & 31;
-  const int hpw = a.hpw;                 // heads per workgroup: 8, 4, 2 or 1
+  const int lg = lane >> 4, lc = lane & 15;   // lane group (8-key run / 8-feature run), query column
+  const int hpw = a.hpw;                      // heads per workgroup: 8, 4, 2 or 1
   const int tok_wg = 256 / hpw;
 
   // ---- which (sequence, token block, head group, split) this workgroup owns --
@@ -133,100 +201,133 @@ __global__ __launch_bounds__(512, 1) void prefill_paged_kernel(const PrefillArgs
   const int j_lo = split * tps;
   const int j_hi = min(n_tiles, j_lo + tps);
 
-  const int64_t t = t0 + col;
-  const bool row_valid = t < c;
-  const int64_t t_c = row_valid ? t : c - 1;
-  const int64_t pos = P + t_c;
+  // This lane's two query rows, one per 16-row block.
+  int64_t t[2], pos[2];
+  bool row_valid[2];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    t[qb] = t0 + 16 * qb + lc;
+    row_valid[qb] = t[qb] < c;
+    pos[qb] = P + (row_valid[qb] ? t[qb] : c - 1);
+  }
   const int64_t wave_first_pos = P + min(t0, c - 1);
   const float cs = a.scale_log2;
 
   if (j_lo >= j_hi) {
-    if (row_valid && hl == 0) {
-      const int64_t row = t * a.heads + h;
-      *(float2*)(a.ws_ml + ((int64_t)split * c * a.heads + row) * 2) = make_float2(-INFINITY, 0.f);
-    }
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+      if (row_valid[qb] && lg == 0) {
+        const int64_t row = t[qb] * a.heads + h;
+        *(float2*)(a.ws_ml + ((int64_t)split * c * a.heads + row) * 2) = make_float2(-INFINITY, 0.f);
+      }
     return;
   }
 
-  // Query row of this lane as B operands, held for the whole key loop.
-  u32x4_t qreg[C::NQ];
-  {
-    const uint16_t* qrow = qbase + (t_c * a.heads + h) * (int64_t)D;
+  // Query rows of this lane as B operands (features 32i + 8lg .. +7), held for the whole key loop.
+  u32x4_t qreg[2][C::QS];
 #pragma unroll
-    for (int i = 0; i < C::NQ; ++i) qreg[i] = *(const u32x4_t*)(qrow + 16 * i + 8 * hl);
+  for (int qb = 0; qb < 2; ++qb) {
+    const uint16_t* qrow = qbase + ((pos[qb] - P) * a.heads + h) * (int64_t)D + 8 * lg;
+#pragma unroll
+    for (int i = 0; i < C::QS; ++i) qreg[qb][i] = *(const u32x4_t*)(qrow + 32 * i);
   }
 
   // ---- tile transfer: block table through the scalar unit, data straight into LDS ----
-  const __attribute__((address_space(4))) int32_t* bt4 = (const __attribute__((address_space(4))) int32_t*)btab;
-  const unsigned char* kpool = (const unsigned char*)a.k;
-  const unsigned char* vpool = (const unsigned char*)a.v;
+  // A K load instruction covers one 8-feature chunk of all 64 keys; lane s
+  // fetches key key_of_slot(s) into slot s.  V keeps the pool's order.
+  // Loop-local bases (this split's first block-table entry, this KV head's
+  // first tile), so the key loop holds none of the argument block.
+  const __attribute__((address_space(4))) int32_t* bt4 = (const __attribute__((address_space(4))) int32_t*)(btab + j_lo);
+  const unsigned char* kpool = (const unsigned char*)a.k + (int64_t)g * C::KBytes;
+  const unsigned char* vpool = (const unsigned char*)a.v + (int64_t)g * C::VBytes;
+  const int64_t kstride = (int64_t)a.kv_heads * C::KBytes, vstride = (int64_t)a.kv_heads * C::VBytes;
   const uint32_t smem_base = lds_address(smem);
+  // This lane's byte offsets inside a tile for its first K and V loads (the
+  // i-th load adds i * kLoaders * 16 to the base).
+  const uint32_t k_off_lane = wave * 64 * 16 + key_of_slot(lane) * 16;
+  const uint32_t v_off_lane = (wave * 64 + lane) * 16;
   auto issue = [&](int32_t block_id, int st) {
     if (wave >= 4) return;
     const int phys = clamp_block(block_id, a.num_blocks);
-    const int64_t tile = (int64_t)phys * a.kv_heads + g;
-    const unsigned char* kb = kpool + tile * C::KBytes;
-    const unsigned char* vb = vpool + tile * C::VBytes;
+    const unsigned char* kb = kpool + phys * kstride;
+    const unsigned char* vb = vpool + phys * vstride;
     const uint32_t ks = smem_base + st * C::Stage;
 #pragma unroll
     for (int i = 0; i < C::KPT; ++i) {
       const int chunk = wave * 64 + i * C::kLoaders;
-      load_to_lds16(kb + (chunk + lane) * 16, __builtin_amdgcn_readfirstlane(ks + chunk * 16));
+      load_to_lds16(kb + i * C::kLoaders * 16, k_off_lane, __builtin_amdgcn_readfirstlane(ks + chunk * 16));
     }
 #pragma unroll
     for (int i = 0; i < C::VPT; ++i) {
       const int chunk = wave * 64 + i * C::kLoaders;
-      load_to_lds16(vb + (chunk + lane) * 16, __builtin_amdgcn_readfirstlane(ks + C::KBytes + chunk * 16));
+      load_to_lds16(vb + i * C::kLoaders * 16, v_off_lane, __builtin_amdgcn_readfirstlane(ks + C::KBytes + chunk * 16));
     }
   };
   // The same transfer spread over the leading waves' matrix phase: prep() fixes
   // the tile and stage, dma_one(j) moves this thread's j-th 16-byte chunk
   // (K chunks first, then V).  Issued in a burst, the loads would hold the wave
   // for as long as the direct-to-LDS path needs to drain a tile; one load per
-  // four MFMAs stays under that rate, so the wave never waits at issue.
+  // eight MFMAs stays under that rate, so the wave never waits at issue.
   const unsigned char* pend_k = kpool;
   const unsigned char* pend_v = vpool;
   uint32_t pend_lds = 0;
   auto prep = [&](int32_t block_id, int st) {
     const int phys = clamp_block(block_id, a.num_blocks);
-    const int64_t tile = (int64_t)phys * a.kv_heads + g;
-    pend_k = kpool + tile * C::KBytes + (wave * 64 + lane) * 16;
-    pend_v = vpool + tile * C::VBytes + (wave * 64 + lane) * 16;
+    pend_k = kpool + phys * kstride;
+    pend_v = vpool + phys * vstride;
     pend_lds = smem_base + st * C::Stage + wave * 64 * 16;
   };
   auto dma_one = [&](int j) {
     if (j < C::KPT)
-      load_to_lds16(pend_k + j * C::kLoaders * 16, __builtin_amdgcn_readfirstlane(pend_lds + j * C::kLoaders * 16));
+      load_to_lds16(pend_k + j * C::kLoaders * 16, k_off_lane, __builtin_amdgcn_readfirstlane(pend_lds + j * C::kLoaders * 16));
     else
-      load_to_lds16(pend_v + (j - C::KPT) * C::kLoaders * 16,
+      load_to_lds16(pend_v + (j - C::KPT) * C::kLoaders * 16, v_off_lane,
                     __builtin_amdgcn_readfirstlane(pend_lds + C::KBytes + (j - C::KPT) * C::kLoaders * 16));
   };
 
-  f32x16_t o[C::NB];
+  f32x4_t o[C::NDB][2];
 #pragma unroll
-  for (int b = 0; b < C::NB; ++b) o[b] = f32x16_t{};
-  float m_run = -INFINITY, l_run = 0.f;
-  f32x16_t s0 = f32x16_t{}, s1 = f32x16_t{};   // S^T of the tile between QK and softmax
-  u32x4_t pkv[4];                               // bf16 P of the tile between softmax and PV,
-#pragma unroll                                    // one MFMA B operand per 16-key step
-  for (int i = 0; i < 4; ++i) pkv[i] = u32x4_t{0u, 0u, 0u, 0u};
+  for (int b = 0; b < C::NDB; ++b) o[b][0] = o[b][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+  // Per row, kept in step with m_run: the exp offset -m_run*cs (0 while no key
+  // was visible) and the threshold m_run*cs + kLazyRescale that a new maximum
+  // must pass to be taken.
+  float neg_mb[2] = {0.f, 0.f}, thr[2] = {-INFINITY, -INFINITY};
+  f32x4_t s[4][2];                              // S^T of the tile between QK and softmax
+#pragma unroll
+  for (int b = 0; b < 4; ++b) s[b][0] = s[b][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  u32x4_t pkv[2][2];                            // bf16 P^T of the tile between softmax and PV,
+#pragma unroll                                    // one B operand per (query block, 32-key step)
+  for (int qb = 0; qb < 2; ++qb) pkv[qb][0] = pkv[qb][1] = u32x4_t{0u, 0u, 0u, 0u};
 
   auto stage_ptr = [&](int st) { return smem + st * C::Stage; };
 
-  // S^T = K Q^T for one 64-key tile (two 32-key halves).
-  const int k_lane = (hl * kBlock + bf16_key_of_row(col)) * 16;   // this lane's K operand offset
-  const int v_lane = C::KBytes + (hl * DV + col) * 16;             // this lane's V operand offset
+  // Operand offsets: K operand (key block b, feature step i) at k_lane + (256 i + 16 b) * 16,
+  // V operand (key step ks, value block db) at v_lane + (4 ks DV + 16 db) * 16.
+  const int k_lane = (lg * kBlock + lc) * 16;
+  const int v_lane = C::KBytes + (lg * DV + lc) * 16;
+  auto k_off = [](int q) { return (256 * (q >> 2) + 16 * (q & 3)) * 16; };            // QK operand q = 4 i + b
+  auto v_off = [](int u) { return (4 * (u / C::NDB) * DV + 16 * (u % C::NDB)) * 16; };   // PV operand u = NDB ks + db
+  auto qk_mfma = [&](int q, u32x4_t kf, f32x4_t (&n)[4][2]) {
+    n[q & 3][0] = mfma16(kf, qreg[0][q >> 2], n[q & 3][0]);
+    n[q & 3][1] = mfma16(kf, qreg[1][q >> 2], n[q & 3][1]);
+  };
+  auto pv_mfma = [&](int u, u32x4_t vf) {
+    const int ks = u / C::NDB, db = u % C::NDB;
+    o[db][0] = mfma16(vf, pkv[0][ks], o[db][0]);
+    o[db][1] = mfma16(vf, pkv[1][ks], o[db][1]);
+  };
+
+  // S^T = K Q^T for one 64-key tile.
   auto qk = [&](int st) {
     const unsigned char* kb = stage_ptr(st) + k_lane;
-    s0 = f32x16_t{};
-    s1 = f32x16_t{};
+    f32x4_t n[4][2];
 #pragma unroll
-    for (int i = 0; i < C::NQ; ++i) {
-      const u32x4_t k0 = *(const u32x4_t*)(kb + 2 * i * kBlock * 16);
-      const u32x4_t k1 = *(const u32x4_t*)(kb + (2 * i * kBlock + 32) * 16);
-      s0 = mfma_bf16(k0, qreg[i], s0);
-      s1 = mfma_bf16(k1, qreg[i], s1);
-    }
+    for (int b = 0; b < 4; ++b) n[b][0] = n[b][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int q = 0; q < C::KF; ++q) qk_mfma(q, *(const u32x4_t*)(kb + k_off(q)), n);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) s[b][0] = n[b][0], s[b][1] = n[b][1];
   };
 
   // Online softmax of tile j: mask, running max (raised lazily), rescale,
@@ -234,136 +335,131 @@ __global__ __launch_bounds__(512, 1) void prefill_paged_kernel(const PrefillArgs
   auto softmax = [&](int j) {
     const int64_t key0 = (int64_t)j * kBlock;
     if (key0 + kBlock - 1 > wave_first_pos) {
-      const int lim = (int)(pos - key0);          // keys past lim are invisible to this row
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        if (bf16_key_of_reg(0, r, hl) > lim) s0[r] = -INFINITY;
-        if (bf16_key_of_reg(1, r, hl) > lim) s1[r] = -INFINITY;
+      for (int qb = 0; qb < 2; ++qb) {
+        const int lim = (int)(pos[qb] - key0) - 8 * lg;   // register offsets past lim are invisible
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (key_of_reg(b, r) > lim) s[b][qb][r] = -INFINITY;
       }
     }
-    float mx = s0[0];
+    float mx[2];
+    bool grow[2];
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s0[r]);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s1[r]);
-    mx = half_max(mx);
-    const bool grow = mx * cs > m_run * cs + kLazyRescale;
-    if (__any(grow)) {
-      const float m_new = grow ? mx : m_run;
-      const float alpha = grow ? fast_exp2((m_run - m_new) * cs) : 1.f;
-      l_run *= alpha;
-#pragma unroll
-      for (int b = 0; b < C::NB; ++b)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[b][r] *= alpha;
-      m_run = m_new;
+    for (int qb = 0; qb < 2; ++qb) {
+      float m = max3_raw(s[0][qb][0], s[0][qb][1], s[0][qb][2]);
+      m = max3_raw(m, s[0][qb][3], s[1][qb][0]);
+      m = max3_raw(m, s[1][qb][1], s[1][qb][2]);
+      m = max3_raw(m, s[1][qb][3], s[2][qb][0]);
+      m = max3_raw(m, s[2][qb][1], s[2][qb][2]);
+      m = max3_raw(m, s[2][qb][3], s[3][qb][0]);
+      m = max3_raw(m, s[3][qb][1], s[3][qb][2]);
+      mx[qb] = max_raw(m, s[3][qb][3]);
     }
-    const float mb = (m_run == -INFINITY) ? 0.f : m_run * cs;
-    float psum = 0.f;
+    quad_max2(mx[0], mx[1]);
 #pragma unroll
-    for (int rr = 0; rr < 8; ++rr) {
-      const float p0 = fast_exp2(__builtin_fmaf(s0[2 * rr], cs, -mb));
-      const float p1 = fast_exp2(__builtin_fmaf(s0[2 * rr + 1], cs, -mb));
-      const float p2 = fast_exp2(__builtin_fmaf(s1[2 * rr], cs, -mb));
-      const float p3 = fast_exp2(__builtin_fmaf(s1[2 * rr + 1], cs, -mb));
-      psum += (p0 + p1) + (p2 + p3);
-      pkv[rr >> 2][rr & 3] = pack_bf16(p0, p1);
-      pkv[2 + (rr >> 2)][rr & 3] = pack_bf16(p2, p3);
+    for (int qb = 0; qb < 2; ++qb) grow[qb] = mx[qb] * cs > thr[qb];
+    if (__any(grow[0] || grow[1])) {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const float m_new = grow[qb] ? mx[qb] : m_run[qb];
+        const float alpha = grow[qb] ? fast_exp2((m_run[qb] - m_new) * cs) : 1.f;
+        l_run[qb] *= alpha;
+#pragma unroll
+        for (int b = 0; b < C::NDB; ++b)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) o[b][qb][r] *= alpha;
+        m_run[qb] = m_new;
+        if (grow[qb]) {
+          neg_mb[qb] = -(m_new * cs);
+          thr[qb] = m_new * cs + kLazyRescale;
+        }
+      }
     }
-    l_run += psum;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      float p[4][4];
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) p[b][r] = fast_exp2(__builtin_fmaf(s[b][qb][r], cs, neg_mb[qb]));
+      float psum = (p[0][0] + p[0][1]) + (p[0][2] + p[0][3]);
+#pragma unroll
+      for (int b = 1; b < 4; ++b) psum += (p[b][0] + p[b][1]) + (p[b][2] + p[b][3]);
+      l_run[qb] += psum;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+        pkv[qb][ks] = u32x4_t{pack_bf16(p[2 * ks][0], p[2 * ks][1]), pack_bf16(p[2 * ks][2], p[2 * ks][3]),
+                              pack_bf16(p[2 * ks + 1][0], p[2 * ks + 1][1]),
+                              pack_bf16(p[2 * ks + 1][2], p[2 * ks + 1][3])};
+    }
   };
 
-  // O^T += V^T P^T for tile j.
+  // O^T += V^T P^T for one tile.
   auto pv = [&](int st) {
     const unsigned char* vb = stage_ptr(st) + v_lane;
 #pragma unroll
-    for (int stp = 0; stp < 4; ++stp) {
-#pragma unroll
-      for (int b = 0; b < C::NB; ++b) {
-        const u32x4_t va = *(const u32x4_t*)(vb + (2 * stp * DV + 32 * b) * 16);
-        o[b] = mfma_bf16(va, pkv[stp], o[b]);
-      }
-    }
+    for (int u = 0; u < C::VF; ++u) pv_mfma(u, *(const u32x4_t*)(vb + v_off(u)));
   };
 
-  // PV of tile jp and QK of the next tile, issued alternately: six independent
-  // accumulator chains (four O blocks, two S halves), so no matrix-core
-  // instruction waits on the one just before it.
+  // Operand order of the combined matrix phase: PV and QK operands alternate
+  // while both remain, then the rest of QK.  Every operand feeds two MFMAs on
+  // independent accumulators, so no matrix-core instruction waits on the one
+  // just before it.
+  constexpr int kOps = C::VF + C::KF;
+  auto is_pv = [](int k) { return k < 2 * C::VF ? (k & 1) == 0 : false; };
+  auto qk_index = [](int k) { return k < 2 * C::VF ? (k >> 1) : k - C::VF; };
+
+  // PV of the previous tile and QK of the current one (trailing waves).
   auto pv_qk = [&](int st_prev, int st_cur) {
     const unsigned char* vb = stage_ptr(st_prev) + v_lane;
     const unsigned char* kb = stage_ptr(st_cur) + k_lane;
-    f32x16_t n0 = f32x16_t{}, n1 = f32x16_t{};
+    f32x4_t n[4][2];
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      {   // PV step (stp, b) = (u / NB, u % NB), covering all 16 for NB = 4
-        constexpr int kPv = 4 * C::NB;
-        if (u < kPv) {
-          const int stp = u / C::NB, b = u % C::NB;
-          const u32x4_t va = *(const u32x4_t*)(vb + (2 * stp * DV + 32 * b) * 16);
-          o[b] = mfma_bf16(va, pkv[stp], o[b]);
-        }
-      }
-      {   // QK step (i, half) = (u / 2, u % 2)
-        const int i = u >> 1;
-        if (i < C::NQ) {
-          const u32x4_t kk = *(const u32x4_t*)(kb + (2 * i * kBlock + 32 * (u & 1)) * 16);
-          if (u & 1) n1 = mfma_bf16(kk, qreg[i], n1);
-          else n0 = mfma_bf16(kk, qreg[i], n0);
-        }
-      }
+    for (int b = 0; b < 4; ++b) n[b][0] = n[b][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < kOps; ++k) {
+      if (is_pv(k)) pv_mfma(k >> 1, *(const u32x4_t*)(vb + v_off(k >> 1)));
+      else qk_mfma(qk_index(k), *(const u32x4_t*)(kb + k_off(qk_index(k))), n);
     }
 #pragma unroll
-    for (int u = 16; u < 2 * C::NQ; ++u) {   // remaining QK steps when d > 128
-      const int i = u >> 1;
-      const u32x4_t kk = *(const u32x4_t*)(kb + (2 * i * kBlock + 32 * (u & 1)) * 16);
-      if (u & 1) n1 = mfma_bf16(kk, qreg[i], n1);
-      else n0 = mfma_bf16(kk, qreg[i], n0);
-    }
-    s0 = n0;
-    s1 = n1;
-    // Issue order: kLead LDS operand reads ahead, then one matrix op per read,
+    for (int b = 0; b < 4; ++b) s[b][0] = n[b][0], s[b][1] = n[b][1];
+    // Issue order: kLead LDS operand reads ahead, then two matrix ops per read,
     // so about kLead reads are in flight while the matrix cores run.
-    constexpr int kReads = 4 * C::NB + 2 * C::NQ, kLead = 6;
+    constexpr int kLead = 6;
     __builtin_amdgcn_sched_group_barrier(0x100, kLead, 0);
 #pragma unroll
-    for (int r = 0; r < kReads - kLead; ++r) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    for (int r = 0; r < kOps - kLead; ++r) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, kLead, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 2 * kLead, 0);
   };
 
   // pv_qk for the leading waves with the pending tile's loads interleaved: the
   // operand reads are software-pipelined by hand (kAhead in flight) and one
-  // load goes out after every fourth MFMA, fenced so the order stays as written.
+  // load goes out after every fourth operand (eighth MFMA), fenced so the
+  // order stays as written.
   auto pv_qk_dma = [&](int st_prev, int st_cur, bool with_dma) {
     const unsigned char* vb = stage_ptr(st_prev) + v_lane;
     const unsigned char* kb = stage_ptr(st_cur) + k_lane;
-    constexpr int kPv = 4 * C::NB, kQk = 2 * C::NQ, kOps = kPv + kQk, kAhead = 6;
-    // op k: PV and QK alternate while both remain, then the rest of QK
-    auto is_pv = [&](int k) { return k < 2 * kPv ? (k & 1) == 0 : false; };
+    constexpr int kAhead = 6;
     auto op_ptr = [&](int k) -> const u32x4_t* {
-      if (is_pv(k)) {
-        const int u = k >> 1, stp = u / C::NB, b = u % C::NB;
-        return (const u32x4_t*)(vb + (2 * stp * DV + 32 * b) * 16);
-      }
-      const int q = k < 2 * kPv ? (k >> 1) : k - kPv;      // QK step index
-      return (const u32x4_t*)(kb + (2 * (q >> 1) * kBlock + 32 * (q & 1)) * 16);
+      if (is_pv(k)) return (const u32x4_t*)(vb + v_off(k >> 1));
+      return (const u32x4_t*)(kb + k_off(qk_index(k)));
     };
-    f32x16_t n0 = f32x16_t{}, n1 = f32x16_t{};
+    f32x4_t n[4][2];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) n[b][0] = n[b][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     u32x4_t rd[kOps];
 #pragma unroll
     for (int k = 0; k < kAhead; ++k) rd[k] = *op_ptr(k);
 #pragma unroll
     for (int k = 0; k < kOps; ++k) {
-      if (is_pv(k)) {
-        const int u = k >> 1, stp = u / C::NB, b = u % C::NB;
-        o[b] = mfma_bf16(rd[k], pkv[stp], o[b]);
-      } else {
-        const int q = k < 2 * kPv ? (k >> 1) : k - kPv;
-        if (q & 1) n1 = mfma_bf16(rd[k], qreg[q >> 1], n1);
-        else n0 = mfma_bf16(rd[k], qreg[q >> 1], n0);
-      }
+      if (is_pv(k)) pv_mfma(k >> 1, rd[k]);
+      else qk_mfma(qk_index(k), rd[k], n);
       if (k + kAhead < kOps) rd[k + kAhead] = *op_ptr(k + kAhead);
       if ((k & 3) == 3 && (k >> 2) < C::LPT) {
         __builtin_amdgcn_sched_barrier(0);
@@ -371,9 +467,9 @@ __global__ __launch_bounds__(512, 1) void prefill_paged_kernel(const PrefillArgs
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    static_assert(kOps >= 4 * C::LPT, "one load per four MFMAs must fit in the matrix phase");
-    s0 = n0;
-    s1 = n1;
+    static_assert(kOps >= 4 * C::LPT, "one load per four operands must fit in the matrix phase");
+#pragma unroll
+    for (int b = 0; b < 4; ++b) s[b][0] = n[b][0], s[b][1] = n[b][1];
   };
 
   // ---- key loop -------------------------------------------------------------------
@@ -389,8 +485,8 @@ __global__ __launch_bounds__(512, 1) void prefill_paged_kernel(const PrefillArgs
   const int n = j_hi - j_lo;
 #pragma unroll
   for (int p = 0; p < NS - 2; ++p)
-    if (p < n) issue(bt4[j_lo + p], p);
-  int32_t block_ahead = (NS - 2 < n) ? bt4[j_lo + NS - 2] : 0;
+    if (p < n) issue(bt4[p], p);
+  int32_t block_ahead = (NS - 2 < n) ? bt4[NS - 2] : 0;
   // Start of interval i: tile i must have landed (tiles i+1 .. i+NS-3 may
   // still be in flight); after the barrier the stage of tile i-2 is free and
   // receives tile i+NS-2.
@@ -404,9 +500,9 @@ __global__ __launch_bounds__(512, 1) void prefill_paged_kernel(const PrefillArgs
     pending = i + NS - 2 < n;
     if (pending) {
       if (i == 0) issue(block_ahead, NS - 2);          // no matrix phase to hide it in
-      else prep(block_ahead, (i + NS - 2) % NS);       // issued inside pv_qk_dma
+      else if (wave < 4) prep(block_ahead, (i + NS - 2) % NS);   // issued inside pv_qk_dma
     }
-    block_ahead = (i + NS - 1 < n) ? bt4[j_lo + i + NS - 1] : 0;
+    block_ahead = (i + NS - 1 < n) ? bt4[i + NS - 1] : 0;
     const int64_t key0 = (int64_t)(j_lo + i) * kBlock;
     if (i < n && key0 + kBlock > kv_len) {
       // The tile holding the sequence end: zero its values of keys >= kv_len
@@ -461,35 +557,34 @@ __global__ __launch_bounds__(512, 1) void prefill_paged_kernel(const PrefillArgs
   }
 
   // ---- epilogue ------------------------------------------------------------------
-  const float l_tot = half_sum(l_run);
-  if (!row_valid) return;
-  if (S == 1) {
-    const float inv = 1.f / l_tot;
-    EO* orow = obase + (t * a.heads + h) * (int64_t)DV;
+  // Lane (lg, lc) holds values 16 db + 4 lg .. +3 of query row t[qb].
+  float l_tot[2];
 #pragma unroll
-    for (int b = 0; b < C::NB; ++b)
+  for (int qb = 0; qb < 2; ++qb) l_tot[qb] = quad_sum(l_run[qb]);
 #pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        const int dv0 = 32 * b + 8 * rq + 4 * hl;
-        const float v0 = o[b][4 * rq] * inv, v1 = o[b][4 * rq + 1] * inv;
-        const float v2 = o[b][4 * rq + 2] * inv, v3 = o[b][4 * rq + 3] * inv;
-        if constexpr (sizeof(EO) == 2) *(u32x2_t*)(orow + dv0) = u32x2_t{pack_bf16(v0, v1), pack_bf16(v2, v3)};
-        else *(f32x4_t*)(orow + dv0) = f32x4_t{v0, v1, v2, v3};
+  for (int qb = 0; qb < 2; ++qb) {
+    if (!row_valid[qb]) continue;
+    const int64_t row = t[qb] * a.heads + h;
+    if (S == 1) {
+      const float inv = 1.f / l_tot[qb];
+      EO* orow = obase + row * (int64_t)DV + 4 * lg;
+#pragma unroll
+      for (int b = 0; b < C::NDB; ++b) {
+        const float v0 = o[b][qb][0] * inv, v1 = o[b][qb][1] * inv;
+        const float v2 = o[b][qb][2] * inv, v3 = o[b][qb][3] * inv;
+        if constexpr (sizeof(EO) == 2) *(u32x2_t*)(orow + 16 * b) = u32x2_t{pack_bf16(v0, v1), pack_bf16(v2, v3)};
+        else *(f32x4_t*)(orow + 16 * b) = f32x4_t{v0, v1, v2, v3};
       }
-    if (lse && hl == 0) lse[(int64_t)h * a.lse_stride + t] = (m_run * cs + __log2f(l_tot)) * kLn2;
-  } else {
-    const int64_t R = c * a.heads;
-    const int64_t row = t * a.heads + h;
-    float* wo = a.ws_o + ((int64_t)split * R + row) * DV;
+      if (lse && lg == 0) lse[(int64_t)h * a.lse_stride + t[qb]] = (m_run[qb] * cs + __log2f(l_tot[qb])) * kLn2;
+    } else {
+      const int64_t R = c * a.heads;
+      float* wo = a.ws_o + ((int64_t)split * R + row) * DV + 4 * lg;
 #pragma unroll
-    for (int b = 0; b < C::NB; ++b)
-#pragma unroll
-      for (int rq = 0; rq < 4; ++rq)
-        *(f32x4_t*)(wo + 32 * b + 8 * rq + 4 * hl) =
-            f32x4_t{o[b][4 * rq], o[b][4 * rq + 1], o[b][4 * rq + 2], o[b][4 * rq + 3]};
-    if (hl == 0)
-      *(float2*)(a.ws_ml + ((int64_t)split * R + row) * 2) =
-          make_float2(m_run == -INFINITY ? -INFINITY : m_run * cs, l_tot);
+      for (int b = 0; b < C::NDB; ++b) *(f32x4_t*)(wo + 16 * b) = o[b][qb];
+      if (lg == 0)
+        *(float2*)(a.ws_ml + ((int64_t)split * R + row) * 2) =
+            make_float2(m_run[qb] == -INFINITY ? -INFINITY : m_run[qb] * cs, l_tot[qb]);
+    }
   }
 }
 

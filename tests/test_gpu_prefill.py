@@ -191,14 +191,23 @@ def _paged_run(q, pool, table, past, d, **kw):
                                 block_table=table, **kw)
 
 
-def test_paged_equals_contiguous_bitwise():
+def test_paged_matches_contiguous():
+    """The paged-pool kernel (16x16x32 MFMAs) and the contiguous-cache kernel (32x32x16) sum in
+    different fp32 orders, so their bf16 outputs may differ where a value sits at a rounding edge:
+    by at most 2 bf16 units in the last place (unit 2^-7 relative), on a small fraction of elements."""
     c, past, hq, hkv, d = 160, 390, 16, 4, 128
     k, v = seq_kv(past + c, hkv, d, d, "bf16", 101)
     q = inputs.normal((c, hq, d), 102, "bf16").cuda()
     pool, table = single_seq_pool(k, v, 103)
-    a = _paged_run(q, pool, table, past, d, num_splits=1)
-    b = L.chunk_prefill_attn(q, k.cuda(), v.cuda(), past, 1 / math.sqrt(d), num_splits=1)
-    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    a = _paged_run(q, pool, table, past, d, num_splits=1).float()
+    b = L.chunk_prefill_attn(q, k.cuda(), v.cuda(), past, 1 / math.sqrt(d), num_splits=1).float()
+    diff = (a - b).abs()
+    ulp = torch.exp2(torch.floor(torch.log2(torch.maximum(a.abs(), b.abs()).clamp_min(2.0 ** -126))) - 7)
+    same = (diff == 0).float().mean().item()
+    log(f"paged vs contiguous: max diff {diff.max().item():.3e}, max {(diff / ulp).max().item():.0f} ulp, "
+        f"{100 * same:.2f}% identical")
+    assert torch.all(diff <= 2 * ulp)
+    assert same >= 0.95
 
 
 def test_deterministic_bitwise():
