@@ -39,7 +39,9 @@
 //  * Per row the softmax keeps, beside the running max m, the exp offset
 //    -m*scale and the threshold a new max must pass (lazy rescale); both
 //    change only when m does, so a tile costs one fma + exp per logit, the
-//    max3 chains, the pack to bf16 and the fp32 sum.
+//    max3 chains, the pack to bf16 and the fp32 sum.  At d <= 128 the exps
+//    run ahead of the row-max reduction with the current offset and are
+//    redone only for a tile where some row's maximum grew.
 //  * The two waves that share a SIMD run the same tiles half an interval
 //    apart (ping-pong), so one feeds the matrix cores while the other
 //    computes its softmax; the rescale is skipped when no row's maximum grew.
@@ -290,9 +292,10 @@ __global__ __launch_bounds__(512, 1) void prefill_paged_kernel(const PrefillArgs
   for (int b = 0; b < C::NDB; ++b) o[b][0] = o[b][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
   // Per row, kept in step with m_run: the exp offset -m_run*cs (0 while no key
-  // was visible) and the threshold m_run*cs + kLazyRescale that a new maximum
-  // must pass to be taken.
+  // was visible) and the threshold m_run + kLazyRescale/cs that a new maximum
+  // must pass to be taken (cs > 0: the boundary rejects other scales).
   float neg_mb[2] = {0.f, 0.f}, thr[2] = {-INFINITY, -INFINITY};
+  const float lazy_unscaled = kLazyRescale / cs;
   f32x4_t s[4][2];                              // S^T of the tile between QK and softmax
 #pragma unroll
   for (int b = 0; b < 4; ++b) s[b][0] = s[b][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -345,6 +348,22 @@ __global__ __launch_bounds__(512, 1) void prefill_paged_kernel(const PrefillArgs
             if (key_of_reg(b, r) > lim) s[b][qb][r] = -INFINITY;
       }
     }
+    // With registers to spare (d <= 128) the exps start before the row maxima
+    // are known, with the current offset; a row whose maximum grows (rare,
+    // given the lazy threshold) has them recomputed.  Overflow in a discarded
+    // speculative value is harmless.
+    constexpr bool kSpec = D <= 128;
+    float p[2][4][4];
+    auto exps = [&](int qb) {
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) p[qb][b][r] = fast_exp2(__builtin_fmaf(s[b][qb][r], cs, neg_mb[qb]));
+    };
+    if constexpr (kSpec) {
+      exps(0);
+      exps(1);
+    }
     float mx[2];
     bool grow[2];
 #pragma unroll
@@ -360,7 +379,15 @@ __global__ __launch_bounds__(512, 1) void prefill_paged_kernel(const PrefillArgs
     }
     quad_max2(mx[0], mx[1]);
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) grow[qb] = mx[qb] * cs > thr[qb];
+    for (int qb = 0; qb < 2; ++qb) grow[qb] = mx[qb] > thr[qb];
+    if constexpr (kSpec) {
+      // keep the speculative exps ahead of the branch (not sunk into its
+      // no-growth side, where they would wait for the maxima again)
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) asm volatile("" ::"v"(p[qb][b][0]), "v"(p[qb][b][1]), "v"(p[qb][b][2]), "v"(p[qb][b][3]));
+    }
     if (__any(grow[0] || grow[1])) {
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
@@ -374,26 +401,30 @@ __global__ __launch_bounds__(512, 1) void prefill_paged_kernel(const PrefillArgs
         m_run[qb] = m_new;
         if (grow[qb]) {
           neg_mb[qb] = -(m_new * cs);
-          thr[qb] = m_new * cs + kLazyRescale;
+          thr[qb] = m_new + lazy_unscaled;
         }
       }
+      if constexpr (kSpec) {
+        exps(0);
+        exps(1);
+      }
+    }
+    if constexpr (!kSpec) {
+      exps(0);
+      exps(1);
     }
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      float p[4][4];
+      float (&pq)[4][4] = p[qb];
+      float psum = (pq[0][0] + pq[0][1]) + (pq[0][2] + pq[0][3]);
 #pragma unroll
-      for (int b = 0; b < 4; ++b)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) p[b][r] = fast_exp2(__builtin_fmaf(s[b][qb][r], cs, neg_mb[qb]));
-      float psum = (p[0][0] + p[0][1]) + (p[0][2] + p[0][3]);
-#pragma unroll
-      for (int b = 1; b < 4; ++b) psum += (p[b][0] + p[b][1]) + (p[b][2] + p[b][3]);
+      for (int b = 1; b < 4; ++b) psum += (pq[b][0] + pq[b][1]) + (pq[b][2] + pq[b][3]);
       l_run[qb] += psum;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
-        pkv[qb][ks] = u32x4_t{pack_bf16(p[2 * ks][0], p[2 * ks][1]), pack_bf16(p[2 * ks][2], p[2 * ks][3]),
-                              pack_bf16(p[2 * ks + 1][0], p[2 * ks + 1][1]),
-                              pack_bf16(p[2 * ks + 1][2], p[2 * ks + 1][3])};
+        pkv[qb][ks] = u32x4_t{pack_bf16(pq[2 * ks][0], pq[2 * ks][1]), pack_bf16(pq[2 * ks][2], pq[2 * ks][3]),
+                              pack_bf16(pq[2 * ks + 1][0], pq[2 * ks + 1][1]),
+                              pack_bf16(pq[2 * ks + 1][2], pq[2 * ks + 1][3])};
     }
   };
 
@@ -428,7 +459,7 @@ __global__ __launch_bounds__(512, 1) void prefill_paged_kernel(const PrefillArgs
     for (int b = 0; b < 4; ++b) s[b][0] = n[b][0], s[b][1] = n[b][1];
     // Issue order: kLead LDS operand reads ahead, then two matrix ops per read,
     // so about kLead reads are in flight while the matrix cores run.
-    constexpr int kLead = 6;
+    constexpr int kLead = 8;
     __builtin_amdgcn_sched_group_barrier(0x100, kLead, 0);
 #pragma unroll
     for (int r = 0; r < kOps - kLead; ++r) {
@@ -445,7 +476,7 @@ __global__ __launch_bounds__(512, 1) void prefill_paged_kernel(const PrefillArgs
   auto pv_qk_dma = [&](int st_prev, int st_cur, bool with_dma) {
     const unsigned char* vb = stage_ptr(st_prev) + v_lane;
     const unsigned char* kb = stage_ptr(st_cur) + k_lane;
-    constexpr int kAhead = 6;
+    constexpr int kAhead = 8;
     auto op_ptr = [&](int k) -> const u32x4_t* {
       if (is_pv(k)) return (const u32x4_t*)(vb + v_off(k >> 1));
       return (const u32x4_t*)(kb + k_off(qk_index(k)));
