@@ -275,3 +275,29 @@ def test_rejected_arguments_raise():
         L.chunk_prefill_attn(q, k, k, 500, 0.1, num_splits=4,
                              workspace=torch.empty(16, dtype=torch.uint8, device="cuda"))
     assert e.value.status == L.CA_EWORKSPACE
+
+
+@pytest.mark.parametrize("d,dv,splits", [(128, 128, 1), (64, 64, 1), (192, 128, 1), (128, 128, 3)])
+def test_late_max_growth(d, dv, splits):
+    """Keys scaled x1 before a step and x50 (rising) after it: every row's running maximum jumps by
+    ~175 log2 units at the step, so exp2 at the stale offset overflows and must be discarded, and it
+    keeps growing past the lazy-rescale margin afterwards.  Output and LSE still match the oracle.
+    The output is fp32: such peaked rows average a handful of values, |o| reaches ~4, and a bf16 store
+    alone could then err by up to 2^-7 on top of the bf16 weights."""
+    c, past, hq, hkv = 200, 700, 8, 2
+    n = past + c
+    k, v = seq_kv(n, hkv, d, dv, "bf16", 141)
+    j = torch.arange(n, dtype=torch.float32)
+    gain = torch.where(j < 450, torch.ones_like(j), 50.0 + 0.2 * (j - 450)).view(n, 1, 1)
+    k = (k.float() * gain).to(torch.bfloat16)
+    q = inputs.normal((c, hq, d), 142, "bf16")
+    pool, table = single_seq_pool(k, v, 143)
+    scale = 1 / math.sqrt(d)
+    out, lse = L.chunk_prefill_attn(q.cuda(), pool.k, pool.v, past, scale, kv_layout="paged",
+                                    block_table=table, return_lse=True, num_splits=splits,
+                                    out_dtype=torch.float32)
+    ref, ref_lse = oracle_chunk(q, k, v, past, scale)
+    e, el = max_err(out, ref), max_err(lse, ref_lse)
+    log(f"late max growth d={d}/{dv} splits={splits}: max err {e:.3e}, lse err {el:.2e}")
+    assert torch.isfinite(out.float()).all()
+    assert e <= BF16_TOL and el <= LSE_TOL
