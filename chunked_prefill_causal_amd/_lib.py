@@ -26,6 +26,7 @@ BLOCK_SIZE = 64
 MLA_LATENT, MLA_ROPE = 512, 64
 
 EXPORTED = ("ca_prefill_opts_init", "chunk_prefill_attn", "chunkattn_prefill_workspace_size",
+            "chunkattn_prefill_contiguous_workspace_size",
             "chunkattn_prefill_auto_splits", "chunk_attn_varlen", "chunkattn_varlen_workspace_size",
             "chunkattn_kv_append", "chunkattn_sched_simulate", "chunkattn_sched_drain_pack",
             "chunkattn_alp_features", "chunkattn_alp_init", "chunkattn_alp_predict", "chunkattn_alp_update",
@@ -74,6 +75,8 @@ def lib() -> ctypes.CDLL:
     L.chunk_prefill_attn.restype = ctypes.c_int
     L.chunkattn_prefill_workspace_size.argtypes = [i64, i32, i32, i32]
     L.chunkattn_prefill_workspace_size.restype = sz
+    L.chunkattn_prefill_contiguous_workspace_size.argtypes = [i64, i64, i32, i32, i32, i32, i32]
+    L.chunkattn_prefill_contiguous_workspace_size.restype = sz
     L.chunkattn_prefill_auto_splits.argtypes = [i64, i64, i32, i32]
     L.chunkattn_prefill_auto_splits.restype = i32
     L.chunk_attn_varlen.argtypes = [vp, vp, vp, vp, i32, i32, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32,
@@ -227,6 +230,12 @@ def chunkattn_prefill_workspace_size(chunk_len: int, heads: int, head_dim_v: int
     return lib().chunkattn_prefill_workspace_size(chunk_len, heads, head_dim_v, num_splits)
 
 
+def chunkattn_prefill_contiguous_workspace_size(past_len: int, chunk_len: int, heads: int, kv_heads: int,
+                                                head_dim: int, head_dim_v: int, num_splits: int) -> int:
+    return lib().chunkattn_prefill_contiguous_workspace_size(past_len, chunk_len, heads, kv_heads, head_dim,
+                                                             head_dim_v, num_splits)
+
+
 def chunkattn_prefill_auto_splits(past_len: int, chunk_len: int, heads: int, kv_heads: int) -> int:
     return lib().chunkattn_prefill_auto_splits(past_len, chunk_len, heads, kv_heads)
 
@@ -235,12 +244,15 @@ def chunk_prefill_attn(q, k_cache, v_cache, past_len: int, scale: float | None =
                        kv_layout: str = "contiguous", block_table=None, num_blocks: int | None = None,
                        kv_heads: int | None = None, head_dim_v: int | None = None, out=None, out_dtype=None,
                        return_lse: bool = False, lse=None, num_splits: int = 0, workspace=None,
-                       kv_capacity: int | None = None, stream=None):
+                       kv_capacity: int | None = None, relayout: bool = True, stream=None):
     """One chunk of causal prefill attention; see ``chunk_prefill_attn`` in the header.
 
     ``q`` is ``[chunk_len, heads, head_dim]``.  Contiguous caches are
     ``[capacity, kv_heads, head_dim(_v)]``; paged pools come from
-    :func:`paged_pool` with ``block_table`` an int32 device tensor.
+    :func:`paged_pool` with ``block_table`` an int32 device tensor.  For a
+    bf16 contiguous cache the workspace allocated here has room for the
+    library to re-lay the prefix for the paged kernel (``relayout=False``
+    sizes it for split partials only, so the cache is read in place).
     Returns ``out`` (and ``lse [heads, chunk_len]`` when requested).
     """
     c, heads, d = q.shape
@@ -261,6 +273,10 @@ def chunk_prefill_attn(q, k_cache, v_cache, past_len: int, scale: float | None =
         out = torch.empty((c, heads, dv), dtype=out_dtype, device=q.device)
     if return_lse and lse is None:
         lse = torch.empty((heads, c), dtype=torch.float32, device=q.device)
+    if workspace is None and not paged and relayout and c > 0:
+        need = chunkattn_prefill_contiguous_workspace_size(past_len, c, heads, hkv, d, dv, num_splits)
+        if need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     if num_splits == 0 and workspace is None:
         auto = chunkattn_prefill_auto_splits(past_len, c, heads, hkv)
         if auto > 1:

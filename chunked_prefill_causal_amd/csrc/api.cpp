@@ -60,6 +60,23 @@ size_t prefill_ws_bytes(int64_t chunk_len, int heads, int dv, int splits) {
   return align_up(rows * dv * sizeof(float), 256) + rows * 2 * sizeof(float);
 }
 
+// A bf16 contiguous cache is read by the paged kernel after the K/V prefix is
+// re-laid into the workspace: an identity block table, then K and V pools of
+// ceil(kv_len / 64) blocks in the paged tile layout.
+struct Relayout {
+  int64_t blocks = 0;
+  size_t table = 0, k = 0, v = 0, bytes = 0;
+};
+Relayout relayout_plan(int64_t kv_len, int kv_heads, int d, int dv) {
+  Relayout r;
+  r.blocks = (kv_len + kBlock - 1) / kBlock;
+  r.table = align_up((size_t)r.blocks * sizeof(int32_t), 256);
+  r.k = (size_t)r.blocks * kv_heads * d * kBlock * 2;
+  r.v = (size_t)r.blocks * kv_heads * dv * kBlock * 2;
+  r.bytes = r.table + r.k + r.v;
+  return r;
+}
+
 // Decode split length: aim for enough waves to fill the chip several times
 // over, in multiples of the 64-token tile.
 int decode_split_tokens(const int32_t* cu, const int32_t* kv, int num_seqs, int kv_heads, int group) {
@@ -215,6 +232,19 @@ size_t chunkattn_prefill_workspace_size(int64_t chunk_len, int32_t heads, int32_
   return prefill_ws_bytes(chunk_len, heads, head_dim_v, num_splits);
 }
 
+size_t chunkattn_prefill_contiguous_workspace_size(int64_t past_len, int64_t chunk_len, int32_t heads,
+                                                   int32_t kv_heads, int32_t head_dim, int32_t head_dim_v,
+                                                   int32_t num_splits) {
+  if (past_len < 0 || chunk_len <= 0 || heads <= 0 || kv_heads <= 0 || heads % kv_heads || head_dim <= 0)
+    return 0;
+  const int dv = head_dim_v ? head_dim_v : head_dim;
+  const int splits = num_splits == 0 ? auto_splits(past_len, chunk_len, heads, kv_heads) : num_splits;
+  size_t bytes = prefill_ws_bytes(chunk_len, heads, dv, splits);
+  if (prefill_paged_supported(head_dim, dv) && past_len + chunk_len <= kMaxTokens)
+    bytes += relayout_plan(past_len + chunk_len, kv_heads, head_dim, dv).bytes;
+  return bytes;
+}
+
 int32_t chunkattn_prefill_auto_splits(int64_t past_len, int64_t chunk_len, int32_t heads, int32_t kv_heads) {
   if (past_len < 0 || chunk_len < 0 || heads <= 0 || kv_heads <= 0 || heads % kv_heads) return 0;
   return auto_splits(past_len, chunk_len, heads, kv_heads);
@@ -261,7 +291,18 @@ ca_status chunk_prefill_attn(const void* q, const void* k, const void* v, int64_
   if (o.num_splits < 0) return fail(CA_EINVAL, "num_splits must be >= 0");
 
   const int group = heads / kv_heads;
-  const bool use_paged_kernel = paged && din == DType::BF16 && prefill_paged_supported(head_dim, dv);
+  // bf16 contiguous cache + room in the workspace: re-lay the prefix and run the paged kernel
+  const bool paged_dims = din == DType::BF16 && prefill_paged_supported(head_dim, dv);
+  Relayout rl;
+  bool relay = false;
+  if (!paged && paged_dims && o.workspace && aligned(o.workspace, 256)) {
+    rl = relayout_plan(kv_len, kv_heads, head_dim, dv);
+    relay = o.workspace_bytes >= rl.bytes;
+  }
+  // split partials follow the re-laid pools in the workspace
+  void* const ws_split = relay ? (void*)((char*)o.workspace + rl.bytes) : o.workspace;
+  const size_t ws_split_bytes = relay ? o.workspace_bytes - rl.bytes : o.workspace_bytes;
+  const bool use_paged_kernel = (paged || relay) && paged_dims;
   const int hpw = heads_per_wg(group, use_paged_kernel ? kWavesPaged : kWavesSmall);
   const int tok_wg = (use_paged_kernel ? 256 : 128) / hpw;
   const int64_t n_tb = (chunk_len + tok_wg - 1) / tok_wg;
@@ -271,14 +312,15 @@ ca_status chunk_prefill_attn(const void* q, const void* k, const void* v, int64_
   int splits = o.num_splits;
   if (splits == 0) {
     const int want = auto_splits(past_len, chunk_len, heads, kv_heads);
-    splits = (want > 1 && o.workspace && o.workspace_bytes >= prefill_ws_bytes(chunk_len, heads, dv, want)) ? want : 1;
+    splits = (want > 1 && ws_split && ws_split_bytes >= prefill_ws_bytes(chunk_len, heads, dv, want)) ? want : 1;
   } else if (splits > n_tiles) {
     splits = (int)(n_tiles > 0 ? n_tiles : 1);
   }
   if (splits > 1) {
     const size_t need = prefill_ws_bytes(chunk_len, heads, dv, splits);
-    if (!o.workspace || o.workspace_bytes < need)
-      return fail(CA_EWORKSPACE, "split-KV with %d splits needs %zu workspace bytes", splits, need);
+    if (!ws_split || ws_split_bytes < need)
+      return fail(CA_EWORKSPACE, "split-KV with %d splits needs %zu workspace bytes%s", splits, need,
+                  relay ? " after the re-laid K/V" : "");
     if (!aligned(o.workspace, 256)) return fail(CA_EINVAL, "workspace must be 256-byte aligned");
   }
   if (base * splits > 0x7fffffffLL) return fail(CA_ERANGE, "launch grid too large");
@@ -307,10 +349,23 @@ ca_status chunk_prefill_attn(const void* q, const void* k, const void* v, int64_
   a.scale_log2 = scale * kLog2e;
   if (splits > 1) {
     const size_t rows = (size_t)chunk_len * heads * splits;
-    a.ws_o = (float*)o.workspace;
-    a.ws_ml = (float*)((char*)o.workspace + align_up(rows * dv * sizeof(float), 256));
+    a.ws_o = (float*)ws_split;
+    a.ws_ml = (float*)((char*)ws_split + align_up(rows * dv * sizeof(float), 256));
   }
   hipStream_t s = (hipStream_t)stream;
+  if (relay) {
+    int32_t* table = (int32_t*)o.workspace;
+    void* kpool = (char*)o.workspace + rl.table;
+    void* vpool = (char*)o.workspace + rl.table + rl.k;
+    hipError_t e = launch_block_iota(table, (int)rl.blocks, s);
+    if (e == hipSuccess)
+      e = launch_kv_append(DType::BF16, head_dim, dv, k, v, 0, kv_len, kv_heads, table, (int)rl.blocks, kpool, vpool, s);
+    if (e != hipSuccess) return hip_status(e, "contiguous cache re-layout");
+    a.k = kpool;
+    a.v = vpool;
+    a.block_table = table;
+    a.num_blocks = (int)rl.blocks;
+  }
   hipError_t e = use_paged_kernel ? launch_prefill_paged(dout, head_dim, dv, a, (int)(base * splits), s)
                                   : launch_prefill(din, dout, head_dim, dv, paged, a, (int)(base * splits), s);
   if (e != hipSuccess) return hip_status(e, "prefill launch");

@@ -45,6 +45,19 @@ __global__ __launch_bounds__(256) void kv_append_kernel(const E* __restrict__ k_
   }
 }
 
+// Identity block table t[i] = i: lets a contiguous cache, re-laid into a
+// scratch pool block by block, be read by the paged kernels.
+__global__ __launch_bounds__(256) void block_iota_kernel(int32_t* __restrict__ t, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) t[i] = i;
+}
+
+hipError_t launch_block_iota(int32_t* table, int n, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(block_iota_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, table, n);
+  return hipGetLastError();
+}
+
 hipError_t launch_kv_append(DType dt, int D, int DV, const void* k_new, const void* v_new,
                             int64_t start_pos, int64_t n_tokens, int kv_heads,
                             const int32_t* block_table, int num_blocks, void* k_pool, void* v_pool,

@@ -127,6 +127,7 @@ struct MlaAppendArgs {
 hipError_t launch_mla_decode(bool fp8, const MlaArgs& a, hipStream_t stream);
 hipError_t launch_mla_append(bool fp8, const MlaAppendArgs& a, hipStream_t stream);
 
+hipError_t launch_block_iota(int32_t* table, int n, hipStream_t stream);
 hipError_t launch_kv_append(DType dt, int D, int DV, const void* k_new, const void* v_new,
                             int64_t start_pos, int64_t n_tokens, int kv_heads,
                             const int32_t* block_table, int num_blocks, void* k_pool, void* v_pool,

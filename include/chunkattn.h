@@ -91,7 +91,8 @@ typedef struct ca_prefill_opts {
   int32_t num_blocks;          /* paged: blocks in the pool */
   float* lse_out;              /* optional device fp32 [heads, chunk_len]:
                                   natural-log sum of exp(scale * logits) per row */
-  void* workspace;             /* device scratch for split-KV partials */
+  void* workspace;             /* device scratch: split-KV partials and, for a
+                                  bf16 contiguous cache, its re-laid copy */
   size_t workspace_bytes;
   int32_t num_splits;          /* 0 = choose (never needs more workspace than
                                   given; no workspace => no split); 1 = never
@@ -116,6 +117,15 @@ void ca_prefill_opts_init(ca_prefill_opts* opts);
  * Keys at positions >= past_len + chunk_len are never read for V and never
  * influence any row; K/V beyond a row's own position do not change that row.
  * The result is deterministic (bitwise) for fixed arguments and split count.
+ *
+ * Contiguous bf16 cache with a paged-kernel head-dim pair: when the workspace
+ * (256-byte aligned) holds at least the re-layout bytes counted by
+ * chunkattn_prefill_contiguous_workspace_size, the prefix [0, past_len +
+ * chunk_len) of K and V is first copied into the paged tile layout inside the
+ * workspace (an identity block table), and the paged kernel runs on that copy:
+ * its output is then bitwise that of the paged layout.  Without that room the
+ * contiguous kernel reads the cache in place (same result within bf16
+ * rounding, ~3x slower at 128K).  Split-KV partials, if any, follow the copy.
  */
 ca_status chunk_prefill_attn(const void* q_chunk, const void* k_cache, const void* v_cache,
                              int64_t past_len, int64_t chunk_len,
@@ -128,6 +138,16 @@ ca_status chunk_prefill_attn(const void* q_chunk, const void* k_cache, const voi
  */
 size_t chunkattn_prefill_workspace_size(int64_t chunk_len, int32_t heads, int32_t head_dim_v,
                                         int32_t num_splits);
+
+/*
+ * Workspace bytes chunk_prefill_attn uses with a contiguous cache: the
+ * re-laid K/V prefix (bf16 and a paged-kernel head-dim pair; for other
+ * dtypes or dims nothing) plus the split partials of `num_splits` splits
+ * (0 = the count it would choose).  Returns 0 for invalid sizes.
+ */
+size_t chunkattn_prefill_contiguous_workspace_size(int64_t past_len, int64_t chunk_len, int32_t heads,
+                                                   int32_t kv_heads, int32_t head_dim, int32_t head_dim_v,
+                                                   int32_t num_splits);
 
 /*
  * The split count chunk_prefill_attn picks for num_splits = 0 when the

@@ -91,6 +91,9 @@ CASES = [
     (130, 70, 32, 8, 128, 128, "contiguous"),
     (200, 111, 5, 5, 64, 64, "contiguous"),
     (96, 450, 8, 4, 192, 128, "contiguous"),
+    (130, 70, 32, 8, 128, 128, "contiguous-direct"),
+    (200, 111, 5, 5, 64, 64, "contiguous-direct"),
+    (96, 450, 8, 4, 192, 128, "contiguous-direct"),
 ]
 
 
@@ -112,7 +115,7 @@ def test_prefill_bf16_vs_oracle(c, past, hq, hkv, d, dv, layout):
         vc = torch.full((cap, hkv, dv), float("nan"), dtype=torch.bfloat16)
         kc[:n], vc[:n] = k, v
         out, lse = L.chunk_prefill_attn(q.cuda(), kc.cuda(), vc.cuda(), past, scale, return_lse=True,
-                                        num_splits=1)
+                                        num_splits=1, relayout=layout == "contiguous")
     ref, ref_lse = oracle_chunk(q, k, v, past, scale)
     e, el = max_err(out, ref), max_err(lse, ref_lse)
     log(f"  max err {e:.3e}  lse err {el:.2e}")
@@ -152,6 +155,8 @@ SPLIT_CASES = [
     (33, 3000, 16, 16, 64, 64, "paged", "bf16", "bf16", 3),
     (80, 2100, 8, 4, 192, 128, "paged", "bf16", "bf16", 2),
     (50, 1500, 6, 2, 192, 128, "contiguous", "bf16", "bf16", 4),
+    (50, 1500, 6, 2, 192, 128, "contiguous-direct", "bf16", "bf16", 4),
+    (90, 2200, 16, 4, 128, 128, "contiguous", "bf16", "f32", 3),
     (100, 2500, 16, 4, 128, 128, "paged", "bf16", "f32", 5),
     (40, 1200, 8, 8, 64, 64, "contiguous", "f32", "f32", 3),
 ]
@@ -159,7 +164,9 @@ SPLIT_CASES = [
 
 @pytest.mark.parametrize("c,past,hq,hkv,d,dv,layout,dtype,odtype,splits", SPLIT_CASES)
 def test_split_kv_dims_layouts_dtypes(c, past, hq, hkv, d, dv, layout, dtype, odtype, splits):
-    """Forced key splits for every head-dim pair, both cache layouts and every dtype pair."""
+    """Forced key splits for every head-dim pair, both cache layouts (a bf16 contiguous cache both
+    re-laid for the paged kernel, its partials after the copy in the workspace, and read in place)
+    and every dtype pair."""
     seed = 3000 + c + d + splits
     n = past + c
     k, v = seq_kv(n, hkv, d, dv, dtype, seed)
@@ -176,7 +183,8 @@ def test_split_kv_dims_layouts_dtypes(c, past, hq, hkv, d, dv, layout, dtype, od
         kc = torch.full((cap, hkv, d), float("nan"), dtype=torch_dtype(dtype))
         vc = torch.full((cap, hkv, dv), float("nan"), dtype=torch_dtype(dtype))
         kc[:n], vc[:n] = k, v
-        out, lse = L.chunk_prefill_attn(q.cuda(), kc.cuda(), vc.cuda(), past, scale, **kw)
+        out, lse = L.chunk_prefill_attn(q.cuda(), kc.cuda(), vc.cuda(), past, scale,
+                                        relayout=layout == "contiguous", **kw)
     ref, ref_lse = oracle_chunk(q, k, v, past, scale)
     e, el = max_err(out, ref), max_err(lse, ref_lse)
     log(f"  max err {e:.3e}  lse err {el:.2e}")
@@ -192,15 +200,19 @@ def _paged_run(q, pool, table, past, d, **kw):
 
 
 def test_paged_matches_contiguous():
-    """The paged-pool kernel (16x16x32 MFMAs) and the contiguous-cache kernel (32x32x16) sum in
-    different fp32 orders, so their bf16 outputs may differ where a value sits at a rounding edge:
-    by at most 2 bf16 units in the last place (unit 2^-7 relative), on a small fraction of elements."""
+    """A bf16 contiguous cache re-laid into the workspace runs the paged kernel: bitwise the paged
+    result.  Read in place (no room to re-lay), the contiguous kernel (32x32x16 MFMAs) sums in a
+    different fp32 order from the paged one (16x16x32), so bf16 outputs may differ where a value sits
+    at a rounding edge: by at most 2 units in the last place (unit 2^-7 relative), on few elements."""
     c, past, hq, hkv, d = 160, 390, 16, 4, 128
     k, v = seq_kv(past + c, hkv, d, d, "bf16", 101)
     q = inputs.normal((c, hq, d), 102, "bf16").cuda()
     pool, table = single_seq_pool(k, v, 103)
-    a = _paged_run(q, pool, table, past, d, num_splits=1).float()
-    b = L.chunk_prefill_attn(q, k.cuda(), v.cuda(), past, 1 / math.sqrt(d), num_splits=1).float()
+    a = _paged_run(q, pool, table, past, d, num_splits=1)
+    r = L.chunk_prefill_attn(q, k.cuda(), v.cuda(), past, 1 / math.sqrt(d), num_splits=1)
+    assert torch.equal(a.view(torch.int16), r.view(torch.int16))
+    a = a.float()
+    b = L.chunk_prefill_attn(q, k.cuda(), v.cuda(), past, 1 / math.sqrt(d), num_splits=1, relayout=False).float()
     diff = (a - b).abs()
     ulp = torch.exp2(torch.floor(torch.log2(torch.maximum(a.abs(), b.abs()).clamp_min(2.0 ** -126))) - 7)
     same = (diff == 0).float().mean().item()
