@@ -114,6 +114,21 @@ def varlen(q=FAKE, cu=(0, 1, 2), kv=(10, 20), hq=8, hkv=2, d=128, dv=128, ws=FAK
                                      scale, out, None, ws, ws_bytes, None)
 
 
+def test_contiguous_workspace_query():
+    """Re-layout room for a bf16 contiguous cache: an identity block table (256-byte aligned) plus
+    K and V pools of ceil(kv_len / 64) blocks, then the split partials."""
+    past, c, hq, hkv, d = 1000, 100, 8, 2, 128
+    blocks = -(-(past + c) // 64)
+    relay = -(-blocks * 4 // 256) * 256 + blocks * hkv * (d + d) * 64 * 2
+    assert L.chunkattn_prefill_contiguous_workspace_size(past, c, hq, hkv, d, d, 1) == relay
+    assert (L.chunkattn_prefill_contiguous_workspace_size(past, c, hq, hkv, d, d, 3)
+            == relay + L.chunkattn_prefill_workspace_size(c, hq, d, 3))
+    # head-dim pairs the paged kernel does not take get no re-layout room
+    assert L.chunkattn_prefill_contiguous_workspace_size(past, c, hq, hkv, 96, 96, 1) == 0
+    assert L.chunkattn_prefill_contiguous_workspace_size(past, 0, hq, hkv, d, d, 1) == 0
+    assert L.chunkattn_prefill_contiguous_workspace_size(past, c, 8, 3, d, d, 1) == 0
+
+
 @pytest.mark.parametrize("kwargs,status", [
     (dict(k=None), L.CA_EINVAL),
     (dict(q=None), L.CA_EINVAL),
