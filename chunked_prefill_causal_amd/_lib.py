@@ -46,7 +46,9 @@ class PrefillOpts(ctypes.Structure):
                 ("block_table", ctypes.c_void_p), ("block_table_len", ctypes.c_int32),
                 ("num_blocks", ctypes.c_int32), ("lse_out", ctypes.c_void_p),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
-                ("num_splits", ctypes.c_int32)]
+                ("num_splits", ctypes.c_int32), ("k_stride_tok", ctypes.c_int64),
+                ("k_stride_head", ctypes.c_int64), ("v_stride_tok", ctypes.c_int64),
+                ("v_stride_head", ctypes.c_int64)]
 
 
 ALP_FEATURES = 4
@@ -249,7 +251,9 @@ def chunk_prefill_attn(q, k_cache, v_cache, past_len: int, scale: float | None =
 
     ``q`` is ``[chunk_len, heads, head_dim]``.  Contiguous caches are
     ``[capacity, kv_heads, head_dim(_v)]``; paged pools come from
-    :func:`paged_pool` with ``block_table`` an int32 device tensor.  For a
+    :func:`paged_pool` with ``block_table`` an int32 device tensor.  A
+    contiguous cache may be a strided view (e.g. K and V sliced out of a
+    fused QKV tensor) as long as its last dim is dense.  For a
     bf16 contiguous cache the workspace allocated here has room for the
     library to re-lay the prefix for the paged kernel (``relayout=False``
     sizes it for split partials only, so the cache is read in place).
@@ -297,6 +301,12 @@ def chunk_prefill_attn(q, k_cache, v_cache, past_len: int, scale: float | None =
         o.num_blocks = nb if num_blocks is None else num_blocks
     else:
         o.kv_capacity = k_cache.shape[0] if kv_capacity is None else kv_capacity
+        for t, name in ((k_cache, "k"), (v_cache, "v")):
+            if t.stride(2) != 1:
+                raise ValueError(f"{name}_cache: the head dim must be dense")
+            if not t.is_contiguous():
+                setattr(o, f"{name}_stride_tok", t.stride(0))
+                setattr(o, f"{name}_stride_head", t.stride(1))
     o.lse_out = _ptr(lse)
     if workspace is not None:
         o.workspace = _ptr(workspace)

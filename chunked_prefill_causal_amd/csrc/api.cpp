@@ -290,6 +290,19 @@ ca_status chunk_prefill_attn(const void* q, const void* k, const void* v, int64_
     if (cap < kv_len) return fail(CA_ERANGE, "kv_capacity %lld < past_len + chunk_len %lld", (long long)cap,
                                   (long long)kv_len);
   }
+  // Contiguous-cache strides in elements (0 = dense); 16-byte multiples keep every load aligned.
+  if (paged && (o.k_stride_tok || o.k_stride_head || o.v_stride_tok || o.v_stride_head))
+    return fail(CA_EINVAL, "cache strides apply to the contiguous layout only");
+  const int64_t ks_tok = o.k_stride_tok ? o.k_stride_tok : (int64_t)kv_heads * head_dim;
+  const int64_t ks_head = o.k_stride_head ? o.k_stride_head : head_dim;
+  const int64_t vs_tok = o.v_stride_tok ? o.v_stride_tok : (int64_t)kv_heads * dv;
+  const int64_t vs_head = o.v_stride_head ? o.v_stride_head : dv;
+  {
+    const int64_t x = din == DType::BF16 ? 8 : 4;
+    if (ks_tok <= 0 || ks_head <= 0 || vs_tok <= 0 || vs_head <= 0 || ks_tok % x || ks_head % x || vs_tok % x ||
+        vs_head % x)
+      return fail(CA_EINVAL, "cache strides must be positive multiples of 16 bytes (%lld elements)", (long long)x);
+  }
   if (o.num_splits < 0) return fail(CA_EINVAL, "num_splits must be >= 0");
 
   const int group = heads / kv_heads;
@@ -339,6 +352,10 @@ ca_status chunk_prefill_attn(const void* q, const void* k, const void* v, int64_
   a.chunk_len = chunk_len;
   a.kv_len = kv_len;
   a.lse_stride = chunk_len;
+  a.k_stride_tok = ks_tok;
+  a.k_stride_head = ks_head;
+  a.v_stride_tok = vs_tok;
+  a.v_stride_head = vs_head;
   a.heads = heads;
   a.kv_heads = kv_heads;
   a.group = group;
@@ -361,7 +378,8 @@ ca_status chunk_prefill_attn(const void* q, const void* k, const void* v, int64_
     void* vpool = (char*)o.workspace + rl.table + rl.k;
     hipError_t e = launch_block_iota(table, (int)rl.blocks, s);
     if (e == hipSuccess)
-      e = launch_kv_append(DType::BF16, head_dim, dv, k, v, 0, kv_len, kv_heads, table, (int)rl.blocks, kpool, vpool, s);
+      e = launch_kv_append(DType::BF16, head_dim, dv, k, v, ks_tok, ks_head, vs_tok, vs_head, 0, kv_len, kv_heads,
+                           table, (int)rl.blocks, kpool, vpool, s);
     if (e != hipSuccess) return hip_status(e, "contiguous cache re-layout");
     a.k = kpool;
     a.v = vpool;
@@ -508,7 +526,8 @@ ca_status chunkattn_kv_append(const void* k_new, const void* v_new, int64_t star
     return fail(CA_ERANGE, "block table covers %lld tokens, need %lld", (long long)block_table_len * kBlock,
                 (long long)(start_pos + n_tokens));
   if (n_tokens == 0) return ok();
-  hipError_t e = launch_kv_append((DType)dtype, head_dim, head_dim_v, k_new, v_new, start_pos, n_tokens, kv_heads,
+  hipError_t e = launch_kv_append((DType)dtype, head_dim, head_dim_v, k_new, v_new, (int64_t)kv_heads * head_dim,
+                                  head_dim, (int64_t)kv_heads * head_dim_v, head_dim_v, start_pos, n_tokens, kv_heads,
                                   block_table, num_blocks, k_pool, v_pool, (hipStream_t)stream);
   return hip_status(e, "kv_append launch");
 }

@@ -17,6 +17,7 @@ namespace chunkattn {
 
 template <typename E>
 __global__ __launch_bounds__(256) void kv_append_kernel(const E* __restrict__ k_new, const E* __restrict__ v_new,
+                                                       int64_t k_tok, int64_t k_head, int64_t v_tok, int64_t v_head,
                                                        int64_t start_pos, int64_t n_tokens, int kv_heads,
                                                        int D, int DV, const int32_t* __restrict__ block_table,
                                                        int num_blocks, E* __restrict__ k_pool,
@@ -33,7 +34,7 @@ __global__ __launch_bounds__(256) void kv_append_kernel(const E* __restrict__ k_
       const int64_t tok = start_pos + tg / kv_heads;
       const int64_t phys = clamp_block(block_table[tok / kBlock], num_blocks);
       const int slot = (int)(tok % kBlock);
-      const u32x4_t v = *(const u32x4_t*)(k_new + tg * D + dc * X);
+      const u32x4_t v = *(const u32x4_t*)(k_new + (tg / kv_heads) * k_tok + g * k_head + dc * X);
       *(u32x4_t*)(k_pool + (((phys * kv_heads + g) * (D / X) + dc) * kBlock + slot) * X) = v;
     } else {
       const int64_t e = idx - nk;
@@ -43,7 +44,8 @@ __global__ __launch_bounds__(256) void kv_append_kernel(const E* __restrict__ k_
       const int64_t tok = start_pos + tg / kv_heads;
       const int64_t phys = clamp_block(block_table[tok / kBlock], num_blocks);
       const int slot = (int)(tok % kBlock);
-      v_pool[(((phys * kv_heads + g) * (kBlock / X) + slot / X) * DV + dv) * X + slot % X] = v_new[tg * DV + dv];
+      v_pool[(((phys * kv_heads + g) * (kBlock / X) + slot / X) * DV + dv) * X + slot % X] =
+          v_new[(tg / kv_heads) * v_tok + g * v_head + dv];
     }
   }
 }
@@ -63,7 +65,8 @@ hipError_t launch_block_iota(int32_t* table, int n, hipStream_t stream) {
 
 // bf16 V by 8-token runs (see the header comment).  Work item: (run, head,
 // value pair), value pair fastest.
-__global__ __launch_bounds__(256) void kv_append_v_bf16_kernel(const uint16_t* __restrict__ v_new, int64_t start_pos,
+__global__ __launch_bounds__(256) void kv_append_v_bf16_kernel(const uint16_t* __restrict__ v_new, int64_t v_tok,
+                                                               int64_t v_head, int64_t start_pos,
                                                                int64_t n_tokens, int kv_heads, int DV,
                                                                const int32_t* __restrict__ block_table,
                                                                int num_blocks, uint16_t* __restrict__ v_pool) {
@@ -72,7 +75,6 @@ __global__ __launch_bounds__(256) void kv_append_v_bf16_kernel(const uint16_t* _
   const int pairs = DV / 2;
   const int64_t items = (run1 - run0 + 1) * kv_heads * pairs;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  const int64_t row = (int64_t)kv_heads * DV;                 // elements per token in v_new
   for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < items; idx += stride) {
     const int dp = (int)(idx % pairs);
     const int64_t rg = idx / pairs;
@@ -82,10 +84,10 @@ __global__ __launch_bounds__(256) void kv_append_v_bf16_kernel(const uint16_t* _
     const int64_t phys = clamp_block(block_table[tok0 / kBlock], num_blocks);
     uint16_t* dst = v_pool + (((phys * kv_heads + g) * (kBlock / X) + (tok0 % kBlock) / X) * DV + 2 * dp) * X;
     if (tok0 >= start_pos && tok0 + X <= start_pos + n_tokens) {
-      const uint32_t* src = (const uint32_t*)(v_new + (tok0 - start_pos) * row + g * DV + 2 * dp);
+      const uint32_t* src = (const uint32_t*)(v_new + (tok0 - start_pos) * v_tok + g * v_head + 2 * dp);
       uint32_t w[X];
 #pragma unroll
-      for (int t = 0; t < X; ++t) w[t] = src[t * (row / 2)];
+      for (int t = 0; t < X; ++t) w[t] = src[t * (v_tok / 2)];
       u32x4_t lo, hi;                                         // value 2dp, value 2dp + 1 of tokens 0..7
 #pragma unroll
       for (int t = 0; t < X / 2; ++t) {
@@ -98,7 +100,7 @@ __global__ __launch_bounds__(256) void kv_append_v_bf16_kernel(const uint16_t* _
       for (int t = 0; t < X; ++t) {
         const int64_t tok = tok0 + t;
         if (tok < start_pos || tok >= start_pos + n_tokens) continue;
-        const uint16_t* src = v_new + (tok - start_pos) * row + g * DV + 2 * dp;
+        const uint16_t* src = v_new + (tok - start_pos) * v_tok + g * v_head + 2 * dp;
         dst[t] = src[0];
         dst[X + t] = src[1];
       }
@@ -107,6 +109,7 @@ __global__ __launch_bounds__(256) void kv_append_v_bf16_kernel(const uint16_t* _
 }
 
 hipError_t launch_kv_append(DType dt, int D, int DV, const void* k_new, const void* v_new,
+                            int64_t k_tok, int64_t k_head, int64_t v_tok, int64_t v_head,
                             int64_t start_pos, int64_t n_tokens, int kv_heads,
                             const int32_t* block_table, int num_blocks, void* k_pool, void* v_pool,
                             hipStream_t stream) {
@@ -116,16 +119,16 @@ hipError_t launch_kv_append(DType dt, int D, int DV, const void* k_new, const vo
   };
   if (dt == DType::BF16) {
     hipLaunchKernelGGL(kv_append_kernel<uint16_t>, dim3(grid_for(n_tokens * kv_heads * (int64_t)(D / 8))), dim3(256), 0,
-                       stream, (const uint16_t*)k_new, (const uint16_t*)v_new, start_pos, n_tokens, kv_heads, D, DV,
-                       block_table, num_blocks, (uint16_t*)k_pool, (uint16_t*)v_pool, false);
+                       stream, (const uint16_t*)k_new, (const uint16_t*)v_new, k_tok, k_head, v_tok, v_head, start_pos,
+                       n_tokens, kv_heads, D, DV, block_table, num_blocks, (uint16_t*)k_pool, (uint16_t*)v_pool, false);
     const int64_t runs = (start_pos + n_tokens - 1) / 8 - start_pos / 8 + 1;
     hipLaunchKernelGGL(kv_append_v_bf16_kernel, dim3(grid_for(runs * kv_heads * (DV / 2))), dim3(256), 0, stream,
-                       (const uint16_t*)v_new, start_pos, n_tokens, kv_heads, DV, block_table, num_blocks,
-                       (uint16_t*)v_pool);
+                       (const uint16_t*)v_new, v_tok, v_head, start_pos, n_tokens, kv_heads, DV, block_table,
+                       num_blocks, (uint16_t*)v_pool);
   } else {
     hipLaunchKernelGGL(kv_append_kernel<float>, dim3(grid_for(n_tokens * kv_heads * (int64_t)(D + DV))), dim3(256), 0,
-                       stream, (const float*)k_new, (const float*)v_new, start_pos, n_tokens, kv_heads, D, DV,
-                       block_table, num_blocks, (float*)k_pool, (float*)v_pool, true);
+                       stream, (const float*)k_new, (const float*)v_new, k_tok, k_head, v_tok, v_head, start_pos,
+                       n_tokens, kv_heads, D, DV, block_table, num_blocks, (float*)k_pool, (float*)v_pool, true);
   }
   return hipGetLastError();
 }

@@ -28,6 +28,8 @@ struct PrefillArgs {
   int64_t chunk_len;
   int64_t kv_len;            // past_len + chunk_len
   int64_t lse_stride;
+  int64_t k_stride_tok, k_stride_head;   // contiguous cache, in elements (always set)
+  int64_t v_stride_tok, v_stride_head;
   int32_t heads, kv_heads, group;
   int32_t num_blocks;
   int32_t hpw;               // query heads per workgroup (1/2/4; paged bf16 path 1/2/4/8)
@@ -128,7 +130,9 @@ hipError_t launch_mla_decode(bool fp8, const MlaArgs& a, hipStream_t stream);
 hipError_t launch_mla_append(bool fp8, const MlaAppendArgs& a, hipStream_t stream);
 
 hipError_t launch_block_iota(int32_t* table, int n, hipStream_t stream);
+// k_new / v_new: element (t, g, e) at t * *_tok + g * *_head + e (dense: kv_heads * D, D).
 hipError_t launch_kv_append(DType dt, int D, int DV, const void* k_new, const void* v_new,
+                            int64_t k_tok, int64_t k_head, int64_t v_tok, int64_t v_head,
                             int64_t start_pos, int64_t n_tokens, int kv_heads,
                             const int32_t* block_table, int num_blocks, void* k_pool, void* v_pool,
                             hipStream_t stream);

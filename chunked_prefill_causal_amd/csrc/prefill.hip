@@ -200,7 +200,7 @@ __global__ __launch_bounds__(256, sizeof(E) == 2 ? 2 : 1) void prefill_kernel(co
         const int tok = cidx / (D / C::X), dc = cidx % (D / C::X);
         const int64_t key = key0 + tok;
         kst[i] = key < kv_len
-                     ? *(const u32x4_t*)(kbase + (key * a.kv_heads + g) * (int64_t)D + dc * C::X)
+                     ? *(const u32x4_t*)(kbase + key * a.k_stride_tok + g * a.k_stride_head + dc * C::X)
                      : u32x4_t{0u, 0u, 0u, 0u};
       }
 #pragma unroll
@@ -209,7 +209,7 @@ __global__ __launch_bounds__(256, sizeof(E) == 2 ? 2 : 1) void prefill_kernel(co
         const int tok = cidx / (DV / C::X), dvc = cidx % (DV / C::X);
         const int64_t key = key0 + tok;
         vst[i] = key < kv_len
-                     ? *(const u32x4_t*)(vbase + (key * a.kv_heads + g) * (int64_t)DV + dvc * C::X)
+                     ? *(const u32x4_t*)(vbase + key * a.v_stride_tok + g * a.v_stride_head + dvc * C::X)
                      : u32x4_t{0u, 0u, 0u, 0u};
       }
     }

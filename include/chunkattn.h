@@ -33,7 +33,8 @@
  *  - Calls are thread-safe; calls that share output or workspace buffers on
  *    one stream are ordered by the stream, on different streams they race.
  *  - Device pointers must be 16-byte aligned.
- *  - All strides are dense; layouts are given per argument below.
+ *  - Strides are dense except where an argument says otherwise (the
+ *    contiguous cache of chunk_prefill_attn); layouts are given per argument.
  *
  * KV cache layouts (B = CA_BLOCK_SIZE = 64 tokens, X = 16 / sizeof(element)):
  *  - CA_KV_CONTIGUOUS: k [capacity, kv_heads, head_dim],
@@ -60,7 +61,7 @@ extern "C" {
 #endif
 
 #define CA_BLOCK_SIZE 64
-#define CHUNKATTN_VERSION 1
+#define CHUNKATTN_VERSION 2
 
 typedef enum {
   CA_OK = 0,
@@ -98,6 +99,15 @@ typedef struct ca_prefill_opts {
                                   given; no workspace => no split); 1 = never
                                   split; > 1 = exactly this many key splits
                                   (capped at the number of key tiles) */
+  int64_t k_stride_tok;        /* contiguous only, in elements: K[t, g, e] is at
+                                  k_cache + t * k_stride_tok + g * k_stride_head + e;
+                                  0 = dense (kv_heads * head_dim, head_dim).  Both
+                                  must be multiples of 16 bytes (8 bf16 / 4 fp32
+                                  elements), e.g. K and V as views into a fused
+                                  QKV projection output. */
+  int64_t k_stride_head;
+  int64_t v_stride_tok;        /* the same for V (dense: kv_heads * head_dim_v, head_dim_v) */
+  int64_t v_stride_head;
 } ca_prefill_opts;
 
 void ca_prefill_opts_init(ca_prefill_opts* opts);

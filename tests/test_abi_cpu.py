@@ -7,6 +7,7 @@ must fail before a single byte of device memory is touched.
 import ctypes
 import os
 import re
+import subprocess
 
 import pytest
 
@@ -35,13 +36,28 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_defaults():
-    assert L.version() == 1
+    assert L.version() == 2
     o = L.PrefillOpts()
     o.num_splits = 7
     L.lib().ca_prefill_opts_init(ctypes.byref(o))
     assert (o.dtype, o.out_dtype, o.kv_layout, o.num_splits, o.head_dim_v) == (L.CA_BF16, L.CA_BF16,
                                                                                 L.CA_KV_CONTIGUOUS, 0, 0)
-    assert ctypes.sizeof(L.PrefillOpts) == 72
+    assert ctypes.sizeof(L.PrefillOpts) == 104
+
+
+def test_options_struct_matches_the_header(tmp_path):
+    """The ctypes mirror of ca_prefill_opts has the size and field offsets the C header gives."""
+    fields = [f for f, _ in L.PrefillOpts._fields_]
+    src = tmp_path / "probe.c"
+    src.write_text('#include <stddef.h>\n#include <stdio.h>\n#include "chunkattn.h"\nint main(void) {\n'
+                   '  printf("%zu", sizeof(ca_prefill_opts));\n'
+                   + "".join(f'  printf(" %zu", offsetof(ca_prefill_opts, {f}));\n' for f in fields)
+                   + "  return 0;\n}\n")
+    exe = tmp_path / "probe"
+    subprocess.run(["gcc", "-std=c11", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split()]
+    assert got[0] == ctypes.sizeof(L.PrefillOpts)
+    assert got[1:] == [getattr(L.PrefillOpts, f).offset for f in fields]
 
 
 def prefill(q=FAKE, k=FAKE, v=FAKE, past=0, c=4, hq=8, hkv=8, d=128, scale=0.1, out=FAKE, opts=None):
@@ -74,6 +90,11 @@ def opts(**kw):
     (dict(opts=opts(dtype=7)), L.CA_EINVAL),
     (dict(opts=opts(kv_layout=9)), L.CA_EINVAL),
     (dict(opts=opts(kv_capacity=3)), L.CA_ERANGE),
+    (dict(opts=opts(k_stride_tok=1028)), L.CA_EINVAL),                   # not a 16-byte multiple (bf16)
+    (dict(opts=opts(v_stride_head=-8)), L.CA_EINVAL),
+    (dict(opts=opts(dtype=L.CA_F32, out_dtype=L.CA_F32, k_stride_head=130)), L.CA_EINVAL),
+    (dict(opts=opts(kv_layout=L.CA_KV_PAGED, block_table=FAKE, block_table_len=1, num_blocks=4,
+                    k_stride_tok=2048)), L.CA_EINVAL),                   # strides are contiguous-only
     (dict(past=(1 << 30), c=1), L.CA_ERANGE),
     (dict(opts=opts(kv_layout=L.CA_KV_PAGED)), L.CA_EINVAL),            # no block table
     (dict(opts=opts(kv_layout=L.CA_KV_PAGED, block_table=FAKE, block_table_len=1, num_blocks=4), past=61),

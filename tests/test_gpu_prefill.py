@@ -313,3 +313,44 @@ def test_late_max_growth(d, dv, splits):
     log(f"late max growth d={d}/{dv} splits={splits}: max err {e:.3e}, lse err {el:.2e}")
     assert torch.isfinite(out.float()).all()
     assert e <= BF16_TOL and el <= LSE_TOL
+
+
+@pytest.mark.parametrize("relayout", [True, False])
+def test_strided_cache_views_of_fused_qkv(relayout):
+    """K and V as views into one fused [tokens, Hq + 2 Hkv, d] projection output (token stride
+    (Hq + 2 Hkv) d, head stride d), read both re-laid for the paged kernel and in place."""
+    c, past, hq, hkv, d = 150, 333, 16, 4, 128
+    n = past + c
+    qkv = inputs.normal((n, hq + 2 * hkv, d), 151, "bf16")
+    k, v = qkv[:, hq:hq + hkv], qkv[:, hq + hkv:]
+    q = qkv[past:, :hq].contiguous()
+    qkv_d = qkv.cuda()
+    kd, vd = qkv_d[:, hq:hq + hkv], qkv_d[:, hq + hkv:]
+    assert not kd.is_contiguous()
+    scale = 1 / math.sqrt(d)
+    out, lse = L.chunk_prefill_attn(q.cuda(), kd, vd, past, scale, return_lse=True, num_splits=1,
+                                    relayout=relayout)
+    ref, ref_lse = oracle_chunk(q, k.contiguous(), v.contiguous(), past, scale)
+    e, el = max_err(out, ref), max_err(lse, ref_lse)
+    log(f"fused-QKV cache views (relayout={relayout}): max err {e:.3e}, lse err {el:.2e}")
+    assert e <= BF16_TOL and el <= LSE_TOL
+
+
+@pytest.mark.parametrize("relayout,splits", [(True, 3), (False, 2)])
+def test_strided_cache_padded_heads(relayout, splits):
+    """A d=192 key cache whose heads are padded to 256 elements (head stride 256, token stride
+    Hkv * 256) beside a dense d_v=128 value cache, with forced key splits."""
+    c, past, hq, hkv, d, dv = 90, 1400, 8, 2, 192, 128
+    n = past + c
+    kbuf = inputs.normal((n, hkv, 256), 161, "bf16")
+    k = kbuf[:, :, :d]
+    v = inputs.normal((n, hkv, dv), 162, "bf16")
+    q = inputs.normal((c, hq, d), 163, "bf16")
+    kd = kbuf.cuda()[:, :, :d]
+    scale = 1 / math.sqrt(d)
+    out, lse = L.chunk_prefill_attn(q.cuda(), kd, v.cuda(), past, scale, return_lse=True, num_splits=splits,
+                                    relayout=relayout)
+    ref, ref_lse = oracle_chunk(q, k.contiguous(), v, past, scale)
+    e, el = max_err(out, ref), max_err(lse, ref_lse)
+    log(f"padded-head K cache (relayout={relayout}, splits={splits}): max err {e:.3e}, lse err {el:.2e}")
+    assert e <= BF16_TOL and el <= LSE_TOL
