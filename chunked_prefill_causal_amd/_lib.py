@@ -86,7 +86,8 @@ def lib() -> ctypes.CDLL:
     L.chunk_attn_varlen.restype = ctypes.c_int
     L.chunkattn_varlen_workspace_size.argtypes = [vp, vp, i32, i32, i32, i32]
     L.chunkattn_varlen_workspace_size.restype = sz
-    L.chunkattn_kv_append.argtypes = [vp, vp, i64, i64, i32, i32, i32, ctypes.c_int, vp, i32, i32, vp, vp, vp]
+    L.chunkattn_kv_append.argtypes = [vp, vp, i64, i64, i32, i32, i32, ctypes.c_int, vp, i32, i32, vp, vp,
+                                      ctypes.POINTER(ctypes.c_int64), vp]
     L.chunkattn_kv_append.restype = ctypes.c_int
     f64 = ctypes.c_double
     L.chunkattn_sched_simulate.argtypes = [i32, i32, vp, vp, f64, i32, vp, vp, vp, vp]
@@ -363,13 +364,20 @@ def chunk_attn_varlen(q, k_pool, v_pool, block_tables, cu_seqlens_q, kv_lens, sc
 
 def chunkattn_kv_append(k_new, v_new, start_pos: int, block_table, k_pool, v_pool, *, num_blocks: int | None = None,
                         stream=None) -> None:
-    """Write ``k_new [n, kv_heads, d]`` / ``v_new [n, kv_heads, dv]`` at positions start_pos.."""
+    """Write ``k_new [n, kv_heads, d]`` / ``v_new [n, kv_heads, dv]`` at positions start_pos..
+
+    Either may be a strided view (e.g. sliced out of a fused QKV tensor) with a dense last dim."""
     n, hkv, d = k_new.shape
     dv = v_new.shape[2]
+    strides = None
+    if not (k_new.is_contiguous() and v_new.is_contiguous()):
+        if k_new.stride(2) != 1 or v_new.stride(2) != 1:
+            raise ValueError("k_new / v_new: the head dim must be dense")
+        strides = (ctypes.c_int64 * 4)(k_new.stride(0), k_new.stride(1), v_new.stride(0), v_new.stride(1))
     _check(lib().chunkattn_kv_append(_ptr(k_new), _ptr(v_new), start_pos, n, hkv, d, dv, _dtype_code(k_new.dtype),
                                      _ptr(block_table), block_table.numel(),
                                      k_pool.shape[0] if num_blocks is None else num_blocks,
-                                     _ptr(k_pool), _ptr(v_pool), _stream(stream)))
+                                     _ptr(k_pool), _ptr(v_pool), strides, _stream(stream)))
 
 
 def chunkattn_mla_block_bytes(fmt: int) -> int:

@@ -511,7 +511,7 @@ ca_status chunk_attn_varlen(const void* q, const void* k_pool, const void* v_poo
 ca_status chunkattn_kv_append(const void* k_new, const void* v_new, int64_t start_pos, int64_t n_tokens,
                               int32_t kv_heads, int32_t head_dim, int32_t head_dim_v, ca_dtype dtype,
                               const int32_t* block_table, int32_t block_table_len, int32_t num_blocks, void* k_pool,
-                              void* v_pool, void* stream) {
+                              void* v_pool, const int64_t* src_strides, void* stream) {
   if (!k_new || !v_new || !block_table || !k_pool || !v_pool) return fail(CA_EINVAL, "null pointer argument");
   if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) ||
       !aligned(block_table, 4))
@@ -525,9 +525,18 @@ ca_status chunkattn_kv_append(const void* k_new, const void* v_new, int64_t star
   if (start_pos + n_tokens > (int64_t)block_table_len * kBlock)
     return fail(CA_ERANGE, "block table covers %lld tokens, need %lld", (long long)block_table_len * kBlock,
                 (long long)(start_pos + n_tokens));
+  int64_t st[4] = {(int64_t)kv_heads * head_dim, head_dim, (int64_t)kv_heads * head_dim_v, head_dim_v};
+  if (src_strides) {
+    for (int i = 0; i < 4; ++i) {
+      if (src_strides[i] <= 0 || src_strides[i] % x)
+        return fail(CA_EINVAL, "src_strides[%d] = %lld must be a positive multiple of %d elements", i,
+                    (long long)src_strides[i], x);
+      st[i] = src_strides[i];
+    }
+  }
   if (n_tokens == 0) return ok();
-  hipError_t e = launch_kv_append((DType)dtype, head_dim, head_dim_v, k_new, v_new, (int64_t)kv_heads * head_dim,
-                                  head_dim, (int64_t)kv_heads * head_dim_v, head_dim_v, start_pos, n_tokens, kv_heads,
+  hipError_t e = launch_kv_append((DType)dtype, head_dim, head_dim_v, k_new, v_new, st[0], st[1], st[2], st[3],
+                                  start_pos, n_tokens, kv_heads,
                                   block_table, num_blocks, k_pool, v_pool, (hipStream_t)stream);
   return hip_status(e, "kv_append launch");
 }

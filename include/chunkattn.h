@@ -34,7 +34,8 @@
  *    one stream are ordered by the stream, on different streams they race.
  *  - Device pointers must be 16-byte aligned.
  *  - Strides are dense except where an argument says otherwise (the
- *    contiguous cache of chunk_prefill_attn); layouts are given per argument.
+ *    contiguous cache of chunk_prefill_attn, the new tokens of
+ *    chunkattn_kv_append); layouts are given per argument.
  *
  * KV cache layouts (B = CA_BLOCK_SIZE = 64 tokens, X = 16 / sizeof(element)):
  *  - CA_KV_CONTIGUOUS: k [capacity, kv_heads, head_dim],
@@ -215,12 +216,16 @@ size_t chunkattn_varlen_workspace_size(const int32_t* cu_seqlens_q_host, const i
  * (the cache write that precedes each chunk's attention, VPP review §2.3).
  *   k_new [n_tokens, kv_heads, head_dim], v_new [n_tokens, kv_heads, head_dim_v]
  *   block_table [block_table_len] device int32, covering start_pos + n_tokens.
+ *   src_strides: NULL for dense k_new / v_new, else a host array {k token,
+ *   k head, v token, v head} of element strides (element (t, g, e) of k_new at
+ *   t * src_strides[0] + g * src_strides[1] + e), each a positive multiple of
+ *   16 bytes: e.g. the new tokens' K and V as views into a fused QKV output.
  * Bitwise copy; no arithmetic.  Block ids are clamped to [0, num_blocks).
  */
 ca_status chunkattn_kv_append(const void* k_new, const void* v_new, int64_t start_pos, int64_t n_tokens,
                               int32_t kv_heads, int32_t head_dim, int32_t head_dim_v, ca_dtype dtype,
                               const int32_t* block_table, int32_t block_table_len, int32_t num_blocks,
-                              void* k_pool, void* v_pool, void* stream);
+                              void* k_pool, void* v_pool, const int64_t* src_strides, void* stream);
 
 /*
  * Pipeline schedules that chunked prefill feeds (host only: no GPU work, no

@@ -177,13 +177,17 @@ def test_kv_append_rejections():
     lib = L.lib()
     f = lambda **kw: lib.chunkattn_kv_append(kw.get("k", FAKE), FAKE, kw.get("start", 0), kw.get("n", 10), 2,
                                              kw.get("d", 128), 128, kw.get("dt", L.CA_BF16), FAKE,
-                                             kw.get("tl", 1), 4, FAKE, FAKE, None)
+                                             kw.get("tl", 1), 4, FAKE, FAKE, kw.get("st"), None)
+    strides = lambda *v: (ctypes.c_int64 * 4)(*v)
     assert f(k=None) == L.CA_EINVAL
     assert f(start=-1) == L.CA_EINVAL
     assert f(d=100) == L.CA_EUNSUPPORTED
     assert f(dt=5) == L.CA_EINVAL
     assert f(start=60, n=10) == L.CA_ERANGE
     assert f(n=0) == L.CA_OK
+    assert f(n=0, st=strides(2048, 128, 2048, 128)) == L.CA_OK
+    assert f(st=strides(2048, 128, 2052, 128)) == L.CA_EINVAL        # not a 16-byte multiple
+    assert f(st=strides(2048, 0, 2048, 128)) == L.CA_EINVAL
 
 
 def test_mla_block_bytes_follow_the_per_token_record():

@@ -58,6 +58,26 @@ def test_kv_append_layout_bitwise(dtype):
     assert torch.isnan(kp[last, :, :, n % 64:, :].float()).all()
 
 
+@pytest.mark.parametrize("d,dv", [(128, 128), (192, 128)])
+def test_kv_append_from_fused_qkv_views_bitwise(d, dv):
+    """New tokens' K and V given as strided views (K, V sliced out of one fused projection
+    buffer) land bit for bit where a dense copy of them does: unaligned start, partial last run."""
+    hkv, n, start = 2, 203, 37
+    buf = inputs.normal((n, hkv * (d + dv) + 64), 171 + d, "bf16").cuda()   # 64 spare columns
+    k = buf[:, : hkv * d].view(n, hkv, d)
+    v = buf[:, hkv * d: hkv * (d + dv)].view(n, hkv, dv)
+    assert not k.is_contiguous() and not v.is_contiguous()
+    needed = math.ceil((start + n) / 64)
+    table = torch.from_numpy(inputs.block_table(needed, 172)).cuda()
+    a = Pool(inputs.pool_size(needed), hkv, d, dv, torch.bfloat16, poison=True)
+    b = Pool(inputs.pool_size(needed), hkv, d, dv, torch.bfloat16, poison=True)
+    L.chunkattn_kv_append(k, v, start, table, a.k, a.v)
+    L.chunkattn_kv_append(k.contiguous(), v.contiguous(), start, table, b.k, b.v)
+    torch.cuda.synchronize()
+    assert torch.equal(a.k.view(torch.int16), b.k.view(torch.int16))
+    assert torch.equal(a.v.view(torch.int16), b.v.view(torch.int16))
+
+
 # ------------------------------------------------------------------ tiny fp32 --
 
 def test_tiny_f32_workload_all_rows():
