@@ -77,7 +77,7 @@ def lib() -> ctypes.CDLL:
     L.chunk_prefill_attn.restype = ctypes.c_int
     L.chunkattn_prefill_workspace_size.argtypes = [i64, i32, i32, i32]
     L.chunkattn_prefill_workspace_size.restype = sz
-    L.chunkattn_prefill_contiguous_workspace_size.argtypes = [i64, i64, i32, i32, i32, i32, i32]
+    L.chunkattn_prefill_contiguous_workspace_size.argtypes = [i64, i64, i32, i32, i32, i32, ctypes.c_int, i32]
     L.chunkattn_prefill_contiguous_workspace_size.restype = sz
     L.chunkattn_prefill_auto_splits.argtypes = [i64, i64, i32, i32]
     L.chunkattn_prefill_auto_splits.restype = i32
@@ -234,9 +234,10 @@ def chunkattn_prefill_workspace_size(chunk_len: int, heads: int, head_dim_v: int
 
 
 def chunkattn_prefill_contiguous_workspace_size(past_len: int, chunk_len: int, heads: int, kv_heads: int,
-                                                head_dim: int, head_dim_v: int, num_splits: int) -> int:
+                                                head_dim: int, head_dim_v: int, num_splits: int,
+                                                dtype: int = CA_BF16) -> int:
     return lib().chunkattn_prefill_contiguous_workspace_size(past_len, chunk_len, heads, kv_heads, head_dim,
-                                                             head_dim_v, num_splits)
+                                                             head_dim_v, dtype, num_splits)
 
 
 def chunkattn_prefill_auto_splits(past_len: int, chunk_len: int, heads: int, kv_heads: int) -> int:
@@ -279,7 +280,8 @@ def chunk_prefill_attn(q, k_cache, v_cache, past_len: int, scale: float | None =
     if return_lse and lse is None:
         lse = torch.empty((heads, c), dtype=torch.float32, device=q.device)
     if workspace is None and not paged and relayout and c > 0:
-        need = chunkattn_prefill_contiguous_workspace_size(past_len, c, heads, hkv, d, dv, num_splits)
+        need = chunkattn_prefill_contiguous_workspace_size(past_len, c, heads, hkv, d, dv, num_splits,
+                                                           _dtype_code(q.dtype))
         if need:
             workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     if num_splits == 0 and workspace is None:

@@ -236,13 +236,13 @@ size_t chunkattn_prefill_workspace_size(int64_t chunk_len, int32_t heads, int32_
 
 size_t chunkattn_prefill_contiguous_workspace_size(int64_t past_len, int64_t chunk_len, int32_t heads,
                                                    int32_t kv_heads, int32_t head_dim, int32_t head_dim_v,
-                                                   int32_t num_splits) {
+                                                   ca_dtype dtype, int32_t num_splits) {
   if (past_len < 0 || chunk_len <= 0 || heads <= 0 || kv_heads <= 0 || heads % kv_heads || head_dim <= 0)
     return 0;
   const int dv = head_dim_v ? head_dim_v : head_dim;
   const int splits = num_splits == 0 ? auto_splits(past_len, chunk_len, heads, kv_heads) : num_splits;
   size_t bytes = prefill_ws_bytes(chunk_len, heads, dv, splits);
-  if (prefill_paged_supported(head_dim, dv) && past_len + chunk_len <= kMaxTokens)
+  if (dtype == CA_BF16 && prefill_paged_supported(head_dim, dv) && past_len + chunk_len <= kMaxTokens)
     bytes += relayout_plan(past_len + chunk_len, kv_heads, head_dim, dv).bytes;
   return bytes;
 }

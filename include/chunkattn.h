@@ -151,14 +151,15 @@ size_t chunkattn_prefill_workspace_size(int64_t chunk_len, int32_t heads, int32_
                                         int32_t num_splits);
 
 /*
- * Workspace bytes chunk_prefill_attn uses with a contiguous cache: the
- * re-laid K/V prefix (bf16 and a paged-kernel head-dim pair; for other
- * dtypes or dims nothing) plus the split partials of `num_splits` splits
- * (0 = the count it would choose).  Returns 0 for invalid sizes.
+ * Workspace bytes chunk_prefill_attn uses with a contiguous cache of element
+ * type `dtype`: the re-laid K/V prefix (CA_BF16 and a paged-kernel head-dim
+ * pair; for other dtypes or dims nothing) plus the split partials of
+ * `num_splits` splits (0 = the count it would choose).  Returns 0 for invalid
+ * sizes.
  */
 size_t chunkattn_prefill_contiguous_workspace_size(int64_t past_len, int64_t chunk_len, int32_t heads,
                                                    int32_t kv_heads, int32_t head_dim, int32_t head_dim_v,
-                                                   int32_t num_splits);
+                                                   ca_dtype dtype, int32_t num_splits);
 
 /*
  * The split count chunk_prefill_attn picks for num_splits = 0 when the

@@ -148,6 +148,10 @@ def test_contiguous_workspace_query():
     assert L.chunkattn_prefill_contiguous_workspace_size(past, c, hq, hkv, 96, 96, 1) == 0
     assert L.chunkattn_prefill_contiguous_workspace_size(past, 0, hq, hkv, d, d, 1) == 0
     assert L.chunkattn_prefill_contiguous_workspace_size(past, c, 8, 3, d, d, 1) == 0
+    # fp32 caches are read in place: split partials only
+    assert L.chunkattn_prefill_contiguous_workspace_size(past, c, hq, hkv, d, d, 1, L.CA_F32) == 0
+    assert (L.chunkattn_prefill_contiguous_workspace_size(past, c, hq, hkv, d, d, 3, L.CA_F32)
+            == L.chunkattn_prefill_workspace_size(c, hq, d, 3))
 
 
 @pytest.mark.parametrize("kwargs,status", [
