@@ -384,6 +384,33 @@ def mla_decode_summary(L, inputs, torch, timed, reps, warmup):
     return res
 
 
+def contiguous_cache_summary(L, loop, torch, timed, reps):
+    """Chunks 3 and 7 read from a bf16 contiguous [tokens, kv_heads, d] cache holding the same logical K/V
+    as the paged pool.  With workspace room the library re-lays the prefix for the paged kernel; that copy
+    is inside the timed call.  The paged pool's time for the same chunk is measured beside it."""
+    w = loop.w
+    last = w.n_chunks - 1
+    ws = torch.empty(L.chunkattn_prefill_contiguous_workspace_size(last * w.chunk_len, w.chunk_len, w.heads,
+                                                                   w.kv_heads, w.head_dim, w.head_dim_v, 0),
+                     dtype=torch.uint8, device="cuda")
+    res = {"chunks": [], "ms": [], "tflops": [], "paged_ms": []}
+    for c in (3, last):
+        past = c * w.chunk_len
+        kc, vc = loop.k_logical[: past + w.chunk_len], loop.v_logical[: past + w.chunk_len]
+        f = lambda: L.chunk_prefill_attn(loop.q[c], kc, vc, past, w.scale, out=loop.out, workspace=ws)
+        f()
+        torch.cuda.synchronize()
+        t = timed(f, reps)
+        tp = timed(lambda: loop.run_chunk(L, c), reps)
+        res["chunks"].append(c)
+        res["ms"].append(round(t, 3))
+        res["tflops"].append(round(loop.flops[c] / (t / 1e3) / 1e12, 1))
+        res["paged_ms"].append(round(tp, 3))
+    res["note"] = ("bf16 contiguous cache re-laid into the workspace (identity block table) and read by the paged "
+                   "kernel; the copy is timed")
+    return res
+
+
 def chunk_latency_stats(L, loop, torch, reps):
     """Each chunk `reps` times (median, p10, p90); then each once cold, after a 512 MiB write evicts the
     caches."""
@@ -657,6 +684,9 @@ def main():
     pre_ms = timed(lambda: pre_only.run(L), args.reps)
     dec_gbps = dec_only.decode_bytes / (dec_ms / 1e3) / 1e9
     log(f"decode-only {dec_ms:.3f} ms = {dec_gbps:.0f} GB/s; mixed prefill-only {pre_ms:.3f} ms")
+    contig = contiguous_cache_summary(L, loop, torch, timed, args.reps)
+    log(f"contiguous cache, chunks {contig['chunks']}: {contig['ms']} ms ({contig['tflops']} TFLOP/s); "
+        f"paged pool {contig['paged_ms']} ms")
 
     if args.copy_calibration:
         src = torch.empty(CALIB_BYTES, dtype=torch.uint8, device="cuda")
@@ -736,6 +766,7 @@ def main():
                                 "unit": "GB/s", "frac": round(dec_gbps / PEAK_HBM_GBPS, 4),
                                 "algorithmic_bytes": mixed.decode_bytes},
         },
+        "contiguous_cache": contig,
         "mla_decode": mla,
         "schedule_sim": sched,
         "latency_predictor": alp,
