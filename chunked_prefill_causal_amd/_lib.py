@@ -308,8 +308,8 @@ def chunk_prefill_attn(q, k_cache, v_cache, past_len: int, scale: float | None =
             if t.stride(2) != 1:
                 raise ValueError(f"{name}_cache: the head dim must be dense")
             if not t.is_contiguous():
-                setattr(o, f"{name}_stride_tok", t.stride(0))
-                setattr(o, f"{name}_stride_head", t.stride(1))
+                setattr(o, f"{name}_stride_tok", _stride(t, 0))
+                setattr(o, f"{name}_stride_head", _stride(t, 1))
     o.lse_out = _ptr(lse)
     if workspace is not None:
         o.workspace = _ptr(workspace)
@@ -318,6 +318,14 @@ def chunk_prefill_attn(q, k_cache, v_cache, past_len: int, scale: float | None =
     _check(lib().chunk_prefill_attn(_ptr(q), _ptr(k_cache), _ptr(v_cache), past_len, c, heads, hkv, d,
                                     float(scale), _ptr(out), ctypes.byref(o), _stream(stream)))
     return (out, lse) if return_lse else out
+
+
+def _stride(t, dim: int) -> int:
+    """Element stride of a [tokens, heads, d] view along `dim`; torch may report any stride for a size-1
+    dimension, which is never stepped, so that case gets the dense value."""
+    if t.shape[dim] > 1:
+        return t.stride(dim)
+    return t.shape[2] * (t.shape[1] if dim == 0 else 1)
 
 
 def _host_i32(x):
@@ -375,7 +383,7 @@ def chunkattn_kv_append(k_new, v_new, start_pos: int, block_table, k_pool, v_poo
     if not (k_new.is_contiguous() and v_new.is_contiguous()):
         if k_new.stride(2) != 1 or v_new.stride(2) != 1:
             raise ValueError("k_new / v_new: the head dim must be dense")
-        strides = (ctypes.c_int64 * 4)(k_new.stride(0), k_new.stride(1), v_new.stride(0), v_new.stride(1))
+        strides = (ctypes.c_int64 * 4)(_stride(k_new, 0), _stride(k_new, 1), _stride(v_new, 0), _stride(v_new, 1))
     _check(lib().chunkattn_kv_append(_ptr(k_new), _ptr(v_new), start_pos, n, hkv, d, dv, _dtype_code(k_new.dtype),
                                      _ptr(block_table), block_table.numel(),
                                      k_pool.shape[0] if num_blocks is None else num_blocks,
