@@ -374,3 +374,30 @@ def test_strided_cache_padded_heads(relayout, splits):
     e, el = max_err(out, ref), max_err(lse, ref_lse)
     log(f"padded-head K cache (relayout={relayout}, splits={splits}): max err {e:.3e}, lse err {el:.2e}")
     assert e <= BF16_TOL and el <= LSE_TOL
+
+
+def test_contiguous_workspace_too_small_to_relay_runs_in_place():
+    """A caller workspace sized for split partials only (too small for the re-laid copy) makes the
+    library read the contiguous cache in place, with the requested splits, still matching the oracle;
+    the same call with room to re-lay gives the paged kernel's result."""
+    c, past, hq, hkv, d = 60, 2500, 8, 2, 128
+    n = past + c
+    k, v = seq_kv(n, hkv, d, d, "bf16", 181)
+    q = inputs.normal((c, hq, d), 182, "bf16")
+    scale = 1 / math.sqrt(d)
+    small = torch.empty(L.chunkattn_prefill_workspace_size(c, hq, d, 3), dtype=torch.uint8, device="cuda")
+    big = torch.empty(L.chunkattn_prefill_contiguous_workspace_size(past, c, hq, hkv, d, d, 3),
+                      dtype=torch.uint8, device="cuda")
+    assert big.numel() > small.numel()
+    ref, ref_lse = oracle_chunk(q, k, v, past, scale)
+    outs = []
+    for ws in (small, big):
+        out, lse = L.chunk_prefill_attn(q.cuda(), k.cuda(), v.cuda(), past, scale, return_lse=True,
+                                        num_splits=3, workspace=ws)
+        e, el = max_err(out, ref), max_err(lse, ref_lse)
+        log(f"workspace {ws.numel()} B: max err {e:.3e}, lse err {el:.2e}")
+        assert e <= BF16_TOL and el <= LSE_TOL
+        outs.append(out)
+    pool, table = single_seq_pool(k, v, 183)
+    paged = _paged_run(q.cuda(), pool, table, past, d, num_splits=3)
+    assert torch.equal(outs[1].view(torch.int16), paged.view(torch.int16))
