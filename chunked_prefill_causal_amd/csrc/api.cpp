@@ -106,11 +106,12 @@ struct BatchPlan {
   }
 };
 
-BatchPlan plan_batch(const int32_t* cu, const int32_t* kv, int num_seqs, int heads, int kv_heads, int dv) {
+BatchPlan plan_batch(const int32_t* cu, const int32_t* kv, int num_seqs, int heads, int kv_heads, int dv,
+                     int paged_rows) {
   BatchPlan p;
   const int group = heads / kv_heads;
   const int hpw = heads_per_wg(group, kWavesPaged);
-  const int tok_wg = 256 / hpw;
+  const int tok_wg = paged_rows / hpw;
   p.split_tokens = decode_split_tokens(cu, kv, num_seqs, kv_heads, group);
   for (int s = 0; s < num_seqs; ++s) {
     const int q_len = cu[s + 1] - cu[s];
@@ -136,9 +137,10 @@ BatchPlan plan_batch(const int32_t* cu, const int32_t* kv, int num_seqs, int hea
 // the launch is a single round, each split keeping at least 16 key tiles.
 // Measured on MI355X, one round beats two (1.5-16% on chunks of 512 down to
 // 128 tokens over 32K-200K prefixes).
-int auto_splits(int64_t past_len, int64_t chunk_len, int heads, int kv_heads) {
+int auto_splits(int64_t past_len, int64_t chunk_len, int heads, int kv_heads, int paged_rows) {
   const int hpw = heads_per_wg(heads / kv_heads, kWavesPaged);
-  const int64_t base = (chunk_len + 256 / hpw - 1) / (256 / hpw) * (heads / hpw);
+  const int tok_wg = paged_rows / hpw;
+  const int64_t base = (chunk_len + tok_wg - 1) / tok_wg * (heads / hpw);
   const int64_t n_tiles = (past_len + chunk_len + kBlock - 1) / kBlock;
   if (base == 0 || base >= kNumCUs || n_tiles < 32) return 1;
   int64_t want = (kNumCUs + base - 1) / base;
@@ -240,7 +242,8 @@ size_t chunkattn_prefill_contiguous_workspace_size(int64_t past_len, int64_t chu
   if (past_len < 0 || chunk_len <= 0 || heads <= 0 || kv_heads <= 0 || heads % kv_heads || head_dim <= 0)
     return 0;
   const int dv = head_dim_v ? head_dim_v : head_dim;
-  const int splits = num_splits == 0 ? auto_splits(past_len, chunk_len, heads, kv_heads) : num_splits;
+  const int splits =
+      num_splits == 0 ? auto_splits(past_len, chunk_len, heads, kv_heads, prefill_paged_rows(head_dim, dv)) : num_splits;
   size_t bytes = prefill_ws_bytes(chunk_len, heads, dv, splits);
   if (dtype == CA_BF16 && prefill_paged_supported(head_dim, dv) && past_len + chunk_len <= kMaxTokens)
     bytes += relayout_plan(past_len + chunk_len, kv_heads, head_dim, dv).bytes;
@@ -249,7 +252,7 @@ size_t chunkattn_prefill_contiguous_workspace_size(int64_t past_len, int64_t chu
 
 int32_t chunkattn_prefill_auto_splits(int64_t past_len, int64_t chunk_len, int32_t heads, int32_t kv_heads) {
   if (past_len < 0 || chunk_len < 0 || heads <= 0 || kv_heads <= 0 || heads % kv_heads) return 0;
-  return auto_splits(past_len, chunk_len, heads, kv_heads);
+  return auto_splits(past_len, chunk_len, heads, kv_heads, prefill_paged_rows(128, 128));
 }
 
 ca_status chunk_prefill_attn(const void* q, const void* k, const void* v, int64_t past_len, int64_t chunk_len,
@@ -319,14 +322,15 @@ ca_status chunk_prefill_attn(const void* q, const void* k, const void* v, int64_
   const size_t ws_split_bytes = relay ? o.workspace_bytes - rl.bytes : o.workspace_bytes;
   const bool use_paged_kernel = (paged || relay) && paged_dims;
   const int hpw = heads_per_wg(group, use_paged_kernel ? kWavesPaged : kWavesSmall);
-  const int tok_wg = (use_paged_kernel ? 256 : 128) / hpw;
+  const int paged_rows = prefill_paged_rows(head_dim, dv);
+  const int tok_wg = (use_paged_kernel ? paged_rows : 128) / hpw;
   const int64_t n_tb = (chunk_len + tok_wg - 1) / tok_wg;
   const int n_hg = heads / hpw;
   const int64_t base = n_tb * n_hg;
   const int64_t n_tiles = (kv_len + kBlock - 1) / kBlock;
   int splits = o.num_splits;
   if (splits == 0) {
-    const int want = auto_splits(past_len, chunk_len, heads, kv_heads);
+    const int want = auto_splits(past_len, chunk_len, heads, kv_heads, paged_rows);
     splits = (want > 1 && ws_split && ws_split_bytes >= prefill_ws_bytes(chunk_len, heads, dv, want)) ? want : 1;
   } else if (splits > n_tiles) {
     splits = (int)(n_tiles > 0 ? n_tiles : 1);
@@ -399,7 +403,8 @@ ca_status chunk_prefill_attn(const void* q, const void* k, const void* v, int64_
 size_t chunkattn_varlen_workspace_size(const int32_t* cu, const int32_t* kv, int32_t num_seqs, int32_t heads,
                                        int32_t kv_heads, int32_t head_dim_v) {
   if (!cu || !kv || num_seqs <= 0 || heads <= 0 || kv_heads <= 0 || heads % kv_heads || head_dim_v <= 0) return 0;
-  return plan_batch(cu, kv, num_seqs, heads, kv_heads, head_dim_v).total();
+  // the workspace does not depend on the prefill launch geometry
+  return plan_batch(cu, kv, num_seqs, heads, kv_heads, head_dim_v, prefill_paged_rows(128, 128)).total();
 }
 
 ca_status chunk_attn_varlen(const void* q, const void* k_pool, const void* v_pool, const int32_t* block_tables,
@@ -433,7 +438,8 @@ ca_status chunk_attn_varlen(const void* q, const void* k_pool, const void* v_poo
   }
   const int64_t total_q = cu[num_seqs];
   const int group = heads / kv_heads;
-  const BatchPlan plan = plan_batch(cu, kv, num_seqs, heads, kv_heads, head_dim_v);
+  const int paged_rows = prefill_paged_rows(head_dim, head_dim_v);
+  const BatchPlan plan = plan_batch(cu, kv, num_seqs, heads, kv_heads, head_dim_v, paged_rows);
   if (plan.total()) {
     if (!workspace || workspace_bytes < plan.total())
       return fail(CA_EWORKSPACE, "this batch needs %zu workspace bytes", plan.total());
@@ -468,7 +474,7 @@ ca_status chunk_attn_varlen(const void* q, const void* k_pool, const void* v_poo
   d.kv_heads = kv_heads;
   d.group = group;
   d.split_tokens = plan.split_tokens;
-  d.tok_wg = 256 / hpw;
+  d.tok_wg = paged_rows / hpw;
   d.n_head_groups = heads / hpw;
   d.scale_log2 = cs;
   hipError_t e = launch_batch_plan(d, st);

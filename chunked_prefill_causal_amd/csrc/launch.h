@@ -78,6 +78,8 @@ hipError_t launch_prefill_merge(DType out, int DV, const PrefillArgs& a, hipStre
 hipError_t launch_prefill_varlen(int D, int DV, const PrefillArgs& a, int grid, hipStream_t stream);
 // Paged bf16 path: 8-wave workgroups (256 query rows), direct-to-LDS tiles.
 bool prefill_paged_supported(int D, int DV);
+// Query rows per workgroup of the paged bf16 kernel for these head dims.
+int prefill_paged_rows(int D, int DV);
 hipError_t launch_prefill_paged(DType out, int D, int DV, const PrefillArgs& a, int grid, hipStream_t stream);
 hipError_t launch_prefill_paged_varlen(int D, int DV, const PrefillArgs& a, int grid, hipStream_t stream);
 bool prefill_supported(DType in, DType out, int D, int DV);
