@@ -22,12 +22,14 @@ CA_F32, CA_BF16 = 0, 1
 CA_KV_CONTIGUOUS, CA_KV_PAGED = 0, 1
 CA_SCHED_CPP, CA_SCHED_VPP, CA_SCHED_VPP_ASYNC = 0, 1, 2
 CA_MLA_BF16, CA_MLA_FP8 = 0, 1
+NOALLOC_SCRATCH_BYTES = 64 << 20     # CHUNKATTN_NOALLOC_SCRATCH_BYTES
 BLOCK_SIZE = 64
 MLA_LATENT, MLA_ROPE = 512, 64
 
 EXPORTED = ("ca_prefill_opts_init", "chunk_prefill_attn", "chunkattn_prefill_workspace_size",
             "chunkattn_prefill_contiguous_workspace_size",
-            "chunkattn_prefill_auto_splits", "chunk_attn_varlen", "chunkattn_varlen_workspace_size",
+            "chunkattn_prefill_auto_splits", "chunk_attn_varlen", "chunk_attn_varlen_noalloc",
+            "chunkattn_varlen_workspace_size",
             "chunkattn_kv_append", "chunkattn_sched_simulate", "chunkattn_sched_drain_pack",
             "chunkattn_alp_features", "chunkattn_alp_init", "chunkattn_alp_predict", "chunkattn_alp_update",
             "chunkattn_mla_block_bytes", "chunkattn_mla_decode_workspace_size", "chunkattn_mla_kv_append",
@@ -84,6 +86,9 @@ def lib() -> ctypes.CDLL:
     L.chunk_attn_varlen.argtypes = [vp, vp, vp, vp, i32, i32, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32,
                                     vp, vp, vp, sz, vp]
     L.chunk_attn_varlen.restype = ctypes.c_int
+    L.chunk_attn_varlen_noalloc.argtypes = [vp, vp, vp, vp, i32, i32, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32,
+                                            vp, vp, vp]
+    L.chunk_attn_varlen_noalloc.restype = ctypes.c_int
     L.chunkattn_varlen_workspace_size.argtypes = [vp, vp, i32, i32, i32, i32]
     L.chunkattn_varlen_workspace_size.restype = sz
     L.chunkattn_kv_append.argtypes = [vp, vp, i64, i64, i32, i32, i32, ctypes.c_int, vp, i32, i32, vp, vp,
@@ -370,6 +375,27 @@ def chunk_attn_varlen(q, k_pool, v_pool, block_tables, cu_seqlens_q, kv_lens, sc
         cu.data_ptr(), kv.data_ptr(), n, heads, hkv, d, dv, float(scale), _ptr(out), _ptr(lse),
         _ptr(workspace), workspace.numel(), _stream(stream)))
     return (out, lse) if return_lse else out
+
+
+def chunk_attn_varlen_noalloc(q, k_pool, v_pool, block_tables, cu_seqlens_q, kv_lens, scale: float | None = None, *,
+                              out, cu_seqlens_q_dev, kv_lens_dev, num_blocks: int | None = None, lse=None,
+                              stream=None):
+    """``chunk_attn_varlen`` on the library's static per-device scratch (no workspace).
+
+    For callers that cannot allocate: every tensor, the output and the device
+    copies of the lengths included, must be passed in; this function creates
+    none.  ``cu_seqlens_q`` and ``kv_lens`` are host sequences (int32).
+    """
+    total_q, heads, d = q.shape
+    hkv, dv = k_pool.shape[1], v_pool.shape[3]
+    cu, kv = _host_i32(cu_seqlens_q), _host_i32(kv_lens)
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    _check(lib().chunk_attn_varlen_noalloc(
+        _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables), block_tables.shape[1],
+        k_pool.shape[0] if num_blocks is None else num_blocks, _ptr(cu_seqlens_q_dev), _ptr(kv_lens_dev),
+        cu.data_ptr(), kv.data_ptr(), kv.numel(), heads, hkv, d, dv, float(scale), _ptr(out), _ptr(lse),
+        _stream(stream)))
+    return out
 
 
 def chunkattn_kv_append(k_new, v_new, start_pos: int, block_table, k_pool, v_pool, *, num_blocks: int | None = None,

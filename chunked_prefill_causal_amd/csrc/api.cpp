@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <mutex>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -407,11 +408,42 @@ size_t chunkattn_varlen_workspace_size(const int32_t* cu, const int32_t* kv, int
   return plan_batch(cu, kv, num_seqs, heads, kv_heads, head_dim_v, prefill_paged_rows(128, 128)).total();
 }
 
-ca_status chunk_attn_varlen(const void* q, const void* k_pool, const void* v_pool, const int32_t* block_tables,
-                            int32_t max_blocks, int32_t num_blocks, const int32_t* cu_dev, const int32_t* kv_dev,
-                            const int32_t* cu, const int32_t* kv, int32_t num_seqs, int32_t heads, int32_t kv_heads,
-                            int32_t head_dim, int32_t head_dim_v, float scale, void* out, float* lse_out,
-                            void* workspace, size_t workspace_bytes, void* stream) {
+// Scratch of the allocation-free varlen entry: one array per device, in the
+// library's code object, reached through the address hipGetSymbolAddress
+// returns for the current device (the symbol's name is not a device address
+// in host code).  It holds what the caller's workspace holds in
+// chunk_attn_varlen: per-sequence offsets and decode partials, all written by
+// the batch's own plan and decode kernels before they are read, so nothing
+// needs clearing between calls.
+static constexpr size_t kNoAllocScratchBytes = CHUNKATTN_NOALLOC_SCRATCH_BYTES;
+static __device__ __attribute__((aligned(256))) unsigned char scratch[kNoAllocScratchBytes];
+static constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices] = {};
+
+static ca_status device_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(CA_EUNSUPPORTED, "device %d is beyond the %d the library tracks", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress of the static scratch");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return CA_OK;
+}
+
+// The varlen batch, with the caller's workspace or (static_scratch) the
+// library's per-device array.
+static ca_status varlen_run(const void* q, const void* k_pool, const void* v_pool, const int32_t* block_tables,
+                     int32_t max_blocks, int32_t num_blocks, const int32_t* cu_dev, const int32_t* kv_dev,
+                     const int32_t* cu, const int32_t* kv, int32_t num_seqs, int32_t heads, int32_t kv_heads,
+                     int32_t head_dim, int32_t head_dim_v, float scale, void* out, float* lse_out,
+                     void* workspace, size_t workspace_bytes, bool static_scratch, void* stream) {
   if (!k_pool || !v_pool || !block_tables || !cu_dev || !kv_dev || !cu || !kv)
     return fail(CA_EINVAL, "null pointer argument");
   if (num_seqs > 0 && num_seqs <= 65535 && cu[num_seqs] != 0 && (!q || !out))
@@ -440,13 +472,21 @@ ca_status chunk_attn_varlen(const void* q, const void* k_pool, const void* v_poo
   const int group = heads / kv_heads;
   const int paged_rows = prefill_paged_rows(head_dim, head_dim_v);
   const BatchPlan plan = plan_batch(cu, kv, num_seqs, heads, kv_heads, head_dim_v, paged_rows);
-  if (plan.total()) {
+  if (static_scratch) {
+    if (plan.total() > kNoAllocScratchBytes)
+      return fail(CA_EWORKSPACE, "this batch needs %zu scratch bytes; the allocation-free entry holds %zu",
+                  plan.total(), kNoAllocScratchBytes);
+  } else if (plan.total()) {
     if (!workspace || workspace_bytes < plan.total())
       return fail(CA_EWORKSPACE, "this batch needs %zu workspace bytes", plan.total());
     if (!aligned(workspace, 256)) return fail(CA_EINVAL, "workspace must be 256-byte aligned");
   }
   if (plan.prefill_wgs > 0x7fffffffLL) return fail(CA_ERANGE, "launch grid too large");
   if (total_q == 0) return ok();
+  if (static_scratch) {
+    if (ca_status st = device_scratch(&workspace)) return st;
+    workspace_bytes = kNoAllocScratchBytes;
+  }
 
   hipStream_t st = (hipStream_t)stream;
   const float cs = scale * kLog2e;
@@ -512,6 +552,24 @@ ca_status chunk_attn_varlen(const void* q, const void* k_pool, const void* v_poo
     if (e != hipSuccess) return hip_status(e, "varlen decode launch");
   }
   return ok();
+}
+
+ca_status chunk_attn_varlen(const void* q, const void* k_pool, const void* v_pool, const int32_t* block_tables,
+                            int32_t max_blocks, int32_t num_blocks, const int32_t* cu_dev, const int32_t* kv_dev,
+                            const int32_t* cu, const int32_t* kv, int32_t num_seqs, int32_t heads, int32_t kv_heads,
+                            int32_t head_dim, int32_t head_dim_v, float scale, void* out, float* lse_out,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  return varlen_run(q, k_pool, v_pool, block_tables, max_blocks, num_blocks, cu_dev, kv_dev, cu, kv, num_seqs, heads,
+                    kv_heads, head_dim, head_dim_v, scale, out, lse_out, workspace, workspace_bytes, false, stream);
+}
+
+ca_status chunk_attn_varlen_noalloc(const void* q, const void* k_pool, const void* v_pool,
+                                    const int32_t* block_tables, int32_t max_blocks, int32_t num_blocks,
+                                    const int32_t* cu_dev, const int32_t* kv_dev, const int32_t* cu, const int32_t* kv,
+                                    int32_t num_seqs, int32_t heads, int32_t kv_heads, int32_t head_dim,
+                                    int32_t head_dim_v, float scale, void* out, float* lse_out, void* stream) {
+  return varlen_run(q, k_pool, v_pool, block_tables, max_blocks, num_blocks, cu_dev, kv_dev, cu, kv, num_seqs, heads,
+                    kv_heads, head_dim, head_dim_v, scale, out, lse_out, nullptr, 0, true, stream);
 }
 
 ca_status chunkattn_kv_append(const void* k_new, const void* v_new, int64_t start_pos, int64_t n_tokens,

@@ -211,6 +211,36 @@ size_t chunkattn_varlen_workspace_size(const int32_t* cu_seqlens_q_host, const i
                                        int32_t num_seqs, int32_t heads, int32_t kv_heads,
                                        int32_t head_dim_v);
 
+/* Bytes of the per-device scratch array behind chunk_attn_varlen_noalloc. */
+#define CHUNKATTN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/*
+ * chunk_attn_varlen_noalloc — chunk_attn_varlen for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments, layouts and results as
+ * chunk_attn_varlen, without the workspace: the batch's per-sequence offsets
+ * and decode partials go to a static array of CHUNKATTN_NOALLOC_SCRATCH_BYTES
+ * (64 MiB) that the library holds on every device it runs on until the
+ * process ends.  The call allocates nothing (no hipMalloc or hipFree); its
+ * first call on a device looks the array's address up for that device.
+ *   Returns CA_EWORKSPACE, before any HIP call, for a batch whose
+ *   chunkattn_varlen_workspace_size() exceeds the array (e.g. a mixed batch
+ *   of one 2048-token chunk and 256 decodes of up to 32K tokens needs 34 MiB).
+ *   All calls on one device share that device's array and it keeps the last
+ *   call's contents: calls ordered on one stream are safe, calls that may
+ *   overlap on one device (other streams or threads with no ordering between
+ *   them) race and must be serialised by the caller.  The batch's own kernels
+ *   write every byte they later read, so nothing needs clearing between calls.
+ */
+ca_status chunk_attn_varlen_noalloc(const void* q, const void* k_pool, const void* v_pool,
+                                    const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                    int32_t num_blocks,
+                                    const int32_t* cu_seqlens_q, const int32_t* kv_lens,
+                                    const int32_t* cu_seqlens_q_host, const int32_t* kv_lens_host,
+                                    int32_t num_seqs, int32_t heads, int32_t kv_heads,
+                                    int32_t head_dim, int32_t head_dim_v, float scale,
+                                    void* out, float* lse_out, void* stream);
+
 /*
  * chunkattn_kv_append — write n_tokens new keys/values of one sequence into
  * the paged pool at logical positions [start_pos, start_pos + n_tokens)

@@ -173,6 +173,43 @@ def test_varlen_rejections(kwargs, status):
     assert varlen(**kwargs) == status
 
 
+def varlen_noalloc(q=FAKE, cu=(0, 1, 2), kv=(10, 20), hq=8, hkv=2, d=128, dv=128, max_blocks=4, num_blocks=8,
+                   scale=0.1, out=FAKE, k=FAKE):
+    cu_a = (ctypes.c_int32 * len(cu))(*cu)
+    kv_a = (ctypes.c_int32 * len(kv))(*kv)
+    return L.lib().chunk_attn_varlen_noalloc(q, k, FAKE, FAKE, max_blocks, num_blocks, FAKE, FAKE,
+                                             ctypes.addressof(cu_a), ctypes.addressof(kv_a), len(kv), hq, hkv, d, dv,
+                                             scale, out, None, None)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(k=None), L.CA_EINVAL),
+    (dict(cu=(0, 2, 1)), L.CA_EINVAL),
+    (dict(kv=(10, 300)), L.CA_ERANGE),
+    (dict(d=128, dv=64), L.CA_EUNSUPPORTED),
+    (dict(scale=float("nan")), L.CA_EINVAL),
+])
+def test_varlen_noalloc_rejections(kwargs, status):
+    """The allocation-free varlen entry validates like chunk_attn_varlen, before any HIP call."""
+    assert varlen_noalloc(**kwargs) == status
+
+
+def test_varlen_noalloc_rejects_batches_beyond_its_scratch():
+    """A batch whose partials exceed the static scratch fails with CA_EWORKSPACE before any HIP call;
+    the same batch sized just under the limit is accepted by the size query."""
+    n = 4096
+    cu = tuple(range(n + 1))
+    kv = (65536,) * n
+    need = L.chunkattn_varlen_workspace_size(cu, kv, 32, 8, 128)
+    assert need > L.NOALLOC_SCRATCH_BYTES
+    assert varlen_noalloc(cu=cu, kv=kv, hq=32, hkv=8, max_blocks=1024, num_blocks=1 << 20) == L.CA_EWORKSPACE
+    assert b"allocation-free" in L.lib().chunkattn_last_error()
+
+
+def test_varlen_noalloc_empty_batch_succeeds():
+    assert varlen_noalloc(q=None, out=None, cu=(0, 0, 0), kv=(5, 9)) == L.CA_OK
+
+
 def test_varlen_empty_batch_succeeds():
     assert varlen(q=None, out=None, cu=(0, 0, 0), kv=(5, 9), ws=None) == L.CA_OK
 

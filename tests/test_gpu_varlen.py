@@ -15,7 +15,7 @@ import torch
 from chunked_prefill_causal_amd import _lib as L
 from chunked_prefill_causal_amd import inputs
 
-from gpu_common import BF16_TOL, LSE_TOL, Pool, log, max_err, oracle_chunk, require_gpu, seq_kv
+from gpu_common import BF16_TOL, LSE_TOL, build_batch, log, max_err, oracle_chunk, require_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -23,32 +23,6 @@ pytestmark = pytest.mark.gpu
 @pytest.fixture(autouse=True, scope="module")
 def _gpu():
     require_gpu()
-
-
-def build_batch(q_lens, kv_lens, hq, hkv, d, dv, seed, poison=True):
-    """Per-sequence seeded K/V and queries placed in one pool with disjoint random blocks."""
-    n = len(q_lens)
-    max_blocks = max(math.ceil(k / 64) for k in kv_lens)
-    needed = [math.ceil(k / 64) for k in kv_lens]
-    total = sum(needed)
-    pool_blocks = inputs.pool_size(total)
-    perm = inputs.block_table(total, seed, pool_blocks)
-    pool = Pool(pool_blocks, hkv, d, dv, torch.bfloat16, poison=poison)
-    tables = np.zeros((n, max_blocks), dtype=np.int32)
-    seqs = []
-    off = 0
-    for s in range(n):
-        tables[s, : needed[s]] = perm[off: off + needed[s]]
-        off += needed[s]
-        k, v = seq_kv(kv_lens[s], hkv, d, dv, "bf16", seed + 10 * s + 1)
-        q = inputs.normal((q_lens[s], hq, d), seed + 10 * s + 5, "bf16")
-        seqs.append((q, k, v))
-    tables_d = torch.from_numpy(tables).cuda()
-    for s in range(n):
-        pool.append(seqs[s][1], seqs[s][2], tables_d[s])
-    cu = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
-    q_all = torch.cat([x[0] for x in seqs]) if cu[-1] else torch.empty((0, hq, d), dtype=torch.bfloat16)
-    return pool, tables_d, cu, q_all, seqs
 
 
 def check_batch(q_lens, kv_lens, hq, hkv, d, dv, seed):
