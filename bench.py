@@ -762,6 +762,13 @@ def main():
             "prefill_only_ms": round(pre_ms, 4),
             "decode_only_ms": round(dec_ms, 4),
             "prefill_tflops": round(mixed.prefill_flops / (pre_ms / 1e3) / 1e12, 1),
+            "serial_sum_ms": round(pre_ms + dec_ms, 4),
+            "ideal_overlap_ms": round(1e3 * max(mixed.prefill_flops / (PEAK_BF16_TFLOPS * 1e12),
+                                                mixed.decode_bytes / (PEAK_HBM_GBPS * 1e9)), 4),
+            "vs_serial": round(median(mixed_ms) / (pre_ms + dec_ms), 4),
+            "note": ("one chunk_attn_varlen call; the library runs the prefill and decode parts at once on "
+                     "two CU-masked halves of the GPU. serial_sum_ms = prefill-only + decode-only calls; "
+                     "ideal_overlap_ms = max(prefill flops / dense bf16 peak, decode bytes / HBM peak)"),
             "roofline_decode": {"bound": "hbm", "achieved": round(dec_gbps, 1), "peak": PEAK_HBM_GBPS,
                                 "unit": "GB/s", "frac": round(dec_gbps / PEAK_HBM_GBPS, 4),
                                 "algorithmic_bytes": mixed.decode_bytes},

@@ -327,8 +327,12 @@ def chunk_prefill_attn(q, k_cache, v_cache, past_len: int, scale: float | None =
 
 def _stride(t, dim: int) -> int:
     """Element stride of a [tokens, heads, d] view along `dim`; torch may report any stride for a size-1
-    dimension, which is never stepped, so that case gets the dense value."""
+    dimension, which is never stepped, so that case gets the dense value.  A broadcast (stride-0)
+    dimension is refused here: the ABI reads a zero stride as "dense", which would step past the
+    tensor's storage."""
     if t.shape[dim] > 1:
+        if t.stride(dim) <= 0:
+            raise ValueError(f"a cache view broadcast along dim {dim} (stride {t.stride(dim)}) is not supported")
         return t.stride(dim)
     return t.shape[2] * (t.shape[1] if dim == 0 else 1)
 

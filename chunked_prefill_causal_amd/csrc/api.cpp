@@ -316,7 +316,11 @@ ca_status chunk_prefill_attn(const void* q, const void* k, const void* v, int64_
   bool relay = false;
   if (!paged && paged_dims && o.workspace && aligned(o.workspace, 256)) {
     rl = relayout_plan(kv_len, kv_heads, head_dim, dv);
-    relay = o.workspace_bytes >= rl.bytes;
+    // An explicit split count keeps its partials' room: re-lay only when both fit,
+    // otherwise read the cache in place with the whole workspace for partials.
+    const int64_t n_tiles_rl = (kv_len + kBlock - 1) / kBlock;
+    const int want_splits = o.num_splits > n_tiles_rl ? (int)n_tiles_rl : o.num_splits;
+    relay = o.workspace_bytes >= rl.bytes + prefill_ws_bytes(chunk_len, heads, dv, want_splits);
   }
   // split partials follow the re-laid pools in the workspace
   void* const ws_split = relay ? (void*)((char*)o.workspace + rl.bytes) : o.workspace;
@@ -437,6 +441,92 @@ static ca_status device_scratch(void** out) {
   return CA_OK;
 }
 
+// ---- co-scheduling of a mixed batch ----------------------------------------------------
+// The prefill part of a mixed batch is bound by the matrix cores and the
+// decode part by HBM, so they can share the chip.  Measured on MI355X for a
+// 2048-token chunk at past 65536 plus 256 decodes (contexts U[1024, 32768]):
+// decode alone 3.16 ms on all 256 CUs and 3.58 ms on 128; prefill alone
+// 1.73 ms on 256 CUs and 2.90 ms on 128 (two rounds of workgroups, at a
+// higher clock when alone); both at once on disjoint halves 3.78 ms against
+// 4.92 ms back to back.  Run together, the prefill half takes ~3.5 ms (the
+// decode half draws power), so handing decode work to the prefill half after
+// its kernel does not pay; each cross-queue event wait costs ~40-50 us.  A prefill workgroup holds 448 of a SIMD's 512 registers, so
+// a decode wave cannot share its CU: the halves are CU-masked streams.
+struct CoStreams {
+  std::mutex mu;
+  hipStream_t prefill = nullptr, decode = nullptr;
+  hipEvent_t fork = nullptr, join_prefill = nullptr, join_decode = nullptr;
+};
+static std::mutex g_co_mu;
+static CoStreams* g_co[kMaxDevices] = {};
+static bool g_co_failed[kMaxDevices] = {};
+
+// Half of the CUs, taken as CUs whose index has bit 3 clear (or set): half of
+// every XCD whether mask bits map to XCDs in blocks of 32 or round-robin.
+static constexpr int kMaxMaskWords = 64;   // CU masks of up to 2048 CUs
+static hipError_t half_chip_stream(int n_cu, int parity, hipStream_t* s) {
+  uint32_t mask[kMaxMaskWords] = {};
+  const int words = (n_cu + 31) / 32;
+  if (words > kMaxMaskWords) return hipErrorInvalidValue;
+  for (int i = 0; i < n_cu; ++i)
+    if (((i >> 3) & 1) == parity) mask[i >> 5] |= 1u << (i & 31);
+  return hipExtStreamCreateWithCUMask(s, (uint32_t)words, mask);
+}
+
+// The current device's co-scheduling streams and events, made on first use;
+// null (run serially) where they cannot be made.
+static CoStreams* co_streams() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_co_mu);
+  if (g_co[dev] || g_co_failed[dev]) return g_co[dev];
+  int n_cu = 0;
+  CoStreams* c = new CoStreams();
+  hipError_t e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e == hipSuccess && n_cu < 64) e = hipErrorNotSupported;
+  if (e == hipSuccess) e = half_chip_stream(n_cu, 0, &c->prefill);
+  if (e == hipSuccess) e = half_chip_stream(n_cu, 1, &c->decode);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&c->fork, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&c->join_prefill, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&c->join_decode, hipEventDisableTiming);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    g_co_failed[dev] = true;
+    return nullptr;   // the streams and events made so far stay with the process
+  }
+  g_co[dev] = c;
+  return c;
+}
+
+// Whether the two halves finish before the two parts would back to back:
+// both parts must be sizeable, and the prefill on half the CUs (more rounds
+// of its workgroups) and the decode on half the CUs must each end before the
+// serial pair would.  Rates are MI355X figures for these kernels: ~1.25
+// PFLOP/s prefill and ~5.8 TB/s decode on the whole chip; on half of it the
+// decode runs 1.13x longer (measured), and the prefill, sharing the power
+// budget with the decode, gains no clock.
+static bool co_schedule_pays(const int32_t* cu, const int32_t* kv, int num_seqs, int heads, int kv_heads, int d,
+                             int dv, int64_t prefill_wgs) {
+  const int group = heads / kv_heads;
+  double flops = 0, bytes = 0;
+  for (int s = 0; s < num_seqs; ++s) {
+    const int64_t q = cu[s + 1] - cu[s];
+    if (q <= 0) continue;
+    if (q * group <= 32) {
+      bytes += (double)kv[s] * kv_heads * (d + dv) * 2;
+    } else {
+      const double past = (double)(kv[s] - q);
+      flops += (double)heads * (q * past + 0.5 * q * (q + 1)) * 2.0 * (d + dv);
+    }
+  }
+  const double t_prefill = flops / 1.25e15, t_decode = bytes / 5.8e12;
+  if (t_prefill < 0.2 * t_decode || t_decode < 0.2 * t_prefill) return false;
+  const double rounds_full = (double)((prefill_wgs + kNumCUs - 1) / kNumCUs);
+  const double rounds_half = (double)((prefill_wgs + kNumCUs / 2 - 1) / (kNumCUs / 2));
+  const double t_serial = t_prefill + t_decode;
+  return t_prefill * rounds_half / rounds_full < t_serial && 1.13 * t_decode < t_serial;
+}
+
 // The varlen batch, with the caller's workspace or (static_scratch) the
 // library's per-device array.
 static ca_status varlen_run(const void* q, const void* k_pool, const void* v_pool, const int32_t* block_tables,
@@ -543,11 +633,33 @@ static ca_status varlen_run(const void* q, const void* k_pool, const void* v_poo
     a.wg_off = d.wg_off;
     a.num_seqs = num_seqs;
     a.max_blocks = max_blocks;
+    if (plan.n_decode && !static_scratch &&
+        co_schedule_pays(cu, kv, num_seqs, heads, kv_heads, head_dim, head_dim_v, plan.prefill_wgs)) {
+      // The prefill part (matrix-bound) and the decode part (HBM-bound) run at
+      // the same time on two halves of the chip; the decode half merges its
+      // partials before both join the caller's stream.
+      CoStreams* cs2 = co_streams();
+      if (cs2) {
+        std::lock_guard<std::mutex> lock(cs2->mu);
+        e = hipEventRecord(cs2->fork, st);
+        if (e == hipSuccess) e = hipStreamWaitEvent(cs2->prefill, cs2->fork, 0);
+        if (e == hipSuccess) e = hipStreamWaitEvent(cs2->decode, cs2->fork, 0);
+        if (e == hipSuccess) e = launch_prefill_paged_varlen(head_dim, head_dim_v, a, (int)plan.prefill_wgs, cs2->prefill);
+        if (e == hipSuccess) e = launch_decode(head_dim, head_dim_v, d, plan.max_splits, 0, num_seqs, cs2->decode);
+        if (e == hipSuccess) e = launch_decode_merge(head_dim_v, d, cs2->decode);
+        if (e == hipSuccess) e = hipEventRecord(cs2->join_prefill, cs2->prefill);
+        if (e == hipSuccess) e = hipEventRecord(cs2->join_decode, cs2->decode);
+        if (e == hipSuccess) e = hipStreamWaitEvent(st, cs2->join_prefill, 0);
+        if (e == hipSuccess) e = hipStreamWaitEvent(st, cs2->join_decode, 0);
+        if (e != hipSuccess) return hip_status(e, "co-scheduled varlen launch");
+        return ok();
+      }
+    }
     e = launch_prefill_paged_varlen(head_dim, head_dim_v, a, (int)plan.prefill_wgs, st);
     if (e != hipSuccess) return hip_status(e, "varlen prefill launch");
   }
   if (plan.n_decode) {
-    e = launch_decode(head_dim, head_dim_v, d, plan.max_splits, st);
+    e = launch_decode(head_dim, head_dim_v, d, plan.max_splits, 0, num_seqs, st);
     if (e == hipSuccess) e = launch_decode_merge(head_dim_v, d, st);
     if (e != hipSuccess) return hip_status(e, "varlen decode launch");
   }

@@ -86,8 +86,9 @@ __global__ __launch_bounds__(1024) void plan_kernel(const DecodeArgs a) {
 template <int D, int DV>
 __global__ __launch_bounds__(64) void decode_kernel(const DecodeArgs a) {
   constexpr int NQ = D / 16, NB = DV / 32;
-  const int sp = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
+  const int sp = blockIdx.x, g = blockIdx.y, s = a.seq_begin + (int)blockIdx.z;
   const int lane = threadIdx.x, hl = lane >> 5, col = lane & 31;
+  if (s >= a.num_seqs) return;
   const int q0 = a.cu_seqlens_q[s];
   const int q_len = a.cu_seqlens_q[s + 1] - q0;
   const int G = a.group;
@@ -268,8 +269,12 @@ hipError_t launch_batch_plan(const DecodeArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_decode(int D, int DV, const DecodeArgs& a, int max_splits, hipStream_t stream) {
-  const dim3 grid(max_splits, a.kv_heads, a.num_seqs);
+hipError_t launch_decode(int D, int DV, const DecodeArgs& args, int max_splits, int seq_begin, int seq_end,
+                         hipStream_t stream) {
+  if (seq_end <= seq_begin) return hipSuccess;
+  DecodeArgs a = args;
+  a.seq_begin = seq_begin;
+  const dim3 grid(max_splits, a.kv_heads, seq_end - seq_begin);
   if (D == 64 && DV == 64) hipLaunchKernelGGL((decode_kernel<64, 64>), grid, dim3(64), 0, stream, a);
   else if (D == 128 && DV == 128) hipLaunchKernelGGL((decode_kernel<128, 128>), grid, dim3(64), 0, stream, a);
   else if (D == 192 && DV == 128) hipLaunchKernelGGL((decode_kernel<192, 128>), grid, dim3(64), 0, stream, a);

@@ -64,6 +64,7 @@ struct DecodeArgs {
   int64_t total_q;
   int64_t total_slots;           // partial slots the workspace holds (bound on every access)
   int32_t num_seqs, max_blocks, num_blocks;
+  int32_t seq_begin;             // first sequence of this decode launch (grid z counts from it)
   int32_t heads, kv_heads, group;
   int32_t split_tokens;          // keys per split (multiple of 64)
   int32_t tok_wg;                // query tokens per prefill workgroup
@@ -75,7 +76,6 @@ struct DecodeArgs {
 hipError_t launch_prefill(DType in, DType out, int D, int DV, bool paged, const PrefillArgs& a,
                           int grid, hipStream_t stream);
 hipError_t launch_prefill_merge(DType out, int DV, const PrefillArgs& a, hipStream_t stream);
-hipError_t launch_prefill_varlen(int D, int DV, const PrefillArgs& a, int grid, hipStream_t stream);
 // Paged bf16 path: 8-wave workgroups (256 query rows), direct-to-LDS tiles.
 bool prefill_paged_supported(int D, int DV);
 // Query rows per workgroup of the paged bf16 kernel for these head dims.
@@ -85,7 +85,9 @@ hipError_t launch_prefill_paged_varlen(int D, int DV, const PrefillArgs& a, int 
 bool prefill_supported(DType in, DType out, int D, int DV);
 
 hipError_t launch_batch_plan(const DecodeArgs& a, hipStream_t stream);
-hipError_t launch_decode(int D, int DV, const DecodeArgs& a, int max_splits, hipStream_t stream);
+// Decode partials of sequences [seq_begin, seq_end) of the batch.
+hipError_t launch_decode(int D, int DV, const DecodeArgs& a, int max_splits, int seq_begin, int seq_end,
+                         hipStream_t stream);
 hipError_t launch_decode_merge(int DV, const DecodeArgs& a, hipStream_t stream);
 bool decode_supported(int D, int DV);
 

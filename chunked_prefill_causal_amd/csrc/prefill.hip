@@ -64,7 +64,7 @@ __device__ __forceinline__ int key_of_reg(int kb2, int r, int hl) {
   else return 32 * kb2 + 8 * (r >> 2) + 4 * hl + (r & 3);
 }
 
-template <typename E, typename EO, int D, int DV, bool kPaged, bool kVarlen>
+template <typename E, typename EO, int D, int DV, bool kPaged>
 __global__ __launch_bounds__(256, sizeof(E) == 2 ? 2 : 1) void prefill_kernel(const PrefillArgs a) {
   using C = PrefillCfg<E, D, DV>;
   constexpr bool kBf16 = C::kBf16;
@@ -85,33 +85,8 @@ __global__ __launch_bounds__(256, sizeof(E) == 2 ? 2 : 1) void prefill_kernel(co
   int n_tb = a.n_tok_blocks;
   const int S = a.num_splits;
   int split, w;
-  if constexpr (kVarlen) {
-    // Largest s with wg_off[s] <= blockIdx.x (sequences without prefill rows
-    // own an empty range and are never found).
-    const int64_t bid = blockIdx.x;
-    int lo = 0, hi = a.num_seqs;
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (a.wg_off[mid] <= bid) lo = mid;
-      else hi = mid;
-    }
-    const int q0 = a.cu_seqlens_q[lo];
-    c = a.cu_seqlens_q[lo + 1] - q0;
-    kv_len = a.kv_lens[lo];
-    P = kv_len - c;
-    n_tb = (int)((c + tok_wg - 1) / tok_wg);
-    qbase += (int64_t)q0 * a.heads * D;
-    obase += (int64_t)q0 * a.heads * DV;
-    if (lse) lse += q0;
-    btab += (int64_t)lo * a.max_blocks;
-    split = 0;
-    w = (int)(bid - a.wg_off[lo]);
-    // Device lengths that disagree with the host plan never reach memory.
-    if (c <= 0 || P < 0 || kv_len > (int64_t)a.max_blocks * kBlock || w >= n_tb * a.n_head_groups) return;
-  } else {
-    split = blockIdx.x % S;
-    w = blockIdx.x / S;
-  }
+  split = blockIdx.x % S;
+  w = blockIdx.x / S;
   int tb, hg;
   if (a.xcd_remap) {
     // Consecutive workgroup ids go round-robin over the 8 XCDs; give each XCD
@@ -433,21 +408,9 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(const PrefillArgs a)
 template <typename E, typename EO, int D, int DV>
 static hipError_t launch_one(bool paged, const PrefillArgs& a, int grid, hipStream_t stream) {
   if (paged)
-    hipLaunchKernelGGL((prefill_kernel<E, EO, D, DV, true, false>), dim3(grid), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((prefill_kernel<E, EO, D, DV, true>), dim3(grid), dim3(256), 0, stream, a);
   else
-    hipLaunchKernelGGL((prefill_kernel<E, EO, D, DV, false, false>), dim3(grid), dim3(256), 0, stream, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_prefill_varlen(int D, int DV, const PrefillArgs& a, int grid, hipStream_t stream) {
-  if (D == 64 && DV == 64)
-    hipLaunchKernelGGL((prefill_kernel<uint16_t, uint16_t, 64, 64, true, true>), dim3(grid), dim3(256), 0, stream, a);
-  else if (D == 128 && DV == 128)
-    hipLaunchKernelGGL((prefill_kernel<uint16_t, uint16_t, 128, 128, true, true>), dim3(grid), dim3(256), 0, stream, a);
-  else if (D == 192 && DV == 128)
-    hipLaunchKernelGGL((prefill_kernel<uint16_t, uint16_t, 192, 128, true, true>), dim3(grid), dim3(256), 0, stream, a);
-  else
-    return hipErrorInvalidValue;
+    hipLaunchKernelGGL((prefill_kernel<E, EO, D, DV, false>), dim3(grid), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -195,6 +195,11 @@ int32_t chunkattn_prefill_auto_splits(int64_t past_len, int64_t chunk_len, int32
  * whose rows per KV head, q_len_s * (heads / kv_heads), are at most 32 takes
  * the split-KV decode path; longer ones take the prefill path.  Both write
  * straight into out.
+ * When the batch holds both kinds and neither dwarfs the other, the prefill
+ * part (matrix-core bound) and the decode part (HBM bound) run at the same
+ * time on two halves of the GPU's CUs: two internal CU-masked streams, made
+ * once per device, forked from `stream` and joined back to it with events,
+ * so the call still behaves as work enqueued on `stream`.
  */
 ca_status chunk_attn_varlen(const void* q, const void* k_pool, const void* v_pool,
                             const int32_t* block_tables, int32_t max_blocks_per_seq,

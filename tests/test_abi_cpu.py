@@ -10,6 +10,7 @@ import re
 import subprocess
 
 import pytest
+import torch
 
 from chunked_prefill_causal_amd import _lib as L
 
@@ -288,3 +289,31 @@ def test_mla_append_rejections():
     assert f(nb=0) == L.CA_EINVAL
     assert f(start=60, n=10) == L.CA_ERANGE
     assert f(n=0, lat=None) == L.CA_OK
+
+
+def test_stride_of_cache_views():
+    """Strides the binding passes for strided cache views (torch CPU views, no library call)."""
+    t, hq, hkv, d = 7, 8, 1, 128
+    qkv = torch.empty((t, hq + 2 * hkv, d), dtype=torch.bfloat16)
+    k = qkv[:, hq:hq + hkv]                                # one KV head sliced out of a fused QKV
+    assert k.shape == (t, 1, d)
+    assert (L._stride(k, 0), L._stride(k, 1)) == ((hq + 2) * d, d)
+    one = torch.empty((4, 1, d), dtype=torch.bfloat16).transpose(0, 1)   # one token, odd strides
+    assert one.shape == (1, 4, d)
+    assert (L._stride(one, 0), L._stride(one, 1)) == (4 * d, d)
+    pad = torch.empty((t, 4, 256), dtype=torch.bfloat16)[:, :, :192]    # d = 192 in heads padded to 256
+    assert (L._stride(pad, 0), L._stride(pad, 1)) == (4 * 256, 256)
+    one_pad = pad[2:3]
+    assert (L._stride(one_pad, 0), L._stride(one_pad, 1)) == (4 * 192, 256)
+
+
+def test_broadcast_cache_view_is_refused_before_the_library():
+    """An expanded (stride-0) view would read as "dense" through the ABI; the binding refuses it."""
+    base = torch.empty((9, 1, 64), dtype=torch.bfloat16)
+    k = base.expand(9, 4, 64)
+    assert k.stride(1) == 0
+    with pytest.raises(ValueError, match="broadcast"):
+        L._stride(k, 1)
+    q = torch.empty((3, 8, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="broadcast"):
+        L.chunk_prefill_attn(q, k, k, 6, relayout=False)

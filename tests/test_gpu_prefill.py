@@ -17,7 +17,7 @@ import torch
 from chunked_prefill_causal_amd import _lib as L
 from chunked_prefill_causal_amd import inputs
 
-from gpu_common import (BF16_TOL, F32_TOL, LSE_TOL, Pool, log, max_err, oracle_chunk, require_gpu,
+from gpu_common import (BF16_TOL, F32_TOL, LSE_TOL, Pool, log, max_err, oracle_chunk, oracle_rows, require_gpu,
                         seq_kv, single_seq_pool, torch_dtype)
 
 pytestmark = pytest.mark.gpu
@@ -401,3 +401,26 @@ def test_contiguous_workspace_too_small_to_relay_runs_in_place():
     pool, table = single_seq_pool(k, v, 183)
     paged = _paged_run(q.cuda(), pool, table, past, d, num_splits=3)
     assert torch.equal(outs[1].view(torch.int16), paged.view(torch.int16))
+
+
+def test_contiguous_split_workspace_larger_than_relayout_runs_in_place():
+    """A workspace sized for an explicit split count (chunkattn_prefill_workspace_size) that would hold
+    the re-laid K/V but not the re-laid K/V plus the partials: the library reads the cache in place
+    with the requested splits instead of failing with CA_EWORKSPACE."""
+    c, past, hq, hkv, d = 4096, 4096, 32, 8, 128
+    k, v = seq_kv(past + c, hkv, d, d, "bf16", 191)
+    q = inputs.normal((c, hq, d), 192, "bf16")
+    scale = 1 / math.sqrt(d)
+    need = L.chunkattn_prefill_workspace_size(c, hq, d, 2)
+    relay = L.chunkattn_prefill_contiguous_workspace_size(past, c, hq, hkv, d, d, 1)
+    assert relay < need < relay + need
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    out = L.chunk_prefill_attn(q.cuda(), k.cuda(), v.cuda(), past, scale, num_splits=2, workspace=ws)
+    rng = np.random.default_rng(193)
+    tok = np.concatenate([[0, c - 1], rng.integers(0, c, 254)]).astype(np.int64)
+    head = rng.integers(0, hq, tok.size).astype(np.int64)
+    ref, _ = oracle_rows(q, k, v, past, scale, tok, head)
+    got = out[torch.from_numpy(tok).cuda(), torch.from_numpy(head).cuda()]
+    e = max_err(got, ref)
+    log(f"split-only workspace {need} B (re-layout {relay} B), 2 splits in place: max err {e:.3e}")
+    assert e <= BF16_TOL
