@@ -36,9 +36,9 @@ F32, BF16, F64 = 0, 1, 2
 
 
 def build() -> str:
-    """Compile attn_oracle.c with gcc (-O2, OpenMP, no fast-math)."""
+    """Compile attn_oracle.c with gcc (-O3, OpenMP, no fast-math, no FMA contraction)."""
     tmp = _LIB_PATH + ".tmp"
-    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+    cmd = ["gcc", "-O3", "-fopenmp", "-fPIC", "-shared", "-std=c11",
            "-fno-fast-math", "-ffp-contract=off", _SRC, "-o", tmp, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, _LIB_PATH)

@@ -52,7 +52,48 @@ static double orc_load(const void* base, int dtype, int64_t idx) {
   return (double)f;
 }
 
-int orc_version(void) { return 1; }
+/* Elements idx .. idx+n-1 of a tensor stored as dtype, widened exactly to fp64. */
+static void orc_widen(const void* base, int dtype, int64_t idx, int32_t n, double* dst) {
+  if (dtype == ORC_F64) {
+    memcpy(dst, (const double*)base + idx, sizeof(double) * (size_t)n);
+  } else if (dtype == ORC_F32) {
+    const float* src = (const float*)base + idx;
+    for (int32_t e = 0; e < n; ++e) dst[e] = (double)src[e];
+  } else {
+    const uint16_t* src = (const uint16_t*)base + idx;   /* bf16: the upper half of an fp32 */
+    for (int32_t e = 0; e < n; ++e) {
+      const uint32_t bits = (uint32_t)src[e] << 16;
+      float f;
+      memcpy(&f, &bits, sizeof f);
+      dst[e] = (double)f;
+    }
+  }
+}
+
+/* Rows are independent.  They are evaluated in blocks of up to ORC_ROWS rows
+ * that read the same KV head (taken in order of query position), key by key,
+ * so a block reads each key's K and V rows once instead of once per row.
+ * Every row's arithmetic is the one-row definition above, in the same order:
+ * each dot product adds its terms in feature order, and the maximum, the
+ * normaliser and the weighted sum of values run over keys in key order.  So
+ * the blocking changes no value; it only spares host memory traffic. */
+enum { ORC_ROWS = 16 };
+
+int orc_version(void) { return 2; }
+
+typedef struct {
+  int32_t g;        /* KV head */
+  int64_t pos;      /* absolute query position */
+  int64_t r;        /* index into the caller's row list */
+} orc_row;
+
+static int orc_row_cmp(const void* a, const void* b) {
+  const orc_row* x = (const orc_row*)a;
+  const orc_row* y = (const orc_row*)b;
+  if (x->g != y->g) return x->g < y->g ? -1 : 1;
+  if (x->pos != y->pos) return x->pos < y->pos ? -1 : 1;
+  return x->r < y->r ? -1 : (x->r > y->r);
+}
 
 /*
  * Attention for an explicit list of query rows.
@@ -75,58 +116,111 @@ int orc_attend_rows(const void* q, const void* k, const void* v, int dtype,
     if (tok[r] < 0 || tok[r] >= chunk_len || head[r] < 0 || head[r] >= Hq) return -1;
     if (past_len + tok[r] >= kv_len) return -1;
   }
+  if (n_rows == 0) return 0;
+  orc_row* order = (orc_row*)malloc(sizeof(orc_row) * (size_t)n_rows);
+  int64_t* block_start = (int64_t*)malloc(sizeof(int64_t) * (size_t)(n_rows + 1));
+  if (!order || !block_start) {
+    free(order);
+    free(block_start);
+    return -1;
+  }
+  for (int64_t r = 0; r < n_rows; ++r) {
+    order[r].g = head[r] / group;
+    order[r].pos = past_len + tok[r];
+    order[r].r = r;
+  }
+  qsort(order, (size_t)n_rows, sizeof(orc_row), orc_row_cmp);
+  int64_t n_blocks = 0;
+  for (int64_t r = 0; r < n_rows; ++r)
+    if (r == 0 || order[r].g != order[r - 1].g || r - block_start[n_blocks - 1] == ORC_ROWS)
+      block_start[n_blocks++] = r;
+  block_start[n_blocks] = n_rows;
+
   int err = 0;
   if (nthreads > 0) omp_set_num_threads(nthreads);
 #pragma omp parallel
   {
-    double* s = (double*)malloc(sizeof(double) * (size_t)(kv_len > 0 ? kv_len : 1));
-    double* acc = (double*)malloc(sizeof(double) * (size_t)dv);
-    if (!s || !acc) {
+    const int64_t span = kv_len > 0 ? kv_len : 1;
+    double* s = (double*)malloc(sizeof(double) * (size_t)span * ORC_ROWS);      /* logits, [row][key] */
+    double* acc = (double*)malloc(sizeof(double) * (size_t)dv * ORC_ROWS);     /* weighted sums, [row][e] */
+    double* qt = (double*)malloc(sizeof(double) * (size_t)d * ORC_ROWS);      /* queries, [e][row] */
+    double* kd = (double*)malloc(sizeof(double) * (size_t)d);
+    double* vd = (double*)malloc(sizeof(double) * (size_t)dv);
+    if (!s || !acc || !qt || !kd || !vd) {
 #pragma omp atomic write
       err = -1;
     } else {
 #pragma omp for schedule(dynamic, 1)
-      for (int64_t r = 0; r < n_rows; ++r) {
-        const int64_t i = tok[r];
-        const int32_t h = head[r];
-        const int32_t g = h / group;
-        const int64_t p = past_len + i;           /* absolute query position */
-        int64_t lo = key_lo < 0 ? 0 : key_lo;
-        int64_t hi = p + 1;                       /* causal: keys 0..p */
-        if (key_hi >= 0 && key_hi < hi) hi = key_hi;
-        double* o = out + r * dv;
-        if (hi <= lo) {
-          for (int32_t e = 0; e < dv; ++e) o[e] = 0.0;
-          lse[r] = -INFINITY;
-          continue;
+      for (int64_t b = 0; b < n_blocks; ++b) {
+        const orc_row* rows = order + block_start[b];
+        const int32_t nr = (int32_t)(block_start[b + 1] - block_start[b]);
+        const int32_t g = rows[0].g;
+        int64_t lo[ORC_ROWS], hi[ORC_ROWS];
+        double m[ORC_ROWS], l[ORC_ROWS], dot[ORC_ROWS];
+        int64_t j_lo = -1, j_hi = 0;
+        for (int32_t t = 0; t < nr; ++t) {
+          lo[t] = key_lo < 0 ? 0 : key_lo;
+          hi[t] = rows[t].pos + 1;                         /* causal: keys 0..pos */
+          if (key_hi >= 0 && key_hi < hi[t]) hi[t] = key_hi;
+          if (hi[t] > lo[t]) {
+            if (j_lo < 0 || lo[t] < j_lo) j_lo = lo[t];
+            if (hi[t] > j_hi) j_hi = hi[t];
+          }
+          m[t] = -INFINITY;
+          l[t] = 0.0;
+          const int64_t i = rows[t].pos - past_len;
+          const int32_t h = head[rows[t].r];
+          for (int32_t e = 0; e < d; ++e) qt[(int64_t)e * ORC_ROWS + t] = orc_load(q, dtype, (i * Hq + h) * (int64_t)d + e);
+          for (int32_t e = 0; e < dv; ++e) acc[(int64_t)t * dv + e] = 0.0;
         }
-        const int64_t qoff = (i * Hq + h) * (int64_t)d;
-        /* pass 1: logits and their maximum */
-        double m = -INFINITY;
-        for (int64_t j = lo; j < hi; ++j) {
-          const int64_t koff = (j * Hkv + g) * (int64_t)d;
-          double dot = 0.0;
-          for (int32_t e = 0; e < d; ++e)
-            dot += orc_load(q, dtype, qoff + e) * orc_load(k, dtype, koff + e);
-          s[j - lo] = scale * dot;
-          if (s[j - lo] > m) m = s[j - lo];
+        /* pass 1: logits and their maxima */
+        for (int64_t j = (j_lo < 0 ? 0 : j_lo); j < j_hi; ++j) {
+          orc_widen(k, dtype, (j * Hkv + g) * (int64_t)d, d, kd);
+          for (int32_t t = 0; t < nr; ++t) dot[t] = 0.0;
+          for (int32_t e = 0; e < d; ++e) {
+            const double ke = kd[e];
+            const double* qe = qt + (int64_t)e * ORC_ROWS;
+            for (int32_t t = 0; t < nr; ++t) dot[t] += qe[t] * ke;
+          }
+          for (int32_t t = 0; t < nr; ++t) {
+            if (j < lo[t] || j >= hi[t]) continue;
+            const double sj = scale * dot[t];
+            s[(int64_t)t * span + j] = sj;
+            if (sj > m[t]) m[t] = sj;
+          }
         }
-        /* pass 2: weights, normaliser, weighted sum of values */
-        double l = 0.0;
-        for (int32_t e = 0; e < dv; ++e) acc[e] = 0.0;
-        for (int64_t j = lo; j < hi; ++j) {
-          const double w = exp(s[j - lo] - m);
-          l += w;
-          const int64_t voff = (j * Hkv + g) * (int64_t)dv;
-          for (int32_t e = 0; e < dv; ++e) acc[e] += w * orc_load(v, dtype, voff + e);
+        /* pass 2: weights, normalisers, weighted sums of values */
+        for (int64_t j = (j_lo < 0 ? 0 : j_lo); j < j_hi; ++j) {
+          orc_widen(v, dtype, (j * Hkv + g) * (int64_t)dv, dv, vd);
+          for (int32_t t = 0; t < nr; ++t) {
+            if (j < lo[t] || j >= hi[t]) continue;
+            const double w = exp(s[(int64_t)t * span + j] - m[t]);
+            l[t] += w;
+            double* a = acc + (int64_t)t * dv;
+            for (int32_t e = 0; e < dv; ++e) a[e] += w * vd[e];
+          }
         }
-        for (int32_t e = 0; e < dv; ++e) o[e] = acc[e] / l;
-        lse[r] = m + log(l);
+        for (int32_t t = 0; t < nr; ++t) {
+          const int64_t r = rows[t].r;
+          double* o = out + r * dv;
+          if (hi[t] <= lo[t]) {
+            for (int32_t e = 0; e < dv; ++e) o[e] = 0.0;
+            lse[r] = -INFINITY;
+            continue;
+          }
+          for (int32_t e = 0; e < dv; ++e) o[e] = acc[(int64_t)t * dv + e] / l[t];
+          lse[r] = m[t] + log(l[t]);
+        }
       }
     }
     free(s);
     free(acc);
+    free(qt);
+    free(kd);
+    free(vd);
   }
+  free(order);
+  free(block_start);
   return err;
 }
 

@@ -6,13 +6,12 @@ count), and seeded sampled rows are compared with the fp64 oracle, which
 reads the same inputs copied to the host.  The sample always includes each
 chunk's first and last token and tokens on both sides of tile boundaries.
 
-Row counts per chunk: 4096 for the 32K and 128K prompts, 256 for the 512K
-MLA-shaped prompt (4096 with CHUNKATTN_FULL_SAMPLES=1; the fp64 oracle needs
-~8 CPU-minutes on 16 cores for that), every decode row and 2048 prefill rows
-of the mixed batch (all 65536 with CHUNKATTN_FULL_SAMPLES=1).
+Row counts per chunk: 4096 for the 32K, 128K and 512K MLA-shaped prompts
+(the last as its workload states), and every row of the mixed batch: all
+8192 decode rows and all 65536 rows of its 2048-token prefill chunk.  The
+fp64 oracle needs a few CPU-minutes on 16 host cores for all of it.
 """
 import math
-import os
 
 import numpy as np
 import pytest
@@ -24,7 +23,6 @@ from chunked_prefill_causal_amd import inputs
 from gpu_common import BF16_TOL, LSE_TOL, log, max_err, oracle_rows, require_gpu
 
 pytestmark = pytest.mark.gpu
-FULL = os.environ.get("CHUNKATTN_FULL_SAMPLES") == "1"
 
 
 @pytest.fixture(autouse=True, scope="module")
@@ -72,7 +70,7 @@ def test_gqa_128k_all_chunks():
 
 
 def test_mla_512k_all_chunks():
-    run_prompt("mla_512k", 4096 if FULL else 256)
+    run_prompt("mla_512k", 4096)
 
 
 def test_mixed_batch_full_size():
@@ -113,15 +111,12 @@ def test_mixed_batch_full_size():
         worst = max(worst, max_err(out[row], ref))
         worst_lse = max(worst_lse, max_err(lse[:, row], ref_lse))
     log(f"mixed: 256 decode requests x {hq} heads, max err {worst:.3e}, lse err {worst_lse:.2e}")
-    # sampled prefill rows
-    if FULL:    # every (token, head) row of the chunk
-        tok = np.repeat(np.arange(w.chunk_len, dtype=np.int64), hq)
-        head = np.tile(np.arange(hq, dtype=np.int32), w.chunk_len)
-    else:
-        tok, head = inputs.sample_rows(w.chunk_len, hq, 2048, w.seed * 13)
+    # every (token, head) row of the prefill chunk
+    tok = np.repeat(np.arange(w.chunk_len, dtype=np.int64), hq)
+    head = np.tile(np.arange(hq, dtype=np.int32), w.chunk_len)
     ref, ref_lse = oracle_rows(q_host[: w.chunk_len], kv_host[0][0], kv_host[0][1], w.prefill_past, w.scale,
                                tok, head)
     ti, hi = torch.from_numpy(tok).cuda(), torch.from_numpy(head.astype(np.int64)).cuda()
     e, el = max_err(out[ti, hi], ref), max_err(lse[hi, ti], ref_lse)
-    log(f"mixed: prefill chunk {len(tok)} sampled rows, max err {e:.3e}, lse err {el:.2e}")
+    log(f"mixed: prefill chunk, all {len(tok)} rows, max err {e:.3e}, lse err {el:.2e}")
     assert max(worst, e) <= BF16_TOL and max(worst_lse, el) <= LSE_TOL
