@@ -62,7 +62,9 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=5)
     p.add_argument("--warmup", type=int, default=2)
-    p.add_argument("--cpu-rows", type=int, default=1024, help="oracle rows sampled per chunk for the CPU baseline")
+    p.add_argument("--cpu-rows", type=int, default=4096, help="oracle rows sampled per chunk for the CPU baseline")
+    p.add_argument("--curve-reps", type=int, default=3,
+                   help="repetitions per chunk for the 32K and 512K MLA-shaped prompt curves")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--reps", type=int, default=10, help="repetitions for the decode-only / prefill-only timings")
     p.add_argument("--copy-calibration", action="store_true",
@@ -233,10 +235,10 @@ def mfma_counter_summary(mfma_dir):
 
 
 class PrefillLoop:
-    """The long prompt: paged pool, block table, every chunk's queries, one output buffer."""
+    """A chunked prompt: paged pool, block table, every chunk's queries, one output buffer."""
 
-    def __init__(self, L, inputs, torch):
-        w = inputs.WORKLOADS["gqa_128k"]
+    def __init__(self, L, inputs, torch, name="gqa_128k", keep_logical=True):
+        w = inputs.WORKLOADS[name]
         self.w = w
         n, hkv, d, dv = w.seq_len, w.kv_heads, w.head_dim, w.head_dim_v
         needed = math.ceil(n / 64)
@@ -247,7 +249,9 @@ class PrefillLoop:
         kk = inputs.normal_device((n, hkv, d), w.seed + 1, "bf16")
         vv = inputs.normal_device((n, hkv, dv), w.seed + 2, "bf16")
         L.chunkattn_kv_append(kk, vv, 0, self.table, self.k, self.v)
-        self.k_logical, self.v_logical = kk, vv        # kept for the oracle sample
+        if keep_logical:
+            self.k_logical, self.v_logical = kk, vv    # kept for the oracle sample
+        del kk, vv
         self.q = [inputs.normal_device((w.chunk_len, w.heads, d), inputs.chunk_seeds(w, c), "bf16")
                   for c in range(w.n_chunks)]
         self.out = torch.empty((w.chunk_len, w.heads, dv), dtype=torch.bfloat16, device="cuda")
@@ -442,6 +446,125 @@ def chunk_latency_stats(L, loop, torch, reps):
     return {"reps": reps, "median_ms": [round(x[0], 3) for x in warm], "p10_ms": [round(x[1], 3) for x in warm],
             "p90_ms": [round(x[2], 3) for x in warm], "cold_ms": [round(x, 3) for x in cold],
             "cold_note": "one call per chunk right after writing a 512 MiB buffer (L2 and MALL evicted)"}
+
+
+def prompt_curve(L, inputs, torch, name, reps):
+    """Per-chunk latency of a whole prompt (every chunk `reps` times, median), its linear fit and the
+    chunk loop's causal-effective TFLOP/s against the dense bf16 peak."""
+    loop = PrefillLoop(L, inputs, torch, name, keep_logical=False)
+    w = loop.w
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for c in range(w.n_chunks):
+        loop.run_chunk(L, c)
+    per = []
+    for c in range(w.n_chunks):
+        ts = []
+        for _ in range(reps):
+            e0.record()
+            loop.run_chunk(L, c)
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        per.append(median(ts))
+    a, b, r2 = fit_line(list(range(w.n_chunks)), per)
+    tflops = sum(loop.flops) / (sum(per) / 1e3) / 1e12
+    out = {"workload": f"{w.seq_len}-token prompt as {w.n_chunks} chunks of {w.chunk_len}, {w.heads} q / "
+                       f"{w.kv_heads} KV heads, d {w.head_dim}/{w.head_dim_v}, bf16, paged KV block 64",
+           "reps": reps, "per_chunk_ms": [round(x, 4) for x in per],
+           "per_chunk_tflops": [round(f / (t / 1e3) / 1e12, 1) for f, t in zip(loop.flops, per)],
+           "fit": {"a_ms": round(a, 4), "b_ms_per_chunk": round(b, 4), "r2": round(r2, 5),
+                   "b_over_a": round(b / a, 3) if a else None},
+           "loop_ms": round(sum(per), 3), "tflops": round(tflops, 1),
+           "frac": round(tflops / PEAK_BF16_TFLOPS, 4)}
+    del loop
+    torch.cuda.empty_cache()
+    return out
+
+
+def copy_bandwidth(torch, nbytes=1 << 30, reps=5):
+    """A plain device copy and a plain reduction over 1 GiB (torch kernels): what the memory system gives
+    these access patterns, as a sanity figure beside the decode rooflines."""
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def t(fn):
+        fn()
+        ts = []
+        for _ in range(reps):
+            torch.cuda.synchronize()
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return median(ts)
+
+    copy_ms = t(lambda: dst.copy_(src))
+    read_ms = t(lambda: src.sum())
+    del src, dst
+    return {"bytes": nbytes, "copy_gbps": round(2 * nbytes / (copy_ms / 1e3) / 1e9, 1),
+            "read_gbps": round(nbytes / (read_ms / 1e3) / 1e9, 1),
+            "note": "copy counts bytes read + written; read is a sum over the buffer; peak 8000 GB/s"}
+
+
+class GpuMonitor:
+    """Samples the GPU's shader (GFX) clock and socket power with amdsmi, read-only, from a thread while
+    a region runs; every figure is None where the interface is not available."""
+
+    def __init__(self, period_s=0.025):
+        import threading
+        self.period, self.samples, self._stop = period_s, [], threading.Event()
+        self.handle, self.cap_w = None, None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            self.amdsmi = amdsmi
+            self.handle = amdsmi.amdsmi_get_processor_handles()[0]
+            cap = amdsmi.amdsmi_get_power_cap_info(self.handle)
+            self.cap_w = cap.get("power_cap", None)
+            if self.cap_w is not None and self.cap_w > 10000:
+                self.cap_w = self.cap_w / 1e6            # reported in microwatts on some versions
+        except Exception:
+            self.handle = None
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    def _read(self):
+        clk = self.amdsmi.amdsmi_get_clock_info(self.handle, self.amdsmi.AmdSmiClkType.GFX)
+        pwr = self.amdsmi.amdsmi_get_power_info(self.handle)
+        mhz = clk.get("clk", clk.get("cur_clk"))
+        watts = pwr.get("current_socket_power", "N/A")
+        if not isinstance(watts, (int, float)):
+            watts = pwr.get("average_socket_power", None)
+        return mhz, watts if isinstance(watts, (int, float)) else None
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                self.samples.append(self._read())
+            except Exception:
+                return
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        if self.handle is not None:
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self.handle is not None:
+            self._thread.join()
+
+    def summary(self):
+        clk = [c for c, _ in self.samples if isinstance(c, (int, float))]
+        pw = [p for _, p in self.samples if isinstance(p, (int, float))]
+        if not clk:
+            return {"gfx_clock_mhz": None, "note": "amdsmi not available"}
+        return {"samples": len(self.samples), "gfx_clock_mhz_median": median(clk), "gfx_clock_mhz_min": min(clk),
+                "gfx_clock_mhz_max": max(clk), "socket_power_w_median": median(pw) if pw else None,
+                "power_cap_w": self.cap_w,
+                "note": "amdsmi GFX clock and socket power sampled every 25 ms during the timed steps"}
 
 
 def median(xs):
@@ -657,16 +780,18 @@ def main():
     log(f"timing {args.steps} step(s)")
     chunk_ms = [[] for _ in range(n_chunks)]
     mixed_ms = []
+    monitor = GpuMonitor()
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step(True)
+    with monitor:
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step(True)
+            torch.cuda.synchronize()
+            for c in range(n_chunks):
+                chunk_ms[c].append(ev[c][0].elapsed_time(ev[c][1]))
+            mixed_ms.append(ev[n_chunks][0].elapsed_time(ev[n_chunks][1]))
         torch.cuda.synchronize()
-        for c in range(n_chunks):
-            chunk_ms[c].append(ev[c][0].elapsed_time(ev[c][1]))
-        mixed_ms.append(ev[n_chunks][0].elapsed_time(ev[n_chunks][1]))
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+        wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
     step_flops = sum(loop.flops) + mixed.flops
     value = step_flops / (ms_per_step / 1e3) / 1e12
@@ -687,6 +812,15 @@ def main():
     contig = contiguous_cache_summary(L, loop, torch, timed, args.reps)
     log(f"contiguous cache, chunks {contig['chunks']}: {contig['ms']} ms ({contig['tflops']} TFLOP/s); "
         f"paged pool {contig['paged_ms']} ms")
+    log("copy-bandwidth sanity figure")
+    bw = copy_bandwidth(torch)
+    log(f"1 GiB copy {bw['copy_gbps']} GB/s, read {bw['read_gbps']} GB/s")
+    curves = {}
+    for name in ("gqa_32k", "mla_512k"):
+        log(f"per-chunk latency curve of {name}")
+        curves[name] = prompt_curve(L, inputs, torch, name, args.curve_reps)
+        log(f"{name}: chunk loop {curves[name]['loop_ms']} ms = {curves[name]['tflops']} TFLOP/s "
+            f"({100 * curves[name]['frac']:.1f}% of bf16 peak)")
 
     if args.copy_calibration:
         src = torch.empty(CALIB_BYTES, dtype=torch.uint8, device="cuda")
@@ -773,6 +907,9 @@ def main():
                                 "unit": "GB/s", "frac": round(dec_gbps / PEAK_HBM_GBPS, 4),
                                 "algorithmic_bytes": mixed.decode_bytes},
         },
+        "gpu_clock_power": monitor.summary(),
+        "copy_bandwidth": bw,
+        "other_prompts": curves,
         "contiguous_cache": contig,
         "mla_decode": mla,
         "schedule_sim": sched,

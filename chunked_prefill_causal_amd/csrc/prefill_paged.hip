@@ -219,6 +219,8 @@ __global__ __launch_bounds__(512, 1) void prefill_paged_kernel(const PrefillArgs
     pos[qb] = P + (row_valid[qb] ? t[qb] : c - 1);
   }
   const int64_t wave_first_pos = P + min(t0, c - 1);
+  const int wave_first_pos32 = __builtin_amdgcn_readfirstlane((int)wave_first_pos);
+  const int kv_len32 = __builtin_amdgcn_readfirstlane((int)kv_len);
   const float cs = a.scale_log2;
 
   if (j_lo >= j_hi) {
@@ -350,8 +352,8 @@ __global__ __launch_bounds__(512, 1) void prefill_paged_kernel(const PrefillArgs
   // and its exps redone.  Otherwise each exp stays below kPsumCap, which keeps
   // the fp32 sums far from overflow, so the result is the same softmax.
   auto softmax = [&](int j, bool first) {
-    const int64_t key0 = (int64_t)j * kBlock;
-    if (key0 + kBlock - 1 > wave_first_pos) {
+    const int key0 = j * kBlock;                 // positions stay below 2^30 (the boundary checks it)
+    if (key0 + kBlock - 1 > wave_first_pos32) {
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
         const int lim = (int)(pos[qb] - key0) - 8 * lg;   // register offsets past lim are invisible
@@ -384,7 +386,8 @@ __global__ __launch_bounds__(512, 1) void prefill_paged_kernel(const PrefillArgs
     };
     exps();
     row_sums();
-    if (first || __any(!(psum[0] <= kPsumCap) || !(psum[1] <= kPsumCap))) {
+    if (first || (__builtin_amdgcn_ballot_w64(!(psum[0] <= kPsumCap)) |
+                  __builtin_amdgcn_ballot_w64(!(psum[1] <= kPsumCap))) != 0) {
       float mx[2];
       bool grow[2];
 #pragma unroll
@@ -539,8 +542,8 @@ __global__ __launch_bounds__(512, 1) void prefill_paged_kernel(const PrefillArgs
       else if (wave < 4) prep(block_ahead, (i + NS - 2) % NS);   // issued inside pv_qk_dma
     }
     block_ahead = (i + NS - 1 < n) ? bt4[i + NS - 1] : 0;
-    const int64_t key0 = (int64_t)(j_lo + i) * kBlock;
-    if (i < n && key0 + kBlock > kv_len) {
+    const int key0 = (j_lo + i) * kBlock;
+    if (i < n && key0 + kBlock > kv_len32) {
       // The tile holding the sequence end: zero its values of keys >= kv_len
       // in LDS (a masked key has probability 0, but 0 * NaN would poison the
       // sum).  Nobody reads this V before the next barrier.
