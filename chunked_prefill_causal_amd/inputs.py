@@ -28,6 +28,10 @@ Recipe (fixed here, stated once):
     [kv, 64] drawn N(0, 1) on the device from one seeded generator, rounded to
     bf16; queries [requests, heads, 576] N(0, 1) bf16 (GLM5.3 PP-split
     deployment notes §1, §4: one shared latent record per token).
+  * MLA prefill prompt: latents [L, 512] then rotary parts [L, 64] of the one
+    sequence from one seeded device generator (``mla_record_seed(w, 0)``),
+    rounded to bf16; chunk k's queries [chunk, heads, 576] N(0, 1) bf16 from
+    ``chunk_seeds(w, k)``.
   * sampled rows: every chunk's first and last token, tokens on both sides of
     every 64- and 128-token tile boundary (a bounded subset when there are
     many), and a seeded uniform fill; heads uniform.
@@ -100,6 +104,12 @@ WORKLOADS = {
         "per token (bf16 or fp8 latent cache), paged KV (64)",
         0, 0, 16, 1, 576, 512, "bf16", "paged", seed=606,
         decode_requests=256, decode_ctx=(1024, 32768), scale_dim=192),
+    # absorbed MLA chunked prefill: a 128K-token prompt in 8192-token chunks, 16 q heads attending to the
+    # shared latent records (bf16 latent cache)
+    "mla_prefill": Workload(
+        "mla_prefill", "L=131072 as 16 chunks of 8192, 16 q heads over one shared 512+64 latent record per "
+        "token (bf16 latent cache), paged KV (64)",
+        131072, 8192, 16, 1, 576, 512, "bf16", "paged", seed=707, sample_rows=512, scale_dim=192),
 }
 
 

@@ -26,6 +26,10 @@ Readings (also in the design notes):
   records this is plain attention with d_qk = 576, d_v = 512 and one KV head
   shared by every query head — computed by the package's fp64 oracle.
 * A decode query sits at position kv_len - 1 and sees all kv_len records.
+* Absorbed prefill (VPP review §2.3, chunked prefill; §2.2 Eq. (1) for the
+  causal rule): a chunk of c tokens at positions past_len .. past_len + c - 1
+  of one sequence; every head of the token at position p sees records
+  0 .. p.  The same plain attention, row by row.
 """
 from __future__ import annotations
 
@@ -117,3 +121,22 @@ def decode(q, recs, scale: float, threads: int | None = None):
     out, lse = _orc.attend_rows(q, k, v, k.shape[0] - 1, scale, np.zeros(heads, np.int64),
                                 np.arange(heads, dtype=np.int32), threads=threads)
     return out, lse
+
+
+def prefill(q, recs, past_len: int, scale: float, tok=None, head=None, threads: int | None = None):
+    """Absorbed prefill of one chunk: q [c, H, 576] (bf16 bit patterns as uint16, or fp64 values),
+    records [>= past_len + c, 576] (fp64) of the sequence.  Row (tok[i], head[i]) sits at position
+    past_len + tok[i] and sees records 0 .. past_len + tok[i].  Every row by default.
+    Returns out [n, 512] and lse [n] (natural log), fp64."""
+    q = np.asarray(q)
+    q = _orc.bf16_bits_to_f64(q) if q.dtype == np.uint16 else np.asarray(q, dtype=np.float64)
+    c, heads = q.shape[0], q.shape[1]
+    q = np.ascontiguousarray(q).reshape(c, heads, RECORD)
+    if tok is None:
+        tok = np.repeat(np.arange(c, dtype=np.int64), heads)
+        head = np.tile(np.arange(heads, dtype=np.int32), c)
+    n_keys = past_len + c
+    k = np.ascontiguousarray(np.asarray(recs, dtype=np.float64)[:n_keys]).reshape(n_keys, 1, RECORD)
+    v = np.ascontiguousarray(k[:, :, :LATENT])
+    return _orc.attend_rows(q, k, v, past_len, scale, np.asarray(tok, dtype=np.int64),
+                            np.asarray(head, dtype=np.int32), threads=threads)

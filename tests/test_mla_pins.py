@@ -16,6 +16,11 @@
   The expanded side runs through the package's general fp64 oracle with one KV
   head per query head, a different wiring from the shared-latent path.
 * Special cases: one record, a zero query (uniform average, LSE = log L).
+* Absorbed prefill of a chunk at past_len > 0: a zero query averages exactly
+  the records 0 .. its position (LSE = log(position + 1)), so an off-by-one in
+  the causal range or in past_len fails; the first position of a sequence
+  returns record 0's latent; records after a row's position (or past the
+  chunk) never change it; and the chunk equals the expanded multi-head form.
 """
 import math
 
@@ -186,3 +191,62 @@ def test_decode_special_cases():
     recs2 = recs.copy()
     recs2[:, 512:] = rng.normal(0, 1, (50, 64))
     assert np.allclose(mla.decode(q0, recs2, 0.3)[0], out, rtol=1e-13, atol=1e-14)
+
+
+# ---------------------------------------------------------- absorbed prefill
+def test_prefill_zero_query_averages_the_visible_records():
+    rng = np.random.default_rng(8)
+    past, c, heads = 45, 7, 16
+    recs = rng.normal(0, 1, (past + c, 576))
+    out, lse = mla.prefill(np.zeros((c, heads, 576)), recs, past, 0.2)
+    for t in range(c):
+        p = past + t
+        for h in (0, 9, 15):
+            i = t * heads + h
+            assert np.allclose(out[i], recs[: p + 1, :512].mean(axis=0), rtol=1e-12, atol=1e-13)
+            assert math.isclose(lse[i], math.log(p + 1), rel_tol=1e-13)
+
+
+def test_prefill_first_position_and_causality():
+    rng = np.random.default_rng(9)
+    c, heads = 9, 32
+    recs = rng.normal(0, 1, (c, 576))
+    q = f32_to_bf16_bits(rng.normal(0, 1, (c, heads, 576)))
+    out, lse = mla.prefill(q, recs, 0, 0.07)
+    # position 0 sees record 0 alone
+    assert np.array_equal(out[:heads], np.broadcast_to(recs[0, :512], (heads, 512)))
+    assert np.allclose(lse[:heads], 0.07 * orc.bf16_bits_to_f64(q[0]) @ recs[0], rtol=1e-13, atol=1e-13)
+    # records after a row's position do not move it: perturb record 5 onwards
+    recs2 = recs.copy()
+    recs2[5:] = rng.normal(0, 3, (c - 5, 576))
+    out2, lse2 = mla.prefill(q, recs2, 0, 0.07)
+    assert np.array_equal(out2[: 5 * heads], out[: 5 * heads]) and np.array_equal(lse2[: 5 * heads], lse[: 5 * heads])
+    assert not np.allclose(out2[5 * heads:], out[5 * heads:])
+    # records beyond the chunk are never read
+    more = np.concatenate([recs, np.full((4, 576), np.nan)])
+    out3, _ = mla.prefill(q, more, 0, 0.07)
+    assert np.array_equal(out3, out)
+
+
+def test_prefill_chunk_equals_expanded_attention():
+    rng = np.random.default_rng(10)
+    heads, past, c, dn, dr = 4, 29, 6, 128, 64
+    L = past + c
+    lat = rng.normal(0, 1, (L, 512))
+    rope = rng.normal(0, 1, (L, 64))
+    w_uk = rng.normal(0, 512 ** -0.5, (heads, dn, 512))
+    w_uv = rng.normal(0, 512 ** -0.5, (heads, dn, 512))
+    q_nope = rng.normal(0, 1, (c, heads, dn))
+    q_rope = rng.normal(0, 1, (c, heads, dr))
+    scale = 1 / math.sqrt(dn + dr)
+    k = np.concatenate([np.einsum("hdc,lc->lhd", w_uk, lat), np.broadcast_to(rope[:, None, :], (L, heads, dr))], 2)
+    v = np.einsum("hdc,lc->lhd", w_uv, lat)
+    tok = np.repeat(np.arange(c, dtype=np.int64), heads)
+    head = np.tile(np.arange(heads, dtype=np.int32), c)
+    ref_out, ref_lse = orc.attend_rows(np.concatenate([q_nope, q_rope], 2), np.ascontiguousarray(k),
+                                       np.ascontiguousarray(v), past, scale, tok, head)
+    q_abs = np.concatenate([np.einsum("hdc,thd->thc", w_uk, q_nope), q_rope], 2)
+    out_lat, lse = mla.prefill(q_abs, np.concatenate([lat, rope], 1), past, scale)
+    out = np.stack([w_uv[h] @ out_lat[i] for i, h in enumerate(head)])
+    assert np.allclose(out, ref_out, rtol=1e-10, atol=1e-12)
+    assert np.allclose(lse, ref_lse, rtol=1e-12, atol=1e-12)
