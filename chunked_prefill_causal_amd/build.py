@@ -20,7 +20,7 @@ LIB = os.path.join(HERE, "libchunkattn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["prefill.hip", "prefill_paged.hip", "decode.hip", "kv_append.hip", "mla.hip", "api.cpp", "schedule.cpp", "alp.cpp"]
+SOURCES = ["prefill.hip", "prefill_paged.hip", "decode.hip", "kv_append.hip", "mla.hip", "mla_prefill.hip", "api.cpp", "schedule.cpp", "alp.cpp"]
 FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          # the direct-to-LDS loads set m0 in inline asm, which clang flags as a reserved register

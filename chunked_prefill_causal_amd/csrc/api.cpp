@@ -793,4 +793,41 @@ ca_status chunk_mla_decode(const void* q, const void* pool, int32_t format, cons
   return hip_status(launch_mla_decode(format == CA_MLA_FP8, a, (hipStream_t)stream), "MLA decode launch");
 }
 
+ca_status chunk_mla_prefill(const void* q, const void* pool, int32_t format, const int32_t* block_table,
+                            int32_t block_table_len, int32_t num_blocks, int64_t past_len, int64_t chunk_len,
+                            int32_t heads, float scale, void* out, int32_t out_dtype, float* lse_out, void* stream) {
+  if (format != CA_MLA_BF16 && format != CA_MLA_FP8) return fail(CA_EINVAL, "unknown MLA cache format %d", format);
+  if (format == CA_MLA_FP8) return fail(CA_EUNSUPPORTED, "MLA prefill reads the bf16 latent cache only");
+  if (heads <= 0 || heads % 16 || heads > 1024)
+    return fail(CA_EUNSUPPORTED, "heads must be a positive multiple of 16 up to 1024, got %d", heads);
+  if (past_len < 0 || chunk_len < 0) return fail(CA_EINVAL, "past_len and chunk_len must be >= 0");
+  if (out_dtype != CA_BF16 && out_dtype != CA_F32) return fail(CA_EINVAL, "out_dtype must be CA_BF16 or CA_F32");
+  if (!(scale > 0.f) || !std::isfinite(scale)) return fail(CA_EINVAL, "scale must be finite and > 0");
+  if (num_blocks <= 0) return fail(CA_EINVAL, "num_blocks must be > 0");
+  // positions, row blocks and the grid stay in 32-bit ranges
+  if (past_len + chunk_len > ((int64_t)1 << 30) || chunk_len * (heads / 16) > ((int64_t)1 << 31) - 8)
+    return fail(CA_ERANGE, "past_len + chunk_len = %lld is too long", (long long)(past_len + chunk_len));
+  if (chunk_len == 0) return ok();
+  if ((int64_t)block_table_len * kBlock < past_len + chunk_len)
+    return fail(CA_ERANGE, "block table covers %lld tokens, need %lld", (long long)block_table_len * kBlock,
+                (long long)(past_len + chunk_len));
+  if (!q || !pool || !block_table || !out) return fail(CA_EINVAL, "null pointer argument");
+  if (!aligned(q, 16) || !aligned(pool, 16) || !aligned(out, 16) || !aligned(block_table, 4) ||
+      (lse_out && !aligned(lse_out, 4)))
+    return fail(CA_EINVAL, "misaligned pointer argument");
+  MlaPrefillArgs a;
+  a.q = (const uint16_t*)q;
+  a.pool = (const unsigned char*)pool;
+  a.block_table = block_table;
+  a.out = out;
+  a.lse = lse_out;
+  a.past_len = past_len;
+  a.chunk_len = chunk_len;
+  a.num_blocks = num_blocks;
+  a.heads = heads;
+  a.out_f32 = out_dtype == CA_F32 ? 1 : 0;
+  a.scale_log2 = scale * kLog2e;
+  return hip_status(launch_mla_prefill(false, a, (hipStream_t)stream), "MLA prefill launch");
+}
+
 }  // extern "C"

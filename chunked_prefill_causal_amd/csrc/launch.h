@@ -130,7 +130,22 @@ struct MlaAppendArgs {
   int32_t num_blocks;
 };
 
+// MLA latent prefill of one prompt chunk: tokens past_len .. past_len + chunk_len - 1
+// of one sequence, every head attending causally to the records 0 .. its position.
+struct MlaPrefillArgs {
+  const uint16_t* q;             // [chunk_len, heads, 576] bf16
+  const unsigned char* pool;     // [num_blocks][block bytes]
+  const int32_t* block_table;    // [ceil((past_len + chunk_len) / 64)]
+  void* out;                     // [chunk_len, heads, 512] bf16 or fp32
+  float* lse;                    // [heads, chunk_len] or null
+  int64_t past_len, chunk_len;
+  int32_t num_blocks, heads;     // heads: a multiple of 16
+  int32_t out_f32;
+  float scale_log2;
+};
+
 hipError_t launch_mla_decode(bool fp8, const MlaArgs& a, hipStream_t stream);
+hipError_t launch_mla_prefill(bool fp8, const MlaPrefillArgs& a, hipStream_t stream);
 hipError_t launch_mla_append(bool fp8, const MlaAppendArgs& a, hipStream_t stream);
 
 hipError_t launch_block_iota(int32_t* table, int n, hipStream_t stream);

@@ -277,6 +277,40 @@ def test_mla_decode_empty_batch_succeeds():
     assert mla_decode(q=None, out=None, kv=(), ws=None) == L.CA_OK
 
 
+def mla_prefill(q=FAKE, fmt=L.CA_MLA_BF16, table_len=8, num_blocks=8, past=100, chunk=300, heads=16, scale=0.1,
+                out=FAKE, out_dtype=L.CA_BF16, lse=None):
+    return L.lib().chunk_mla_prefill(q, FAKE, fmt, FAKE, table_len, num_blocks, past, chunk, heads, scale, out,
+                                     out_dtype, lse, None)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(fmt=2), L.CA_EINVAL),
+    (dict(fmt=L.CA_MLA_FP8), L.CA_EUNSUPPORTED),
+    (dict(heads=8), L.CA_EUNSUPPORTED),
+    (dict(heads=2048), L.CA_EUNSUPPORTED),
+    (dict(past=-1), L.CA_EINVAL),
+    (dict(chunk=-5), L.CA_EINVAL),
+    (dict(past=300, chunk=213), L.CA_ERANGE),           # 513 tokens > 8 blocks of 64
+    (dict(past=1 << 30, chunk=1), L.CA_ERANGE),
+    (dict(scale=0.0), L.CA_EINVAL),
+    (dict(scale=float("inf")), L.CA_EINVAL),
+    (dict(q=None), L.CA_EINVAL),
+    (dict(out=None), L.CA_EINVAL),
+    (dict(q=MISALIGNED), L.CA_EINVAL),
+    (dict(lse=FAKE + 2), L.CA_EINVAL),
+    (dict(num_blocks=0), L.CA_EINVAL),
+    (dict(out_dtype=5), L.CA_EINVAL),
+])
+def test_mla_prefill_rejections(kwargs, status):
+    assert mla_prefill(**kwargs) == status
+    assert L.lib().chunkattn_last_error().decode()
+
+
+def test_mla_prefill_empty_chunk_succeeds():
+    # 512 tokens fill the 8 blocks exactly: in range; an empty chunk launches nothing
+    assert mla_prefill(q=None, out=None, chunk=0) == L.CA_OK
+
+
 def test_mla_append_rejections():
     lib = L.lib()
     f = lambda **kw: lib.chunkattn_mla_kv_append(kw.get("lat", FAKE), FAKE, kw.get("start", 0), kw.get("n", 10),

@@ -297,3 +297,83 @@ def test_decode_batch_workload_sampled(fmt):
         worst_lse = max(worst_lse, max_err(lse[:, s], ref_lse))
     log(f"  sampled {sample}: max abs err {worst:.3e} lse {worst_lse:.3e}")
     assert worst <= BF16_TOL and worst_lse <= LSE_TOL
+
+
+# ------------------------------------------------------------- chunked prefill
+# VPP review §2.3: a prompt is cut into chunks; each chunk's records are appended
+# to the cache, then its queries attend to every earlier record and causally to
+# the chunk itself.  Pools start as 0xFF (NaN) everywhere: unowned blocks, block
+# tails and the positions of later chunks must never reach an output.
+def prompt_records(n, seed, rope_scale=None):
+    """Latents and rotary parts of one prompt.  ``rope_scale(pos)`` multiplies the rotary parts: that moves
+    the logits (and so the running maxima) while the values, the latents, stay N(0, 1)."""
+    lat = inputs.normal((n, 512), seed, "f32")
+    rope = inputs.normal((n, 64), seed + 1, "f32")
+    if rope_scale is not None:
+        rope = rope * torch.from_numpy(rope_scale(np.arange(n)).astype(np.float32))[:, None]
+    return lat.to(torch.bfloat16), rope.to(torch.bfloat16)
+
+
+def check_prefill(chunks, heads, seed, out_dtype=torch.bfloat16, rope_scale=None, sample=None):
+    n = sum(chunks)
+    lat, rope = prompt_records(n, seed, rope_scale)
+    recs = mla.records(bits(lat), bits(rope), "bf16")
+    needed = math.ceil(n / 64)
+    nb = inputs.pool_size(needed)
+    table = torch.from_numpy(inputs.block_table(needed, seed + 2, nb)).cuda()
+    pool = new_pool("bf16", nb, POISON)
+    worst = worst_excess = worst_lse = 0.0
+    past = 0
+    for ci, c in enumerate(chunks):
+        L.chunkattn_mla_kv_append(lat[past: past + c].cuda(), rope[past: past + c].cuda(), past, table, pool,
+                                  L.CA_MLA_BF16)
+        q = inputs.normal((c, heads, 576), seed + 10 + ci, "bf16")
+        log(f"mla prefill heads={heads} out={out_dtype} chunk {ci}: past {past} len {c} seed {seed}")
+        out, lse = L.chunk_mla_prefill(q.cuda(), pool, L.CA_MLA_BF16, table, past, SCALE, out_dtype=out_dtype,
+                                       return_lse=True)
+        torch.cuda.synchronize()
+        out = out.float().cpu().numpy().astype(np.float64)
+        lse = lse.cpu()
+        assert np.all(np.isfinite(out)) and torch.isfinite(lse).all(), "non-finite GPU output"
+        if sample is None:
+            tok = np.repeat(np.arange(c, dtype=np.int64), heads)
+            head = np.tile(np.arange(heads, dtype=np.int32), c)
+        else:
+            tok, head = inputs.sample_rows(c, heads, sample, seed * 7 + ci)
+        ref, ref_lse = mla.prefill(bits(q), recs, past, SCALE, tok, head)
+        got = out[tok, head]
+        err = np.abs(got - ref)
+        store = bf16_half_ulp(np.maximum(np.abs(ref), np.abs(got))) if out_dtype == torch.bfloat16 else 0.0
+        worst = max(worst, float(err.max()))
+        worst_excess = max(worst_excess, float((err - store).max()))
+        worst_lse = max(worst_lse, max_err(lse[head, tok], ref_lse))
+        past += c
+    log(f"  max abs err {worst:.3e} (beyond the store's rounding {worst_excess:.3e})  lse {worst_lse:.3e}")
+    assert worst_excess <= BF16_TOL and worst_lse <= LSE_TOL
+    if out_dtype == torch.float32:
+        assert worst <= BF16_TOL
+
+
+def test_prefill_multi_chunk_nan_poisoned():
+    # chunk lengths: ragged, a single token, exactly one tile, several tiles; every row compared
+    check_prefill([130, 1, 64, 200, 95, 300], 16, 7100)
+
+
+@pytest.mark.parametrize("heads,out_dtype", [(32, torch.bfloat16), (48, torch.float32), (128, torch.bfloat16)],
+                         ids=["h32", "h48-f32out", "h128"])
+def test_prefill_more_heads(heads, out_dtype):
+    check_prefill([77, 250], heads, 7200 + heads, out_dtype=out_dtype)
+
+
+def test_prefill_long_past_every_row():
+    check_prefill([5000, 700], 16, 7300, sample=None)
+
+
+def test_prefill_late_max_growth():
+    # rotary parts grow with position, so a row's running maximum keeps rising and O is rescaled many times
+    check_prefill([600, 400], 16, 7400, rope_scale=lambda p: 1.0 + 12.0 * p / 1000.0)
+
+
+def test_prefill_early_spike():
+    # one early record with very large logits for many rows, then ordinary ones: the first tile fixes the maximum
+    check_prefill([40, 900], 16, 7500, rope_scale=lambda p: np.where(p == 3, 40.0, 1.0))
