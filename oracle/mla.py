@@ -30,6 +30,9 @@ Readings (also in the design notes):
   causal rule): a chunk of c tokens at positions past_len .. past_len + c - 1
   of one sequence; every head of the token at position p sees records
   0 .. p.  The same plain attention, row by row.
+* Prefill over an fp8 cache runs its matrix products in bf16: a record
+  enters as bf16(fp32(code x scale)) (``fp8_staged_records``), one more
+  relative rounding of at most 2^-8 per value than the exact fp8 record.
 """
 from __future__ import annotations
 
@@ -107,6 +110,24 @@ def records(latent_bits, rope_bits, fmt: str) -> np.ndarray:
     elif fmt != "bf16":
         raise ValueError(fmt)
     return np.concatenate([lat, rope], axis=1)
+
+
+def f32_to_bf16_rne(x) -> np.ndarray:
+    """fp32 values rounded to bf16, nearest with ties to even, returned as fp64 (finite inputs)."""
+    b = np.asarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    b = ((b + 0x7FFF + ((b >> 16) & 1)) >> 16) << 16
+    return b.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def fp8_staged_records(latent_bits, rope_bits) -> np.ndarray:
+    """The records chunked prefill over an fp8 cache computes with: each latent value is its e4m3 code times
+    its group's fp32 scale, the product rounded to fp32 and then to bf16 (both nearest, ties to even); the
+    rotary part is bf16 already.  fp64 [n, 576]."""
+    lat = _orc.bf16_bits_to_f64(latent_bits).astype(np.float32)
+    codes, scales = quantize_latent(lat)
+    prod = e4m3_decode(codes).astype(np.float32).reshape(-1, LATENT // GROUP, GROUP) * scales[:, :, None]
+    lat_b = f32_to_bf16_rne(prod.astype(np.float32)).reshape(-1, LATENT)
+    return np.concatenate([lat_b, _orc.bf16_bits_to_f64(rope_bits)], axis=1)
 
 
 def decode(q, recs, scale: float, threads: int | None = None):

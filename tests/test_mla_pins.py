@@ -21,6 +21,9 @@
   the causal range or in past_len fails; the first position of a sequence
   returns record 0's latent; records after a row's position (or past the
   chunk) never change it; and the chunk equals the expanded multi-head form.
+* fp8 records as the prefill stages them: values representable in bf16,
+  within the bf16 rounding bound (2^-8 relative) of the exact code x scale,
+  equal to it where the scale is a power of two, and nearest-even on a tie.
 """
 import math
 
@@ -250,3 +253,24 @@ def test_prefill_chunk_equals_expanded_attention():
     out = np.stack([w_uv[h] @ out_lat[i] for i, h in enumerate(head)])
     assert np.allclose(out, ref_out, rtol=1e-10, atol=1e-12)
     assert np.allclose(lse, ref_lse, rtol=1e-12, atol=1e-12)
+
+
+def test_fp8_staged_records_round_code_times_scale_once_to_bf16():
+    rng = np.random.default_rng(11)
+    lat = rng.normal(0, 1, (40, 512)).astype(np.float32)
+    lat[0, :128] = np.float32(448.0) * np.linspace(-1, 1, 128, dtype=np.float32)   # amax 448: scale 1
+    lat[1, 128:256] = np.float32(448.0 * 2.0 ** -5) * np.sign(np.linspace(-1, 1, 128, dtype=np.float32))  # 2^-5
+    lat_bits, rope_bits = f32_to_bf16_bits(lat), f32_to_bf16_bits(rng.normal(0, 1, (40, 64)))
+    staged = mla.fp8_staged_records(lat_bits, rope_bits)
+    exact = mla.records(lat_bits, rope_bits, "fp8")
+    # representable in bf16: the low 16 bits of the fp32 pattern are zero
+    assert not np.any(staged.astype(np.float32).view(np.uint32) & 0xFFFF)
+    # within the bf16 rounding bound of the exact record; rotary parts untouched
+    assert np.all(np.abs(staged - exact) <= 2.0 ** -8 * np.abs(exact) * (1 + 2.0 ** -20))
+    assert np.array_equal(staged[:, 512:], exact[:, 512:])
+    # power-of-two scales: code x scale is exact in bf16 (a 4-bit significand)
+    assert np.array_equal(staged[0, :128], exact[0, :128]) and np.array_equal(staged[1, 128:256], exact[1, 128:256])
+    # rounding is to nearest with ties to even: 1 + 2^-8 (a tie between 1 and 1 + 2^-7) goes to 1
+    assert mla.f32_to_bf16_rne(np.float32(1 + 2.0 ** -8)) == 1.0
+    assert mla.f32_to_bf16_rne(np.float32(1 + 3 * 2.0 ** -8)) == 1 + 2 * 2.0 ** -7
+    assert mla.f32_to_bf16_rne(np.float32(1 + 2.0 ** -8 + 2.0 ** -20)) == 1 + 2.0 ** -7
