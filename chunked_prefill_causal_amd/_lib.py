@@ -33,7 +33,8 @@ EXPORTED = ("ca_prefill_opts_init", "chunk_prefill_attn", "chunkattn_prefill_wor
             "chunkattn_kv_append", "chunkattn_sched_simulate", "chunkattn_sched_drain_pack",
             "chunkattn_alp_features", "chunkattn_alp_init", "chunkattn_alp_predict", "chunkattn_alp_update",
             "chunkattn_mla_block_bytes", "chunkattn_mla_decode_workspace_size", "chunkattn_mla_kv_append",
-            "chunk_mla_decode", "chunk_mla_prefill", "chunkattn_last_error", "chunkattn_version")
+            "chunk_mla_decode", "chunkattn_mla_prefill_workspace_size", "chunk_mla_prefill",
+            "chunkattn_last_error", "chunkattn_version")
 
 
 class ChunkAttnError(RuntimeError):
@@ -115,7 +116,9 @@ def lib() -> ctypes.CDLL:
     L.chunkattn_mla_kv_append.restype = ctypes.c_int
     L.chunk_mla_decode.argtypes = [vp, vp, i32, vp, i32, i32, vp, vp, i32, i32, f32, vp, i32, vp, vp, sz, vp]
     L.chunk_mla_decode.restype = ctypes.c_int
-    L.chunk_mla_prefill.argtypes = [vp, vp, i32, vp, i32, i32, i64, i64, i32, f32, vp, i32, vp, vp]
+    L.chunkattn_mla_prefill_workspace_size.argtypes = [i64, i64, i32]
+    L.chunkattn_mla_prefill_workspace_size.restype = sz
+    L.chunk_mla_prefill.argtypes = [vp, vp, i32, vp, i32, i32, i64, i64, i32, f32, vp, i32, vp, vp, sz, vp]
     L.chunk_mla_prefill.restype = ctypes.c_int
     L.chunkattn_last_error.argtypes = []
     L.chunkattn_last_error.restype = ctypes.c_char_p
@@ -475,18 +478,22 @@ def chunk_mla_decode(q, pool, fmt: int, block_tables, kv_lens, scale: float, *, 
 
 def chunk_mla_prefill(q, pool, fmt: int, block_table, past_len: int, scale: float, *,
                       num_blocks: int | None = None, out=None, out_dtype=torch.bfloat16, return_lse: bool = False,
-                      lse=None, stream=None):
+                      lse=None, workspace=None, stream=None):
     """Absorbed MLA prefill of one chunk: ``q [chunk_len, heads, 576]`` bf16 for positions
     ``past_len ..`` of the sequence whose latent records the pool holds through ``block_table``;
     returns ``out [chunk_len, heads, 512]`` (``out_dtype``, or that of ``out``) and
-    ``lse [heads, chunk_len]`` fp32."""
+    ``lse [heads, chunk_len]`` fp32.  An fp8 pool needs a workspace (allocated when not given)."""
     c, heads, _ = q.shape
     if out is None:
         out = torch.empty((c, heads, MLA_LATENT), dtype=out_dtype, device=q.device)
     if return_lse and lse is None:
         lse = torch.empty((heads, c), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        need = lib().chunkattn_mla_prefill_workspace_size(int(past_len), c, fmt)
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device) if need else None
     _check(lib().chunk_mla_prefill(
         _ptr(q), _ptr(pool), fmt, _ptr(block_table), block_table.shape[-1],
         pool.shape[0] if num_blocks is None else num_blocks, int(past_len), c, heads, float(scale), _ptr(out),
-        _dtype_code(out.dtype), _ptr(lse), _stream(stream)))
+        _dtype_code(out.dtype), _ptr(lse), _ptr(workspace), 0 if workspace is None else workspace.numel(),
+        _stream(stream)))
     return (out, lse) if return_lse else out

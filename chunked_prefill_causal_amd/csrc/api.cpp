@@ -793,11 +793,18 @@ ca_status chunk_mla_decode(const void* q, const void* pool, int32_t format, cons
   return hip_status(launch_mla_decode(format == CA_MLA_FP8, a, (hipStream_t)stream), "MLA decode launch");
 }
 
+size_t chunkattn_mla_prefill_workspace_size(int64_t past_len, int64_t chunk_len, int32_t format) {
+  if ((format != CA_MLA_BF16 && format != CA_MLA_FP8) || past_len < 0 || chunk_len < 0 ||
+      past_len + chunk_len > ((int64_t)1 << 30))
+    return 0;
+  return (size_t)mla_prefill_staging_bytes(format == CA_MLA_FP8, past_len + chunk_len);
+}
+
 ca_status chunk_mla_prefill(const void* q, const void* pool, int32_t format, const int32_t* block_table,
                             int32_t block_table_len, int32_t num_blocks, int64_t past_len, int64_t chunk_len,
-                            int32_t heads, float scale, void* out, int32_t out_dtype, float* lse_out, void* stream) {
+                            int32_t heads, float scale, void* out, int32_t out_dtype, float* lse_out,
+                            void* workspace, size_t workspace_bytes, void* stream) {
   if (format != CA_MLA_BF16 && format != CA_MLA_FP8) return fail(CA_EINVAL, "unknown MLA cache format %d", format);
-  if (format == CA_MLA_FP8) return fail(CA_EUNSUPPORTED, "MLA prefill reads the bf16 latent cache only");
   if (heads <= 0 || heads % 16 || heads > 1024)
     return fail(CA_EUNSUPPORTED, "heads must be a positive multiple of 16 up to 1024, got %d", heads);
   if (past_len < 0 || chunk_len < 0) return fail(CA_EINVAL, "past_len and chunk_len must be >= 0");
@@ -815,6 +822,10 @@ ca_status chunk_mla_prefill(const void* q, const void* pool, int32_t format, con
   if (!aligned(q, 16) || !aligned(pool, 16) || !aligned(out, 16) || !aligned(block_table, 4) ||
       (lse_out && !aligned(lse_out, 4)))
     return fail(CA_EINVAL, "misaligned pointer argument");
+  const size_t need = (size_t)mla_prefill_staging_bytes(format == CA_MLA_FP8, past_len + chunk_len);
+  if (need && (!workspace || workspace_bytes < need))
+    return fail(CA_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+  if (need && !aligned(workspace, 256)) return fail(CA_EINVAL, "workspace must be 256-byte aligned");
   MlaPrefillArgs a;
   a.q = (const uint16_t*)q;
   a.pool = (const unsigned char*)pool;
@@ -827,7 +838,7 @@ ca_status chunk_mla_prefill(const void* q, const void* pool, int32_t format, con
   a.heads = heads;
   a.out_f32 = out_dtype == CA_F32 ? 1 : 0;
   a.scale_log2 = scale * kLog2e;
-  return hip_status(launch_mla_prefill(false, a, (hipStream_t)stream), "MLA prefill launch");
+  return hip_status(launch_mla_prefill(format == CA_MLA_FP8, a, workspace, (hipStream_t)stream), "MLA prefill launch");
 }
 
 }  // extern "C"

@@ -135,7 +135,7 @@ struct MlaAppendArgs {
 struct MlaPrefillArgs {
   const uint16_t* q;             // [chunk_len, heads, 576] bf16
   const unsigned char* pool;     // [num_blocks][block bytes]
-  const int32_t* block_table;    // [ceil((past_len + chunk_len) / 64)]
+  const int32_t* block_table;    // [ceil((past_len + chunk_len) / 64)]; null: block j is logical block j
   void* out;                     // [chunk_len, heads, 512] bf16 or fp32
   float* lse;                    // [heads, chunk_len] or null
   int64_t past_len, chunk_len;
@@ -145,7 +145,9 @@ struct MlaPrefillArgs {
 };
 
 hipError_t launch_mla_decode(bool fp8, const MlaArgs& a, hipStream_t stream);
-hipError_t launch_mla_prefill(bool fp8, const MlaPrefillArgs& a, hipStream_t stream);
+// fp8: `staging` holds mla_prefill_staging_bytes(true, past_len + chunk_len) bytes.
+hipError_t launch_mla_prefill(bool fp8, const MlaPrefillArgs& a, void* staging, hipStream_t stream);
+int64_t mla_prefill_staging_bytes(bool fp8, int64_t kv_len);
 hipError_t launch_mla_append(bool fp8, const MlaAppendArgs& a, hipStream_t stream);
 
 hipError_t launch_block_iota(int32_t* table, int n, hipStream_t stream);

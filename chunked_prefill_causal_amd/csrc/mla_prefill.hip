@@ -32,6 +32,13 @@
 //  * Latent values of keys past the sequence end are zeroed in LDS, logits
 //    past a row's position are masked with a select: NaN in unused pool slots
 //    never reaches an output.
+//  * fp8 latent cache (the deployment notes' 656 B record: e4m3 codes, one
+//    fp32 scale per 128 values): a memory-bound pass first widens the chunk's
+//    visible prefix to bf16 blocks in logical order (code x scale, one
+//    rounding), then this same kernel runs on them.  That pass moves about
+//    1.8 KB per visible token, well under 1% of a chunk's matrix time, where
+//    widening inside the kernel would put ~256 vector ops per lane and tile on
+//    the only wave of each SIMD.
 #include "device_common.h"
 #include "launch.h"
 
@@ -161,7 +168,7 @@ __global__ __launch_bounds__(256, 1) void mla_prefill_kernel(const MlaPrefillArg
   const uint32_t smem_base = lds_addr(smem);
   const uint32_t lane_off = (uint32_t)(wave * 64 + lane) * 16;
   auto issue = [&](int j, int st) {
-    const int phys = clamp_block(bt4[j], a.num_blocks);
+    const int phys = a.block_table ? clamp_block(bt4[j], a.num_blocks) : j;   // null table: logical order
     const unsigned char* b = a.pool + (int64_t)phys * kTileBytes;
     const uint32_t lds = smem_base + st * kTileBytes + wave * 1024;
 #pragma unroll
@@ -352,15 +359,56 @@ __global__ __launch_bounds__(256, 1) void mla_prefill_kernel(const MlaPrefillArg
   }
 }
 
-hipError_t launch_mla_prefill(bool fp8, const MlaPrefillArgs& a, hipStream_t stream) {
-  if (fp8) return hipErrorNotSupported;
+// fp8 latent cache -> bf16 blocks in logical order: staging block j holds the
+// records of logical block j, each value its e4m3 code times the token's fp32
+// group scale, rounded once to bf16 (the rotary part is bf16 already).  One
+// workgroup per block; the prefill kernel then reads the staging buffer.
+__global__ __launch_bounds__(256) void mla_dequant_kernel(const unsigned char* pool, const int32_t* table,
+                                                          int32_t num_blocks, unsigned char* staging) {
+  const int j = blockIdx.x;
+  const unsigned char* src = pool + (int64_t)clamp_block(table[j], num_blocks) * kMlaFp8Block;
+  unsigned char* dst = staging + (int64_t)j * kTileBytes;
+  constexpr int kScales = 32 * 64 * 16, kRope = kScales + 64 * 16;
+  for (int it = threadIdx.x; it < 32 * 64; it += kThreads) {   // code run r of token t: values 16 r .. +15
+    const int r = it >> 6, t = it & 63;
+    const u32x4_t c = *(const u32x4_t*)(src + it * 16);
+    const float sc = *(const float*)(src + kScales + t * 16 + (r >> 3) * 4);
+    uint32_t w[8];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {                  // exact widening (unit scale), then the fp32 group scale
+      const auto lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(c[k], 1.0f, false);
+      const auto hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(c[k], 1.0f, true);
+      w[2 * k] = pack_bf16(lo[0] * sc, lo[1] * sc);
+      w[2 * k + 1] = pack_bf16(hi[0] * sc, hi[1] * sc);
+    }
+    *(u32x4_t*)(dst + ((2 * r) * 64 + t) * 16) = u32x4_t{w[0], w[1], w[2], w[3]};
+    *(u32x4_t*)(dst + ((2 * r + 1) * 64 + t) * 16) = u32x4_t{w[4], w[5], w[6], w[7]};
+  }
+  for (int it = threadIdx.x; it < 8 * 64; it += kThreads)          // rotary runs -> bf16 runs 64 .. 71
+    *(u32x4_t*)(dst + (64 * 64 + it) * 16) = *(const u32x4_t*)(src + kRope + it * 16);
+}
+
+int64_t mla_prefill_staging_bytes(bool fp8, int64_t kv_len) {
+  return fp8 ? (kv_len + kBlock - 1) / kBlock * (int64_t)kTileBytes : 0;
+}
+
+hipError_t launch_mla_prefill(bool fp8, const MlaPrefillArgs& a, void* staging, hipStream_t stream) {
   const int64_t n_rb = a.chunk_len * (a.heads / 16);
   const int64_t grid = (n_rb + 7) / 8;
   if (grid == 0) return hipSuccess;
-  if (a.out_f32)
-    hipLaunchKernelGGL((mla_prefill_kernel<float>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+  MlaPrefillArgs b = a;
+  if (fp8) {
+    const int64_t n_blocks = (a.past_len + a.chunk_len + kBlock - 1) / kBlock;
+    hipLaunchKernelGGL(mla_dequant_kernel, dim3((unsigned)n_blocks), dim3(kThreads), 0, stream, a.pool,
+                       a.block_table, a.num_blocks, (unsigned char*)staging);
+    b.pool = (const unsigned char*)staging;
+    b.block_table = nullptr;
+    b.num_blocks = (int32_t)n_blocks;
+  }
+  if (b.out_f32)
+    hipLaunchKernelGGL((mla_prefill_kernel<float>), dim3((unsigned)grid), dim3(kThreads), 0, stream, b);
   else
-    hipLaunchKernelGGL((mla_prefill_kernel<uint16_t>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((mla_prefill_kernel<uint16_t>), dim3((unsigned)grid), dim3(kThreads), 0, stream, b);
   return hipGetLastError();
 }
 

@@ -412,6 +412,11 @@ ca_status chunk_mla_decode(const void* q, const void* pool, int32_t format, cons
                            const int32_t* kv_lens_host, int32_t num_seqs, int32_t heads, float scale, void* out,
                            int32_t out_dtype, float* lse_out, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Workspace bytes chunk_mla_prefill needs: 0 for the bf16 cache; for fp8,
+ * ceil((past_len + chunk_len) / 64) * 73728 (the visible prefix widened to bf16
+ * blocks).  0 for invalid arguments. */
+size_t chunkattn_mla_prefill_workspace_size(int64_t past_len, int64_t chunk_len, int32_t format);
+
 /*
  * chunk_mla_prefill — one prompt chunk of one sequence over its latent cache:
  * the tokens at positions [past_len, past_len + chunk_len) (VPP review §2.3:
@@ -423,20 +428,24 @@ ca_status chunk_mla_decode(const void* q, const void* pool, int32_t format, cons
  *   q    [chunk_len, heads, 576] bf16, dense (device, 16-byte aligned).
  *   pool, format: the cache of the sequence, already holding the records of
  *        positions 0 .. past_len + chunk_len - 1 (append the chunk first).
- *        CA_MLA_BF16 only for now; CA_MLA_FP8 returns CA_EUNSUPPORTED.
+ *        CA_MLA_FP8 records enter the matrix products as bf16(code x scale),
+ *        one rounding per value.
  *   block_table [block_table_len] device int32, >= ceil((past_len + chunk_len) / 64)
  *        entries; ids are clamped to [0, num_blocks).
  *   heads: a positive multiple of 16, at most 1024 (a row block is one token's
  *        16 consecutive heads).
  *   out  [chunk_len, heads, 512] in out_dtype (CA_BF16, rounded to nearest even,
  *        or CA_F32); lse_out optional [heads, chunk_len] fp32, natural log.
- * Pool slots past the sequence end never reach an output.  No workspace; the
- * result is deterministic.  CA_OK, CA_EINVAL, CA_EUNSUPPORTED, CA_ERANGE or
- * CA_EHIP; validation precedes any HIP call.
+ *   workspace: >= chunkattn_mla_prefill_workspace_size bytes, 256-byte aligned
+ *        (fp8 only; may be NULL for bf16).  Its contents are scratch.
+ * Pool slots past the sequence end never reach an output.  Deterministic.
+ * CA_OK, CA_EINVAL, CA_EUNSUPPORTED, CA_ERANGE, CA_EWORKSPACE or CA_EHIP;
+ * validation precedes any HIP call.
  */
 ca_status chunk_mla_prefill(const void* q, const void* pool, int32_t format, const int32_t* block_table,
                             int32_t block_table_len, int32_t num_blocks, int64_t past_len, int64_t chunk_len,
-                            int32_t heads, float scale, void* out, int32_t out_dtype, float* lse_out, void* stream);
+                            int32_t heads, float scale, void* out, int32_t out_dtype, float* lse_out,
+                            void* workspace, size_t workspace_bytes, void* stream);
 
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* chunkattn_last_error(void);

@@ -278,14 +278,16 @@ def test_mla_decode_empty_batch_succeeds():
 
 
 def mla_prefill(q=FAKE, fmt=L.CA_MLA_BF16, table_len=8, num_blocks=8, past=100, chunk=300, heads=16, scale=0.1,
-                out=FAKE, out_dtype=L.CA_BF16, lse=None):
+                out=FAKE, out_dtype=L.CA_BF16, lse=None, ws=None, ws_bytes=0):
     return L.lib().chunk_mla_prefill(q, FAKE, fmt, FAKE, table_len, num_blocks, past, chunk, heads, scale, out,
-                                     out_dtype, lse, None)
+                                     out_dtype, lse, ws, ws_bytes, None)
 
 
 @pytest.mark.parametrize("kwargs,status", [
     (dict(fmt=2), L.CA_EINVAL),
-    (dict(fmt=L.CA_MLA_FP8), L.CA_EUNSUPPORTED),
+    (dict(fmt=L.CA_MLA_FP8), L.CA_EWORKSPACE),           # fp8 widens the prefix into the workspace
+    (dict(fmt=L.CA_MLA_FP8, ws=FAKE, ws_bytes=7 * 73728 - 1), L.CA_EWORKSPACE),   # 400 tokens: 7 blocks
+    (dict(fmt=L.CA_MLA_FP8, ws=FAKE + 16, ws_bytes=1 << 30), L.CA_EINVAL),
     (dict(heads=8), L.CA_EUNSUPPORTED),
     (dict(heads=2048), L.CA_EUNSUPPORTED),
     (dict(past=-1), L.CA_EINVAL),
@@ -304,6 +306,15 @@ def mla_prefill(q=FAKE, fmt=L.CA_MLA_BF16, table_len=8, num_blocks=8, past=100, 
 def test_mla_prefill_rejections(kwargs, status):
     assert mla_prefill(**kwargs) == status
     assert L.lib().chunkattn_last_error().decode()
+
+
+def test_mla_prefill_workspace_size():
+    assert L.lib().chunkattn_mla_prefill_workspace_size(100, 300, L.CA_MLA_BF16) == 0
+    assert L.lib().chunkattn_mla_prefill_workspace_size(100, 300, L.CA_MLA_FP8) == 7 * 73728
+    assert L.lib().chunkattn_mla_prefill_workspace_size(0, 64, L.CA_MLA_FP8) == 73728
+    assert L.lib().chunkattn_mla_prefill_workspace_size(0, 65, L.CA_MLA_FP8) == 2 * 73728
+    assert L.lib().chunkattn_mla_prefill_workspace_size(-1, 65, L.CA_MLA_FP8) == 0
+    assert L.lib().chunkattn_mla_prefill_workspace_size(0, 65, 7) == 0
 
 
 def test_mla_prefill_empty_chunk_succeeds():

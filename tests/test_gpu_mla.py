@@ -25,6 +25,7 @@ import torch
 
 from chunked_prefill_causal_amd import _lib as L
 from chunked_prefill_causal_amd import inputs
+import oracle
 from oracle import mla
 
 from gpu_common import BF16_TOL, LSE_TOL, log, max_err, require_gpu
@@ -314,22 +315,28 @@ def prompt_records(n, seed, rope_scale=None):
     return lat.to(torch.bfloat16), rope.to(torch.bfloat16)
 
 
-def check_prefill(chunks, heads, seed, out_dtype=torch.bfloat16, rope_scale=None, sample=None):
+def check_prefill(fmt, chunks, heads, seed, out_dtype=torch.bfloat16, rope_scale=None, sample=None):
+    """Every compared row against the oracle on the records the prefill computes with: the bf16 records, or
+    for an fp8 cache bf16(fp32(code x scale)).  For fp8 the LSE is also held to the exact fp8 records, within
+    what that one rounding (2^-8 relative per key value) can move a logit: 2^-8 * scale * max_k sum |q| |k|."""
     n = sum(chunks)
     lat, rope = prompt_records(n, seed, rope_scale)
-    recs = mla.records(bits(lat), bits(rope), "bf16")
+    if fmt == "bf16":
+        recs, exact = mla.records(bits(lat), bits(rope), "bf16"), None
+    else:
+        recs, exact = mla.fp8_staged_records(bits(lat), bits(rope)), mla.records(bits(lat), bits(rope), "fp8")
     needed = math.ceil(n / 64)
     nb = inputs.pool_size(needed)
     table = torch.from_numpy(inputs.block_table(needed, seed + 2, nb)).cuda()
-    pool = new_pool("bf16", nb, POISON)
-    worst = worst_excess = worst_lse = 0.0
+    pool = new_pool(fmt, nb, POISON)
+    worst = worst_excess = worst_lse = worst_exact = 0.0
     past = 0
     for ci, c in enumerate(chunks):
         L.chunkattn_mla_kv_append(lat[past: past + c].cuda(), rope[past: past + c].cuda(), past, table, pool,
-                                  L.CA_MLA_BF16)
+                                  FMTS[fmt])
         q = inputs.normal((c, heads, 576), seed + 10 + ci, "bf16")
-        log(f"mla prefill heads={heads} out={out_dtype} chunk {ci}: past {past} len {c} seed {seed}")
-        out, lse = L.chunk_mla_prefill(q.cuda(), pool, L.CA_MLA_BF16, table, past, SCALE, out_dtype=out_dtype,
+        log(f"mla prefill fmt={fmt} heads={heads} out={out_dtype} chunk {ci}: past {past} len {c} seed {seed}")
+        out, lse = L.chunk_mla_prefill(q.cuda(), pool, FMTS[fmt], table, past, SCALE, out_dtype=out_dtype,
                                        return_lse=True)
         torch.cuda.synchronize()
         out = out.float().cpu().numpy().astype(np.float64)
@@ -347,33 +354,49 @@ def check_prefill(chunks, heads, seed, out_dtype=torch.bfloat16, rope_scale=None
         worst = max(worst, float(err.max()))
         worst_excess = max(worst_excess, float((err - store).max()))
         worst_lse = max(worst_lse, max_err(lse[head, tok], ref_lse))
+        if exact is not None:
+            sel = np.random.default_rng(seed + ci).choice(len(tok), size=min(len(tok), 1024), replace=False)
+            ts, hs = tok[sel], head[sel]
+            _, ex_lse = mla.prefill(bits(q), exact, past, SCALE, ts, hs)
+            qa = np.abs(oracle.bf16_bits_to_f64(bits(q))[ts, hs])
+            dots = qa @ np.abs(exact[: past + c]).T
+            dots[np.arange(past + c)[None, :] > (past + ts)[:, None]] = 0.0
+            bound = 2.0 ** -8 * SCALE * dots.max(axis=1)
+            dev = np.abs(lse[hs, ts].numpy().astype(np.float64) - ex_lse)
+            worst_exact = max(worst_exact, float(dev.max()))
+            assert np.all(dev <= LSE_TOL + bound), "LSE beyond the fp8 staging bound"
         past += c
-    log(f"  max abs err {worst:.3e} (beyond the store's rounding {worst_excess:.3e})  lse {worst_lse:.3e}")
+    log(f"  max abs err {worst:.3e} (beyond the store's rounding {worst_excess:.3e})  lse {worst_lse:.3e}"
+        + (f"  lse vs exact fp8 records {worst_exact:.3e}" if exact is not None else ""))
     assert worst_excess <= BF16_TOL and worst_lse <= LSE_TOL
     if out_dtype == torch.float32:
         assert worst <= BF16_TOL
 
 
-def test_prefill_multi_chunk_nan_poisoned():
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_prefill_multi_chunk_nan_poisoned(fmt):
     # chunk lengths: ragged, a single token, exactly one tile, several tiles; every row compared
-    check_prefill([130, 1, 64, 200, 95, 300], 16, 7100)
+    check_prefill(fmt, [130, 1, 64, 200, 95, 300], 16, 7100)
 
 
-@pytest.mark.parametrize("heads,out_dtype", [(32, torch.bfloat16), (48, torch.float32), (128, torch.bfloat16)],
-                         ids=["h32", "h48-f32out", "h128"])
-def test_prefill_more_heads(heads, out_dtype):
-    check_prefill([77, 250], heads, 7200 + heads, out_dtype=out_dtype)
+@pytest.mark.parametrize("fmt,heads,out_dtype", [("bf16", 32, torch.bfloat16), ("bf16", 48, torch.float32),
+                                                 ("bf16", 128, torch.bfloat16), ("fp8", 64, torch.float32)],
+                         ids=["bf16-h32", "bf16-h48-f32out", "bf16-h128", "fp8-h64-f32out"])
+def test_prefill_more_heads(fmt, heads, out_dtype):
+    check_prefill(fmt, [77, 250], heads, 7200 + heads, out_dtype=out_dtype)
 
 
-def test_prefill_long_past_every_row():
-    check_prefill([5000, 700], 16, 7300, sample=None)
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_prefill_long_past_every_row(fmt):
+    check_prefill(fmt, [5000, 700], 16, 7300)
 
 
-def test_prefill_late_max_growth():
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_prefill_late_max_growth(fmt):
     # rotary parts grow with position, so a row's running maximum keeps rising and O is rescaled many times
-    check_prefill([600, 400], 16, 7400, rope_scale=lambda p: 1.0 + 12.0 * p / 1000.0)
+    check_prefill(fmt, [600, 400], 16, 7400, rope_scale=lambda p: 1.0 + 12.0 * p / 1000.0)
 
 
 def test_prefill_early_spike():
     # one early record with very large logits for many rows, then ordinary ones: the first tile fixes the maximum
-    check_prefill([40, 900], 16, 7500, rope_scale=lambda p: np.where(p == 3, 40.0, 1.0))
+    check_prefill("bf16", [40, 900], 16, 7500, rope_scale=lambda p: np.where(p == 3, 40.0, 1.0))
