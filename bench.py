@@ -18,7 +18,11 @@ time.  Inputs are resident in HBM before timing starts.  Per-chunk latency,
 the split into prefill and decode parts, the prefill kernel's roofline
 fraction (bf16 matrix-core peak) and the decode part's HBM fraction are
 reported beside it, with the fp64 CPU oracle timed on a bounded sample of the
-same workload and its outputs compared with the GPU's.
+same workload and its outputs compared with the GPU's.  Beside the step, and
+outside it, the MLA latent paths are timed on their own workloads: 256 latent
+decodes and a 131072-token prompt in 8192-token chunks over the shared
+576/512 latent record (GLM5.3 PP-split deployment notes §1, §4), each from a
+bf16 and an fp8 latent cache.
 """
 from __future__ import annotations
 
@@ -70,7 +74,7 @@ def parse():
     p.add_argument("--copy-calibration", action="store_true",
                    help="after the timed region, copy 1 GiB device to device (a known-size kernel for counter scaling)")
     p.add_argument("--mla-only", action="store_true",
-                   help="time only the MLA latent decode batches (prints their JSON object)")
+                   help="time only the MLA latent decode batches and prompt (prints their JSON object)")
     p.add_argument("--chunk-reps", type=int, default=20, help="repetitions per chunk for the latency distribution")
     p.add_argument("--summarize-profile", nargs="+", metavar="DIR",
                    help="TRACE_DIR FETCH_DIR WRITE_DIR [MFMA_DIR]: write the profile summary from rocprofv3 "
@@ -362,6 +366,79 @@ class MlaDecode:
     def run(self, L):
         return L.chunk_mla_decode(self.q, self.pool, self.fmt, self.tables, self.kv_host, self.w.scale,
                                   out=self.out, workspace=self.ws, kv_lens_dev=self.kv_dev)
+
+
+class MlaPrefill:
+    """The 128K-token latent prompt (16 chunks of 8192, 16 heads) over a paged latent cache of one format.
+
+    The whole prompt's records are written first (0xFF-poisoned pool, fp8 quantised by the write kernel);
+    chunk k then attends to records 0 .. its positions, as after appending it.  Matrix work per chunk:
+    2 * (576 + 512) flops per visible (query, key) pair and head; the fp8 path includes its widening pass.
+    """
+
+    def __init__(self, L, inputs, torch, fmt):
+        w = inputs.WORKLOADS["mla_prefill"]
+        self.w, self.fmt = w, fmt
+        needed = math.ceil(w.seq_len / 64)
+        self.table = torch.from_numpy(inputs.block_table(needed, w.seed + 3)).cuda()
+        self.pool = L.mla_pool(inputs.pool_size(needed), fmt)
+        self.pool.fill_(0xFF)
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(inputs.mla_record_seed(w, 0))
+        lat = torch.randn((w.seq_len, L.MLA_LATENT), generator=gen, device="cuda").to(torch.bfloat16)
+        rope = torch.randn((w.seq_len, L.MLA_ROPE), generator=gen, device="cuda").to(torch.bfloat16)
+        L.chunkattn_mla_kv_append(lat, rope, 0, self.table, self.pool, fmt)
+        del lat, rope
+        self.q = [inputs.normal_device((w.chunk_len, w.heads, w.head_dim), inputs.chunk_seeds(w, k), "bf16")
+                  for k in range(w.n_chunks)]
+        self.out = torch.empty((w.chunk_len, w.heads, w.head_dim_v), dtype=torch.bfloat16, device="cuda")
+        need = L.chunkattn_mla_prefill_workspace_size(0, w.seq_len, fmt)
+        self.ws = torch.empty(need, dtype=torch.uint8, device="cuda") if need else None
+        self.flops = [w.heads * 2 * (w.head_dim + w.head_dim_v) * causal_pairs(k * w.chunk_len, w.chunk_len)
+                      for k in range(w.n_chunks)]
+
+    def run_chunk(self, L, k):
+        return L.chunk_mla_prefill(self.q[k], self.pool, self.fmt, self.table, k * self.w.chunk_len, self.w.scale,
+                                   out=self.out, workspace=self.ws)
+
+
+def mla_prefill_summary(L, inputs, torch, reps):
+    """Both latent formats of the 128K MLA prompt: per-chunk latency (median of `reps`), the chunk loop's
+    matrix TFLOP/s against the dense bf16 peak."""
+    res = {}
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for name, fmt in (("bf16", L.CA_MLA_BF16), ("fp8", L.CA_MLA_FP8)):
+        m = MlaPrefill(L, inputs, torch, fmt)
+        for k in range(m.w.n_chunks):
+            m.run_chunk(L, k)
+        per = []
+        for k in range(m.w.n_chunks):
+            ts = []
+            for _ in range(reps):
+                e0.record()
+                m.run_chunk(L, k)
+                e1.record()
+                torch.cuda.synchronize()
+                ts.append(e0.elapsed_time(e1))
+            per.append(median(ts))
+        a, b, r2 = fit_line(list(range(m.w.n_chunks)), per)
+        tflops = sum(m.flops) / (sum(per) / 1e3) / 1e12
+        res[name] = {"loop_ms": round(sum(per), 3), "per_chunk_ms": [round(x, 4) for x in per],
+                     "fit": {"a_ms": round(a, 4), "b_ms_per_chunk": round(b, 4), "r2": round(r2, 5)},
+                     "tokens_per_s": round(m.w.seq_len / (sum(per) / 1e3), 1),
+                     "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": PEAK_BF16_TFLOPS,
+                                  "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                                  "avg_launch_ms": round(sum(per) / m.w.n_chunks, 4),
+                                  "avg_flops_per_launch": sum(m.flops) / m.w.n_chunks}}
+        log(f"MLA prefill {name}: loop {sum(per):.2f} ms, {tflops:.1f} TFLOP/s "
+            f"({tflops / PEAK_BF16_TFLOPS:.1%} of dense bf16 peak)")
+        del m
+        torch.cuda.empty_cache()
+    w = inputs.WORKLOADS["mla_prefill"]
+    res["workload"] = (f"{w.seq_len}-token prompt as {w.n_chunks} chunks of {w.chunk_len}, {w.heads} q heads over "
+                       "one shared 512+64 latent record per token (d_qk 576, d_v 512), paged KV (64); fp8 includes "
+                       "its widening pass; inputs resident in HBM")
+    return res
 
 
 def mla_decode_summary(L, inputs, torch, timed, reps, warmup):
@@ -748,8 +825,8 @@ def main():
         return median(ts)
 
     if args.mla_only:
-        print(json.dumps({"mla_decode": mla_decode_summary(L, inputs, torch, timed, args.reps, args.warmup)}),
-              flush=True)
+        print(json.dumps({"mla_decode": mla_decode_summary(L, inputs, torch, timed, args.reps, args.warmup),
+                          "mla_prefill": mla_prefill_summary(L, inputs, torch, args.curve_reps)}), flush=True)
         return
     log("generating inputs in HBM")
     loop = PrefillLoop(L, inputs, torch)
@@ -834,6 +911,8 @@ def main():
     log("timing the MLA latent decode batches")
     del dec_only, pre_only
     mla = mla_decode_summary(L, inputs, torch, timed, args.reps, args.warmup)
+    log("timing the MLA latent prompt (both cache formats)")
+    mla_pre = mla_prefill_summary(L, inputs, torch, args.curve_reps)
 
     log("timing the latency-predictor grid")
     alp = latency_predictor(L, loop, torch)
@@ -912,6 +991,7 @@ def main():
         "other_prompts": curves,
         "contiguous_cache": contig,
         "mla_decode": mla,
+        "mla_prefill": mla_pre,
         "schedule_sim": sched,
         "latency_predictor": alp,
         "cpu_baseline": cpu,

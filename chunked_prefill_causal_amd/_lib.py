@@ -476,6 +476,10 @@ def chunk_mla_decode(q, pool, fmt: int, block_tables, kv_lens, scale: float, *, 
     return (out, lse) if return_lse else out
 
 
+def chunkattn_mla_prefill_workspace_size(past_len: int, chunk_len: int, fmt: int) -> int:
+    return lib().chunkattn_mla_prefill_workspace_size(int(past_len), int(chunk_len), fmt)
+
+
 def chunk_mla_prefill(q, pool, fmt: int, block_table, past_len: int, scale: float, *,
                       num_blocks: int | None = None, out=None, out_dtype=torch.bfloat16, return_lse: bool = False,
                       lse=None, workspace=None, stream=None):
@@ -489,7 +493,7 @@ def chunk_mla_prefill(q, pool, fmt: int, block_table, past_len: int, scale: floa
     if return_lse and lse is None:
         lse = torch.empty((heads, c), dtype=torch.float32, device=q.device)
     if workspace is None:
-        need = lib().chunkattn_mla_prefill_workspace_size(int(past_len), c, fmt)
+        need = chunkattn_mla_prefill_workspace_size(past_len, c, fmt)
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device) if need else None
     _check(lib().chunk_mla_prefill(
         _ptr(q), _ptr(pool), fmt, _ptr(block_table), block_table.shape[-1],

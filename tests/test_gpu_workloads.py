@@ -7,8 +7,9 @@ reads the same inputs copied to the host.  The sample always includes each
 chunk's first and last token and tokens on both sides of tile boundaries.
 
 Row counts per chunk: 4096 for the 32K, 128K and 512K MLA-shaped prompts
-(the last as its workload states), and every row of the mixed batch: all
-8192 decode rows and all 65536 rows of its 2048-token prefill chunk.  The
+(the last as its workload states), 512 for the 128K MLA latent prompt (from
+both cache formats), and every row of the mixed batch: all 8192 decode rows
+and all 65536 rows of its 2048-token prefill chunk.  The
 fp64 oracle needs a few CPU-minutes on 16 host cores for all of it.
 """
 import math
@@ -71,6 +72,44 @@ def test_gqa_128k_all_chunks():
 
 def test_mla_512k_all_chunks():
     run_prompt("mla_512k", 4096)
+
+
+def test_mla_prefill_all_chunks():
+    """The 128K latent prompt (16 chunks of 8192, 16 heads) over both cache formats, as the benchmark runs it:
+    the whole prompt's records are written first into a 0xFF-poisoned pool, every chunk runs, and sampled rows
+    of each chunk are compared with the oracle on the records the prefill computes with (bf16, or the fp8
+    records staged as bf16(code x scale))."""
+    from oracle import mla
+    w = inputs.WORKLOADS["mla_prefill"]
+    needed = math.ceil(w.seq_len / 64)
+    table = torch.from_numpy(inputs.block_table(needed, w.seed + 3)).cuda()
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(inputs.mla_record_seed(w, 0))
+    lat = torch.randn((w.seq_len, L.MLA_LATENT), generator=gen, device="cuda").to(torch.bfloat16)
+    rope = torch.randn((w.seq_len, L.MLA_ROPE), generator=gen, device="cuda").to(torch.bfloat16)
+    lat_bits = lat.cpu().view(torch.int16).numpy().view(np.uint16)
+    rope_bits = rope.cpu().view(torch.int16).numpy().view(np.uint16)
+    worst = worst_lse = 0.0
+    for fmt_name, fmt in (("bf16", L.CA_MLA_BF16), ("fp8", L.CA_MLA_FP8)):
+        pool = L.mla_pool(inputs.pool_size(needed), fmt)
+        pool.fill_(0xFF)
+        L.chunkattn_mla_kv_append(lat, rope, 0, table, pool, fmt)
+        recs = (mla.records(lat_bits, rope_bits, "bf16") if fmt_name == "bf16"
+                else mla.fp8_staged_records(lat_bits, rope_bits))
+        for c in range(w.n_chunks):
+            past = c * w.chunk_len
+            q = inputs.normal_device((w.chunk_len, w.heads, w.head_dim), inputs.chunk_seeds(w, c), "bf16")
+            out, lse = L.chunk_mla_prefill(q, pool, fmt, table, past, w.scale, return_lse=True)
+            tok, head = inputs.sample_rows(w.chunk_len, w.heads, w.sample_rows, w.seed * 11 + c)
+            ti, hi = torch.from_numpy(tok).cuda(), torch.from_numpy(head.astype(np.int64)).cuda()
+            q_bits = q.cpu().view(torch.int16).numpy().view(np.uint16)
+            ref, ref_lse = mla.prefill(q_bits, recs, past, w.scale, tok, head)
+            e, el = max_err(out[ti, hi], ref), max_err(lse[hi, ti], ref_lse)
+            worst, worst_lse = max(worst, e), max(worst_lse, el)
+            log(f"mla_prefill {fmt_name} chunk {c} (past {past}): {len(tok)} rows, max err {e:.3e}, lse err {el:.2e}")
+        del pool
+        torch.cuda.empty_cache()
+    assert worst <= BF16_TOL and worst_lse <= LSE_TOL
 
 
 def test_mixed_batch_full_size():
