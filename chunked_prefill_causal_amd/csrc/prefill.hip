@@ -384,12 +384,22 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(const PrefillArgs a)
   float M, L;
   merge_weights(a.ws_ml + row * 2, S, R, M, L);
   f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < S; ++s) {
-    const float m = a.ws_ml[((int64_t)s * R + row) * 2];
-    if (m == -INFINITY) continue;
-    const float wgt = fast_exp2(m - M);
-    const f32x4_t v = *(const f32x4_t*)(a.ws_o + ((int64_t)s * R + row) * DV + 4 * q4);
-    acc += v * wgt;
+  // four splits' partials are loaded before any is used, so each thread keeps 64 B in flight; a partial
+  // with m = -inf (no visible key) is selected away, its O (never written) is not used
+  for (int s0 = 0; s0 < S; s0 += 4) {
+    float m[4];
+    f32x4_t v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int s = min(s0 + i, S - 1);
+      m[i] = s0 + i < S ? a.ws_ml[((int64_t)s * R + row) * 2] : -INFINITY;
+      v[i] = *(const f32x4_t*)(a.ws_o + ((int64_t)s * R + row) * DV + 4 * q4);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float wgt = fast_exp2(m[i] - M);
+      if (m[i] != -INFINITY) acc += v[i] * wgt;
+    }
   }
   const float inv = 1.f / L;
   acc *= inv;
