@@ -97,10 +97,14 @@ constexpr int kMlaLatent = 512, kMlaRope = 64, kMlaRecord = 576, kMlaStepKeys = 
 // A decode work unit holds at most this many steps, so a segment spans at most
 // 64 cache blocks (the kernel keeps their ids one per lane).
 constexpr int kMlaMaxUnitSteps = 127;
-// Block bytes (64 tokens): bf16 [72 runs][64][16 B]; fp8 codes [32 runs][64][16 B] +
-// scales [64][4 fp32] + rotary [8 runs][64][16 B].
+// Block bytes (64 tokens): bf16 [72 runs][64][16 B].  fp8: two 32-token halves,
+// each one contiguous region of codes [32 runs][32][16 B], scales [32][4 fp32]
+// and rotary [8 runs][32][16 B], so a 32-key decode step is a single region.
 constexpr int64_t kMlaBf16Block = 72 * 64 * 16;
-constexpr int64_t kMlaFp8Block = 32 * 64 * 16 + 64 * 16 + 8 * 64 * 16;
+constexpr int64_t kMlaFp8Half = 32 * 32 * 16 + 32 * 16 + 8 * 32 * 16;
+constexpr int64_t kMlaFp8HalfScales = 32 * 32 * 16;                  // offsets inside a half
+constexpr int64_t kMlaFp8HalfRope = kMlaFp8HalfScales + 32 * 16;
+constexpr int64_t kMlaFp8Block = 2 * kMlaFp8Half;
 
 // MLA decode work plan: the 32-key steps of all sequences, laid end to end,
 // are cut into `units` equal ranges; a unit's piece of one sequence (a

@@ -118,8 +118,6 @@ struct MlaCfg {
   static constexpr int kXchg = kStages * kStage;
   static constexpr int kLds = kXchg + kXSlots * 2 * 64 * 32;
   static constexpr int64_t kBlock = FP8 ? kMlaFp8Block : kMlaBf16Block;
-  static constexpr int64_t kBlkScales = 32 * 64 * 16;          // fp8 block: scales, then rotary
-  static constexpr int64_t kBlkRope = FP8 ? kBlkScales + 64 * 16 : 64 * 64 * 16;
 };
 
 }  // namespace
@@ -190,16 +188,20 @@ __global__ __launch_bounds__(128) void mla_decode_kernel(const MlaArgs a) {
     auto issue = [&](int t, int st) {
       const int key0 = key_lo + kMlaStepKeys * t;
       const int blk = clamp_block(__builtin_amdgcn_readlane(bt_lane, (key0 >> 6) - blk0), a.num_blocks);
-      const unsigned char* b = a.pool + (int64_t)blk * C::kBlock + ((key0 >> 5) & 1) * 32 * 16 + (lane >> 5) * 1024 +
-                               (lane & 31) * 16;
       const uint32_t lds = smem_base + st * C::kStage;
       if constexpr (FP8) {
+        // the step is one contiguous half-block: each load moves 1 KiB of it
+        const unsigned char* h = a.pool + (int64_t)blk * C::kBlock + ((key0 >> 5) & 1) * kMlaFp8Half + lane * 16;
 #pragma unroll
-        for (int n = 8 * w; n < 8 * w + 8; ++n) dma16(b + 2 * n * 1024, lds + C::kCodes + n * 1024);
-        dma16(b - (lane >> 5) * 1024 + C::kBlkScales, lds + C::kScales + w * 1024);
+        for (int n = 8 * w; n < 8 * w + 8; ++n) dma16(h + n * 1024, lds + C::kCodes + n * 1024);
+        // the 32 keys' scales; the upper half-wave brings the first 512 B of the rotary runs into the unused
+        // half of the slot
+        dma16(h + kMlaFp8HalfScales, lds + C::kScales + w * 1024);
 #pragma unroll
-        for (int n = 2 * w; n < 2 * w + 2; ++n) dma16(b + C::kBlkRope + 2 * n * 1024, lds + C::kRope + n * 1024);
+        for (int n = 2 * w; n < 2 * w + 2; ++n) dma16(h + kMlaFp8HalfRope + n * 1024, lds + C::kRope + n * 1024);
       } else {
+        const unsigned char* b = a.pool + (int64_t)blk * C::kBlock + ((key0 >> 5) & 1) * 32 * 16 +
+                                 (lane >> 5) * 1024 + (lane & 31) * 16;
 #pragma unroll
         for (int n = 16 * w; n < 16 * w + 16; ++n) dma16(b + 2 * n * 1024, lds + n * 1024);
 #pragma unroll
@@ -504,11 +506,12 @@ __global__ __launch_bounds__(64) void mla_append_kernel(const MlaAppendArgs a) {
       pk = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], pk, true);
       w[q] = (uint32_t)pk;
     }
-    *(u32x2_t*)(b + (lane >> 1) * 1024 + tok * 16 + (lane & 1) * 8) = u32x2_t{w[0], w[1]};
-    if ((lane & 15) == 0) *(float*)(b + 32 * 64 * 16 + tok * 16 + (lane >> 4) * 4) = scale;
+    unsigned char* h = b + (tok >> 5) * kMlaFp8Half;                // this token's half of the block
+    const int u = tok & 31;
+    *(u32x2_t*)(h + ((lane >> 1) * 32 + u) * 16 + (lane & 1) * 8) = u32x2_t{w[0], w[1]};
+    if ((lane & 15) == 0) *(float*)(h + kMlaFp8HalfScales + u * 16 + (lane >> 4) * 4) = scale;
     if (lane < 8)
-      *(u32x4_t*)(b + 32 * 64 * 16 + 64 * 16 + lane * 1024 + tok * 16) =
-          *(const u32x4_t*)(a.rope + i * kMlaRope + 8 * lane);
+      *(u32x4_t*)(h + kMlaFp8HalfRope + (lane * 32 + u) * 16) = *(const u32x4_t*)(a.rope + i * kMlaRope + 8 * lane);
   }
 }
 

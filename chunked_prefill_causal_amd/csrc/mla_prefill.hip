@@ -368,11 +368,11 @@ __global__ __launch_bounds__(256) void mla_dequant_kernel(const unsigned char* p
   const int j = blockIdx.x;
   const unsigned char* src = pool + (int64_t)clamp_block(table[j], num_blocks) * kMlaFp8Block;
   unsigned char* dst = staging + (int64_t)j * kTileBytes;
-  constexpr int kScales = 32 * 64 * 16, kRope = kScales + 64 * 16;
   for (int it = threadIdx.x; it < 32 * 64; it += kThreads) {   // code run r of token t: values 16 r .. +15
     const int r = it >> 6, t = it & 63;
-    const u32x4_t c = *(const u32x4_t*)(src + it * 16);
-    const float sc = *(const float*)(src + kScales + t * 16 + (r >> 3) * 4);
+    const unsigned char* h = src + (t >> 5) * kMlaFp8Half;       // the token's half of the block
+    const u32x4_t c = *(const u32x4_t*)(h + (r * 32 + (t & 31)) * 16);
+    const float sc = *(const float*)(h + kMlaFp8HalfScales + (t & 31) * 16 + (r >> 3) * 4);
     uint32_t w[8];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {                  // exact widening (unit scale), then the fp32 group scale
@@ -384,8 +384,11 @@ __global__ __launch_bounds__(256) void mla_dequant_kernel(const unsigned char* p
     *(u32x4_t*)(dst + ((2 * r) * 64 + t) * 16) = u32x4_t{w[0], w[1], w[2], w[3]};
     *(u32x4_t*)(dst + ((2 * r + 1) * 64 + t) * 16) = u32x4_t{w[4], w[5], w[6], w[7]};
   }
-  for (int it = threadIdx.x; it < 8 * 64; it += kThreads)          // rotary runs -> bf16 runs 64 .. 71
-    *(u32x4_t*)(dst + (64 * 64 + it) * 16) = *(const u32x4_t*)(src + kRope + it * 16);
+  for (int it = threadIdx.x; it < 8 * 64; it += kThreads) {        // rotary runs -> bf16 runs 64 .. 71
+    const int r = it >> 6, t = it & 63;
+    *(u32x4_t*)(dst + (64 * 64 + it) * 16) =
+        *(const u32x4_t*)(src + (t >> 5) * kMlaFp8Half + kMlaFp8HalfRope + (r * 32 + (t & 31)) * 16);
+  }
 }
 
 int64_t mla_prefill_staging_bytes(bool fp8, int64_t kv_len) {

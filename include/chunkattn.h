@@ -358,10 +358,13 @@ ca_status chunkattn_alp_update(ca_alp_state* state, const double* x, double meas
  * DeepSeek-V3.1 and GLM-5.x, use MLA, §6.1).  A record is 512 latent + 64
  * rotary values.  Cache blocks hold 64 tokens, one shared head:
  *   CA_MLA_BF16: [72 runs][64 tokens][8 bf16]                      73728 B per block
- *   CA_MLA_FP8 : [32 runs][64 tokens][16 e4m3] latent codes,
- *                [64 tokens][4 fp32] scales (one per 128 latent values),
- *                [8 runs][64 tokens][8 bf16] rotary                41984 B per block (= 64 x 656)
- * Run r holds values 8r..8r+7 (bf16) or 16r..16r+15 (codes) of every token.
+ *   CA_MLA_FP8 : two halves of 32 tokens (tokens 0-31, then 32-63), each
+ *                [32 runs][32 tokens][16 e4m3] latent codes,
+ *                [32 tokens][4 fp32] scales (one per 128 latent values),
+ *                [8 runs][32 tokens][8 bf16] rotary                20992 B per half,
+ *                                                                  41984 B per block (= 64 x 656)
+ * Run r holds values 8r..8r+7 (bf16) or 16r..16r+15 (codes) of every token
+ * (of the half).
  * fp8 codes are OCP e4m3 (bias 7, largest normal 448): a group's scale is
  * amax / 448 in fp32 (1 for an all-zero group) and a value's code is its fp32
  * quotient by the scale clamped to +-448, rounded to the nearest code.

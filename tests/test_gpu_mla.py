@@ -54,11 +54,14 @@ def byte_offsets(fmt: str, table: np.ndarray, positions: np.ndarray):
         j = np.arange(1152)
         rec = base[:, None] + (j // 16) * 1024 + j % 16
         return rec[:, :1024], None, rec[:, 1024:]
-    j = np.arange(512)                     # codes [32 runs][64][16 B], scales [64][16 B], rotary [8][64][16 B]
-    codes = base[:, None] + (j // 16) * 1024 + j % 16
-    scales = base[:, None] + 32768 + np.arange(16)
+    # fp8: halves of 32 tokens, each codes [32 runs][32][16 B], scales [32][16 B], rotary [8 runs][32][16 B]
+    half = table[positions // 64].astype(np.int64) * bb + ((positions % 64) // 32) * 20992
+    u = positions % 32
+    j = np.arange(512)
+    codes = half[:, None] + ((j // 16) * 32 + u[:, None]) * 16 + j % 16
+    scales = half[:, None] + 16384 + u[:, None] * 16 + np.arange(16)
     j = np.arange(128)
-    rope = base[:, None] + 33792 + (j // 16) * 1024 + j % 16
+    rope = half[:, None] + 16896 + ((j // 16) * 32 + u[:, None]) * 16 + j % 16
     return codes, scales, rope
 
 
