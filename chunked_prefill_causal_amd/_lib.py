@@ -15,7 +15,8 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libchunkattn.so")
+# CHUNKATTN_LIB selects another build of the library (e.g. the host-sanitized one).
+LIB_PATH = os.environ.get("CHUNKATTN_LIB") or os.path.join(_HERE, "libchunkattn.so")
 
 CA_OK, CA_EINVAL, CA_EUNSUPPORTED, CA_ERANGE, CA_EWORKSPACE, CA_EHIP = 0, -1, -2, -3, -4, -5
 CA_F32, CA_BF16 = 0, 1

@@ -3,6 +3,10 @@
 Every HIP source compiles to an object under ``_build/`` (in parallel), then
 one hipcc link produces ``chunked_prefill_causal_amd/libchunkattn.so``.
 Packed-FP32 instructions are disabled for all device code.
+
+``python chunked_prefill_causal_amd/build.py --sanitize`` builds a host-side
+ASan + UBSan copy of the library and of the CPU oracle under ``_build/san``
+and runs the CPU test suite against them.
 """
 from __future__ import annotations
 
@@ -34,9 +38,23 @@ FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-
 EXTRA = {"mla.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+# Host-only AddressSanitizer + UndefinedBehaviorSanitizer build (device code is built as usual).  It
+# links against clang's shared sanitizer runtime, which the process must preload (see `sanitizer_env`).
+SAN_DIR = os.path.join(BUILD_DIR, "san")
+SAN_FLAGS = ("-Xarch_host -fsanitize=address -Xarch_host -fsanitize=undefined "
+             "-Xarch_host -fno-sanitize-recover=undefined -Xarch_host -shared-libsan "
+             "-Xarch_host -fno-omit-frame-pointer -Xarch_host -g").split()
+# the CPU oracle is plain C built by clang, so these need no -Xarch_host
+ORACLE_SAN_FLAGS = ("-fsanitize=address,undefined -fno-sanitize-recover=undefined -shared-libsan "
+                    "-fno-omit-frame-pointer -g").split()
+LLVM = os.environ.get("ROCM_LLVM", "/opt/rocm/lib/llvm")
+
+
+def _compile(src: str, sanitize: bool = False) -> str:
+    out_dir = SAN_DIR if sanitize else BUILD_DIR
+    obj = os.path.join(out_dir, os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), *(SAN_FLAGS if sanitize else []), "-x", "hip", "-c",
+           os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     err = "\n".join(l for l in r.stderr.splitlines() if noise not in l)
@@ -47,18 +65,54 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def build(verbose: bool = False, sanitize: bool = False) -> str:
+    """Build libchunkattn.so in place; with ``sanitize`` a host-sanitized copy under _build/san instead."""
+    out_dir = SAN_DIR if sanitize else BUILD_DIR
+    os.makedirs(out_dir, exist_ok=True)
     with ThreadPoolExecutor(len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+        objs = list(ex.map(lambda src: _compile(src, sanitize), SOURCES))
+    lib = os.path.join(SAN_DIR, "libchunkattn.so") if sanitize else LIB
+    tmp = lib + ".tmp"
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *(SAN_FLAGS if sanitize else []), "-o", tmp, *objs]
     subprocess.run(cmd, check=True, capture_output=not verbose)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {lib}")
+    return lib
+
+
+def sanitizer_env() -> dict:
+    """Environment that runs Python with the sanitized library and oracle: clang's shared ASan runtime
+    preloaded (the interpreter is not instrumented), leak checks off (the interpreter's own allocations),
+    and the library / oracle paths pointed at the _build/san copies."""
+    import glob
+    rt = sorted(glob.glob(os.path.join(LLVM, "lib", "clang", "*", "lib", "linux", "libclang_rt.asan-x86_64.so")))
+    if not rt:
+        raise RuntimeError(f"no clang ASan runtime under {LLVM}")
+    env = dict(os.environ)
+    env["LD_PRELOAD"] = rt[-1]
+    env["ASAN_OPTIONS"] = "detect_leaks=0:abort_on_error=1:detect_odr_violation=0"
+    env["UBSAN_OPTIONS"] = "print_stacktrace=1:halt_on_error=1"
+    env["LD_LIBRARY_PATH"] = os.path.join(LLVM, "lib") + ":" + env.get("LD_LIBRARY_PATH", "")
+    env["CHUNKATTN_LIB"] = os.path.join(SAN_DIR, "libchunkattn.so")
+    env["CHUNKATTN_ORACLE_LIB"] = os.path.join(SAN_DIR, "liboracle.so")
+    return env
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    import argparse
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--sanitize", action="store_true",
+                    help="host ASan + UBSan build of the library and the CPU oracle under _build/san, then run "
+                         "the CPU test suite with them")
+    args = ap.parse_args()
+    if not args.sanitize:
+        build(verbose=True)
+    else:
+        build(verbose=True, sanitize=True)
+        sys.path.insert(0, ROOT)
+        import oracle
+        oracle.build(os.path.join(SAN_DIR, "liboracle.so"), extra=ORACLE_SAN_FLAGS, cc=os.path.join(LLVM, "bin", "clang"))
+        r = subprocess.run([sys.executable, "-m", "pytest", os.path.join(ROOT, "tests"), "-q", "-m", "not gpu",
+                            "-p", "no:cacheprovider"], env=sanitizer_env(), cwd=ROOT)
+        sys.exit(r.returncode)

@@ -239,7 +239,7 @@ size_t chunkattn_prefill_workspace_size(int64_t chunk_len, int32_t heads, int32_
 
 size_t chunkattn_prefill_contiguous_workspace_size(int64_t past_len, int64_t chunk_len, int32_t heads,
                                                    int32_t kv_heads, int32_t head_dim, int32_t head_dim_v,
-                                                   ca_dtype dtype, int32_t num_splits) {
+                                                   int32_t dtype, int32_t num_splits) {
   if (past_len < 0 || chunk_len <= 0 || heads <= 0 || kv_heads <= 0 || heads % kv_heads || head_dim <= 0)
     return 0;
   const int dv = head_dim_v ? head_dim_v : head_dim;
@@ -685,7 +685,7 @@ ca_status chunk_attn_varlen_noalloc(const void* q, const void* k_pool, const voi
 }
 
 ca_status chunkattn_kv_append(const void* k_new, const void* v_new, int64_t start_pos, int64_t n_tokens,
-                              int32_t kv_heads, int32_t head_dim, int32_t head_dim_v, ca_dtype dtype,
+                              int32_t kv_heads, int32_t head_dim, int32_t head_dim_v, int32_t dtype,
                               const int32_t* block_table, int32_t block_table_len, int32_t num_blocks, void* k_pool,
                               void* v_pool, const int64_t* src_strides, void* stream) {
   if (!k_new || !v_new || !block_table || !k_pool || !v_pool) return fail(CA_EINVAL, "null pointer argument");

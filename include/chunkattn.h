@@ -73,6 +73,8 @@ typedef enum {
   CA_EHIP = -5           /* the HIP runtime reported an error */
 } ca_status;
 
+/* Enumerated arguments travel as int32_t: the library validates whatever value
+ * arrives, so an out-of-range one is an error code, never an invalid enum. */
 typedef enum { CA_F32 = 0, CA_BF16 = 1 } ca_dtype;
 typedef enum { CA_KV_CONTIGUOUS = 0, CA_KV_PAGED = 1 } ca_kv_layout;
 
@@ -81,11 +83,11 @@ typedef enum { CA_KV_CONTIGUOUS = 0, CA_KV_PAGED = 1 } ca_kv_layout;
  * passing NULL means the defaults below.
  */
 typedef struct ca_prefill_opts {
-  ca_dtype dtype;              /* element type of q, k, v.  Default CA_BF16. */
-  ca_dtype out_dtype;          /* element type of out.  Default CA_BF16.
+  int32_t dtype;               /* a ca_dtype: element type of q, k, v.  Default CA_BF16. */
+  int32_t out_dtype;           /* a ca_dtype: element type of out.  Default CA_BF16.
                                   Supported pairs: (bf16, bf16), (bf16, f32), (f32, f32). */
   int32_t head_dim_v;          /* value head dim; 0 = head_dim.  Must be <= head_dim. */
-  ca_kv_layout kv_layout;      /* default CA_KV_CONTIGUOUS */
+  int32_t kv_layout;           /* a ca_kv_layout, default CA_KV_CONTIGUOUS */
   int64_t kv_capacity;         /* contiguous: tokens allocated in k and v;
                                   0 = exactly past_len + chunk_len */
   const int32_t* block_table;  /* paged: device int32 [block_table_len] */
@@ -159,7 +161,7 @@ size_t chunkattn_prefill_workspace_size(int64_t chunk_len, int32_t heads, int32_
  */
 size_t chunkattn_prefill_contiguous_workspace_size(int64_t past_len, int64_t chunk_len, int32_t heads,
                                                    int32_t kv_heads, int32_t head_dim, int32_t head_dim_v,
-                                                   ca_dtype dtype, int32_t num_splits);
+                                                   int32_t dtype, int32_t num_splits);
 
 /*
  * The split count chunk_prefill_attn picks for num_splits = 0 when the
@@ -259,7 +261,7 @@ ca_status chunk_attn_varlen_noalloc(const void* q, const void* k_pool, const voi
  * Bitwise copy; no arithmetic.  Block ids are clamped to [0, num_blocks).
  */
 ca_status chunkattn_kv_append(const void* k_new, const void* v_new, int64_t start_pos, int64_t n_tokens,
-                              int32_t kv_heads, int32_t head_dim, int32_t head_dim_v, ca_dtype dtype,
+                              int32_t kv_heads, int32_t head_dim, int32_t head_dim_v, int32_t dtype,
                               const int32_t* block_table, int32_t block_table_len, int32_t num_blocks,
                               void* k_pool, void* v_pool, const int64_t* src_strides, void* stream);
 

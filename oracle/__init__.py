@@ -29,27 +29,31 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "attn_oracle.c")
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# CHUNKATTN_ORACLE_LIB selects another build (the host-sanitized one); it is then used as it is.
+_LIB_PATH = os.environ.get("CHUNKATTN_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 F32, BF16, F64 = 0, 1, 2
 
 
-def build() -> str:
-    """Compile attn_oracle.c with gcc (-O3, OpenMP, no fast-math, no FMA contraction)."""
-    tmp = _LIB_PATH + ".tmp"
-    cmd = ["gcc", "-O3", "-fopenmp", "-fPIC", "-shared", "-std=c11",
-           "-fno-fast-math", "-ffp-contract=off", _SRC, "-o", tmp, "-lm"]
+def build(path: str | None = None, extra=(), cc: str = "gcc") -> str:
+    """Compile attn_oracle.c (-O3, OpenMP, no fast-math, no FMA contraction); ``extra`` flags and another
+    compiler serve the host-sanitized build."""
+    path = path or _LIB_PATH
+    tmp = path + ".tmp"
+    cmd = [cc, "-O3", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+           "-fno-fast-math", "-ffp-contract=off", *extra, _SRC, "-o", tmp, "-lm"]
     subprocess.run(cmd, check=True)
-    os.replace(tmp, _LIB_PATH)
-    return _LIB_PATH
+    os.replace(tmp, path)
+    return path
 
 
 def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+    if not os.environ.get("CHUNKATTN_ORACLE_LIB") and (
+            not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC)):
         build()
     lib = ctypes.CDLL(_LIB_PATH)
     i64p = ctypes.POINTER(ctypes.c_int64)
