@@ -85,11 +85,11 @@ def lib() -> ctypes.CDLL:
     L.chunkattn_prefill_contiguous_workspace_size.restype = sz
     L.chunkattn_prefill_auto_splits.argtypes = [i64, i64, i32, i32]
     L.chunkattn_prefill_auto_splits.restype = i32
-    L.chunk_attn_varlen.argtypes = [vp, vp, vp, vp, i32, i32, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32,
-                                    vp, vp, vp, sz, vp]
+    L.chunk_attn_varlen.argtypes = [vp, vp, vp, vp, i32, i32, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, vp, i32,
+                                    vp, vp, sz, vp]
     L.chunk_attn_varlen.restype = ctypes.c_int
-    L.chunk_attn_varlen_noalloc.argtypes = [vp, vp, vp, vp, i32, i32, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32,
-                                            vp, vp, vp]
+    L.chunk_attn_varlen_noalloc.argtypes = [vp, vp, vp, vp, i32, i32, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, vp,
+                                            i32, vp, vp]
     L.chunk_attn_varlen_noalloc.restype = ctypes.c_int
     L.chunkattn_varlen_workspace_size.argtypes = [vp, vp, i32, i32, i32, i32]
     L.chunkattn_varlen_workspace_size.restype = sz
@@ -355,13 +355,13 @@ def chunkattn_varlen_workspace_size(cu_seqlens_q, kv_lens, heads: int, kv_heads:
 
 
 def chunk_attn_varlen(q, k_pool, v_pool, block_tables, cu_seqlens_q, kv_lens, scale: float | None = None, *,
-                      num_blocks: int | None = None, out=None, return_lse: bool = False, lse=None,
+                      num_blocks: int | None = None, out=None, out_dtype=None, return_lse: bool = False, lse=None,
                       workspace=None, cu_seqlens_q_dev=None, kv_lens_dev=None, stream=None):
     """Mixed prefill + decode batch over a paged pool; see ``chunk_attn_varlen``.
 
     ``cu_seqlens_q`` and ``kv_lens`` are host sequences (int32); device copies
     are made unless given.  ``block_tables`` is ``[num_seqs, max_blocks]`` int32
-    on the device.
+    on the device.  The output is bf16 or fp32 (``out_dtype``, or that of ``out``).
     """
     total_q, heads, d = q.shape
     hkv, dv = k_pool.shape[1], v_pool.shape[3]
@@ -373,7 +373,7 @@ def chunk_attn_varlen(q, k_pool, v_pool, block_tables, cu_seqlens_q, kv_lens, sc
     if kv_lens_dev is None:
         kv_lens_dev = kv.to(q.device)
     if out is None:
-        out = torch.empty((total_q, heads, dv), dtype=q.dtype, device=q.device)
+        out = torch.empty((total_q, heads, dv), dtype=out_dtype or q.dtype, device=q.device)
     if return_lse and lse is None:
         lse = torch.empty((heads, total_q), dtype=torch.float32, device=q.device)
     if workspace is None:
@@ -382,8 +382,8 @@ def chunk_attn_varlen(q, k_pool, v_pool, block_tables, cu_seqlens_q, kv_lens, sc
     _check(lib().chunk_attn_varlen(
         _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables), block_tables.shape[1],
         k_pool.shape[0] if num_blocks is None else num_blocks, _ptr(cu_seqlens_q_dev), _ptr(kv_lens_dev),
-        cu.data_ptr(), kv.data_ptr(), n, heads, hkv, d, dv, float(scale), _ptr(out), _ptr(lse),
-        _ptr(workspace), workspace.numel(), _stream(stream)))
+        cu.data_ptr(), kv.data_ptr(), n, heads, hkv, d, dv, float(scale), _ptr(out), _dtype_code(out.dtype),
+        _ptr(lse), _ptr(workspace), workspace.numel(), _stream(stream)))
     return (out, lse) if return_lse else out
 
 
@@ -394,7 +394,8 @@ def chunk_attn_varlen_noalloc(q, k_pool, v_pool, block_tables, cu_seqlens_q, kv_
 
     For callers that cannot allocate: every tensor, the output and the device
     copies of the lengths included, must be passed in; this function creates
-    none.  ``cu_seqlens_q`` and ``kv_lens`` are host sequences (int32).
+    none.  ``cu_seqlens_q`` and ``kv_lens`` are host sequences (int32); the
+    output dtype (bf16 or fp32) is that of ``out``.
     """
     total_q, heads, d = q.shape
     hkv, dv = k_pool.shape[1], v_pool.shape[3]
@@ -403,8 +404,8 @@ def chunk_attn_varlen_noalloc(q, k_pool, v_pool, block_tables, cu_seqlens_q, kv_
     _check(lib().chunk_attn_varlen_noalloc(
         _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables), block_tables.shape[1],
         k_pool.shape[0] if num_blocks is None else num_blocks, _ptr(cu_seqlens_q_dev), _ptr(kv_lens_dev),
-        cu.data_ptr(), kv.data_ptr(), kv.numel(), heads, hkv, d, dv, float(scale), _ptr(out), _ptr(lse),
-        _stream(stream)))
+        cu.data_ptr(), kv.data_ptr(), kv.numel(), heads, hkv, d, dv, float(scale), _ptr(out), _dtype_code(out.dtype),
+        _ptr(lse), _stream(stream)))
     return out
 
 

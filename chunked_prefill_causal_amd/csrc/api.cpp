@@ -532,7 +532,7 @@ static bool co_schedule_pays(const int32_t* cu, const int32_t* kv, int num_seqs,
 static ca_status varlen_run(const void* q, const void* k_pool, const void* v_pool, const int32_t* block_tables,
                      int32_t max_blocks, int32_t num_blocks, const int32_t* cu_dev, const int32_t* kv_dev,
                      const int32_t* cu, const int32_t* kv, int32_t num_seqs, int32_t heads, int32_t kv_heads,
-                     int32_t head_dim, int32_t head_dim_v, float scale, void* out, float* lse_out,
+                     int32_t head_dim, int32_t head_dim_v, float scale, void* out, int32_t out_dtype, float* lse_out,
                      void* workspace, size_t workspace_bytes, bool static_scratch, void* stream) {
   if (!k_pool || !v_pool || !block_tables || !cu_dev || !kv_dev || !cu || !kv)
     return fail(CA_EINVAL, "null pointer argument");
@@ -547,6 +547,8 @@ static ca_status varlen_run(const void* q, const void* k_pool, const void* v_poo
     return fail(CA_EINVAL, "heads (%d) must be a positive multiple of kv_heads (%d)", heads, kv_heads);
   if (max_blocks <= 0 || num_blocks <= 0) return fail(CA_EINVAL, "max_blocks_per_seq and num_blocks must be > 0");
   if (!std::isfinite(scale) || !(scale > 0.f)) return fail(CA_EINVAL, "scale must be finite and > 0");
+  if (out_dtype != CA_BF16 && out_dtype != CA_F32) return fail(CA_EINVAL, "out_dtype must be CA_BF16 or CA_F32");
+  const DType dout = out_dtype == CA_F32 ? DType::F32 : DType::BF16;
   if (!prefill_supported(DType::BF16, DType::BF16, head_dim, head_dim_v) || !decode_supported(head_dim, head_dim_v))
     return fail(CA_EUNSUPPORTED, "unsupported (head_dim, head_dim_v) = (%d, %d)", head_dim, head_dim_v);
   if (cu[0] != 0) return fail(CA_EINVAL, "cu_seqlens_q[0] must be 0");
@@ -606,6 +608,7 @@ static ca_status varlen_run(const void* q, const void* k_pool, const void* v_poo
   d.split_tokens = plan.split_tokens;
   d.tok_wg = paged_rows / hpw;
   d.n_head_groups = heads / hpw;
+  d.out_f32 = dout == DType::F32 ? 1 : 0;
   d.scale_log2 = cs;
   hipError_t e = launch_batch_plan(d, st);
   if (e != hipSuccess) return hip_status(e, "varlen plan launch");
@@ -644,7 +647,7 @@ static ca_status varlen_run(const void* q, const void* k_pool, const void* v_poo
         e = hipEventRecord(cs2->fork, st);
         if (e == hipSuccess) e = hipStreamWaitEvent(cs2->prefill, cs2->fork, 0);
         if (e == hipSuccess) e = hipStreamWaitEvent(cs2->decode, cs2->fork, 0);
-        if (e == hipSuccess) e = launch_prefill_paged_varlen(head_dim, head_dim_v, a, (int)plan.prefill_wgs, cs2->prefill);
+        if (e == hipSuccess) e = launch_prefill_paged_varlen(dout, head_dim, head_dim_v, a, (int)plan.prefill_wgs, cs2->prefill);
         if (e == hipSuccess) e = launch_decode(head_dim, head_dim_v, d, plan.max_splits, 0, num_seqs, cs2->decode);
         if (e == hipSuccess) e = launch_decode_merge(head_dim_v, d, cs2->decode);
         if (e == hipSuccess) e = hipEventRecord(cs2->join_prefill, cs2->prefill);
@@ -655,7 +658,7 @@ static ca_status varlen_run(const void* q, const void* k_pool, const void* v_poo
         return ok();
       }
     }
-    e = launch_prefill_paged_varlen(head_dim, head_dim_v, a, (int)plan.prefill_wgs, st);
+    e = launch_prefill_paged_varlen(dout, head_dim, head_dim_v, a, (int)plan.prefill_wgs, st);
     if (e != hipSuccess) return hip_status(e, "varlen prefill launch");
   }
   if (plan.n_decode) {
@@ -669,19 +672,21 @@ static ca_status varlen_run(const void* q, const void* k_pool, const void* v_poo
 ca_status chunk_attn_varlen(const void* q, const void* k_pool, const void* v_pool, const int32_t* block_tables,
                             int32_t max_blocks, int32_t num_blocks, const int32_t* cu_dev, const int32_t* kv_dev,
                             const int32_t* cu, const int32_t* kv, int32_t num_seqs, int32_t heads, int32_t kv_heads,
-                            int32_t head_dim, int32_t head_dim_v, float scale, void* out, float* lse_out,
-                            void* workspace, size_t workspace_bytes, void* stream) {
+                            int32_t head_dim, int32_t head_dim_v, float scale, void* out, int32_t out_dtype,
+                            float* lse_out, void* workspace, size_t workspace_bytes, void* stream) {
   return varlen_run(q, k_pool, v_pool, block_tables, max_blocks, num_blocks, cu_dev, kv_dev, cu, kv, num_seqs, heads,
-                    kv_heads, head_dim, head_dim_v, scale, out, lse_out, workspace, workspace_bytes, false, stream);
+                    kv_heads, head_dim, head_dim_v, scale, out, out_dtype, lse_out, workspace, workspace_bytes, false,
+                    stream);
 }
 
 ca_status chunk_attn_varlen_noalloc(const void* q, const void* k_pool, const void* v_pool,
                                     const int32_t* block_tables, int32_t max_blocks, int32_t num_blocks,
                                     const int32_t* cu_dev, const int32_t* kv_dev, const int32_t* cu, const int32_t* kv,
                                     int32_t num_seqs, int32_t heads, int32_t kv_heads, int32_t head_dim,
-                                    int32_t head_dim_v, float scale, void* out, float* lse_out, void* stream) {
+                                    int32_t head_dim_v, float scale, void* out, int32_t out_dtype, float* lse_out,
+                                    void* stream) {
   return varlen_run(q, k_pool, v_pool, block_tables, max_blocks, num_blocks, cu_dev, kv_dev, cu, kv, num_seqs, heads,
-                    kv_heads, head_dim, head_dim_v, scale, out, lse_out, nullptr, 0, true, stream);
+                    kv_heads, head_dim, head_dim_v, scale, out, out_dtype, lse_out, nullptr, 0, true, stream);
 }
 
 ca_status chunkattn_kv_append(const void* k_new, const void* v_new, int64_t start_pos, int64_t n_tokens,

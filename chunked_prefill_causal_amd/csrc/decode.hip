@@ -252,8 +252,9 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const DecodeArgs a) {
       acc += *(const f32x4_t*)(a.ws_o + (slot0 + sp) * DV + 4 * q4) * fast_exp2(m - M);
     }
     acc *= 1.f / L;
-    uint16_t* orow = (uint16_t*)a.out + ((int64_t)(q0 + i) * a.heads + h) * DV + 4 * q4;
-    *(u32x2_t*)orow = u32x2_t{pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3])};
+    const int64_t o_off = ((int64_t)(q0 + i) * a.heads + h) * DV + 4 * q4;
+    if (a.out_f32) *(f32x4_t*)((float*)a.out + o_off) = acc;
+    else *(u32x2_t*)((uint16_t*)a.out + o_off) = u32x2_t{pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3])};
     if (a.lse && q4 == 0) a.lse[(int64_t)h * a.total_q + q0 + i] = (M + __log2f(L)) * kLn2;
   }
 }

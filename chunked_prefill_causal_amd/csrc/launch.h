@@ -69,6 +69,7 @@ struct DecodeArgs {
   int32_t split_tokens;          // keys per split (multiple of 64)
   int32_t tok_wg;                // query tokens per prefill workgroup
   int32_t n_head_groups;         // prefill workgroups per token block
+  int32_t out_f32;               // 1: fp32 output, 0: bf16
   float scale_log2;
 };
 
@@ -81,7 +82,7 @@ bool prefill_paged_supported(int D, int DV);
 // Query rows per workgroup of the paged bf16 kernel for these head dims.
 int prefill_paged_rows(int D, int DV);
 hipError_t launch_prefill_paged(DType out, int D, int DV, const PrefillArgs& a, int grid, hipStream_t stream);
-hipError_t launch_prefill_paged_varlen(int D, int DV, const PrefillArgs& a, int grid, hipStream_t stream);
+hipError_t launch_prefill_paged_varlen(DType out, int D, int DV, const PrefillArgs& a, int grid, hipStream_t stream);
 bool prefill_supported(DType in, DType out, int D, int DV);
 
 hipError_t launch_batch_plan(const DecodeArgs& a, hipStream_t stream);

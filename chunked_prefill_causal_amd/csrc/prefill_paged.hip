@@ -653,8 +653,9 @@ hipError_t launch_prefill_paged(DType out, int D, int DV, const PrefillArgs& a, 
   return launch_paged_dims<float, false>(D, DV, a, grid, stream);
 }
 
-hipError_t launch_prefill_paged_varlen(int D, int DV, const PrefillArgs& a, int grid, hipStream_t stream) {
-  return launch_paged_dims<uint16_t, true>(D, DV, a, grid, stream);
+hipError_t launch_prefill_paged_varlen(DType out, int D, int DV, const PrefillArgs& a, int grid, hipStream_t stream) {
+  if (out == DType::BF16) return launch_paged_dims<uint16_t, true>(D, DV, a, grid, stream);
+  return launch_paged_dims<float, true>(D, DV, a, grid, stream);
 }
 
 }  // namespace chunkattn

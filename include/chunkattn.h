@@ -62,7 +62,7 @@ extern "C" {
 #endif
 
 #define CA_BLOCK_SIZE 64
-#define CHUNKATTN_VERSION 2
+#define CHUNKATTN_VERSION 3
 
 typedef enum {
   CA_OK = 0,
@@ -180,7 +180,9 @@ int32_t chunkattn_prefill_auto_splits(int64_t past_len, int64_t chunk_len, int32
  * Sequence s owns query rows [cu_seqlens_q[s], cu_seqlens_q[s+1]) of q and
  * out; its kv_lens[s] cached tokens include those rows' own keys, so its
  * queries sit at positions kv_lens[s] - q_len_s .. kv_lens[s] - 1.
- *   q            [total_q, heads, head_dim] bf16,  out [total_q, heads, head_dim_v] bf16
+ *   q            [total_q, heads, head_dim] bf16
+ *   out          [total_q, heads, head_dim_v] in out_dtype: CA_BF16 (rounded to
+ *                nearest even) or CA_F32
  *   k_pool, v_pool  paged layout above (bf16)
  *   block_tables [num_seqs, max_blocks_per_seq] device int32
  *   cu_seqlens_q [num_seqs + 1], kv_lens [num_seqs]   device int32
@@ -210,7 +212,7 @@ ca_status chunk_attn_varlen(const void* q, const void* k_pool, const void* v_poo
                             const int32_t* cu_seqlens_q_host, const int32_t* kv_lens_host,
                             int32_t num_seqs, int32_t heads, int32_t kv_heads,
                             int32_t head_dim, int32_t head_dim_v, float scale,
-                            void* out, float* lse_out,
+                            void* out, int32_t out_dtype, float* lse_out,
                             void* workspace, size_t workspace_bytes, void* stream);
 
 /* Workspace bytes chunk_attn_varlen needs for this batch (host arrays). */
@@ -246,7 +248,7 @@ ca_status chunk_attn_varlen_noalloc(const void* q, const void* k_pool, const voi
                                     const int32_t* cu_seqlens_q_host, const int32_t* kv_lens_host,
                                     int32_t num_seqs, int32_t heads, int32_t kv_heads,
                                     int32_t head_dim, int32_t head_dim_v, float scale,
-                                    void* out, float* lse_out, void* stream);
+                                    void* out, int32_t out_dtype, float* lse_out, void* stream);
 
 /*
  * chunkattn_kv_append — write n_tokens new keys/values of one sequence into

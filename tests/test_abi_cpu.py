@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_defaults():
-    assert L.version() == 2
+    assert L.version() == 3
     o = L.PrefillOpts()
     o.num_splits = 7
     L.lib().ca_prefill_opts_init(ctypes.byref(o))
@@ -128,12 +128,12 @@ def test_workspace_queries():
 
 
 def varlen(q=FAKE, cu=(0, 1, 2), kv=(10, 20), hq=8, hkv=2, d=128, dv=128, ws=FAKE, ws_bytes=1 << 30,
-           max_blocks=4, num_blocks=8, scale=0.1, out=FAKE, k=FAKE):
+           max_blocks=4, num_blocks=8, scale=0.1, out=FAKE, k=FAKE, out_dtype=L.CA_BF16):
     cu_a = (ctypes.c_int32 * len(cu))(*cu)
     kv_a = (ctypes.c_int32 * len(kv))(*kv)
     return L.lib().chunk_attn_varlen(q, k, FAKE, FAKE, max_blocks, num_blocks, FAKE, FAKE,
                                      ctypes.addressof(cu_a), ctypes.addressof(kv_a), len(kv), hq, hkv, d, dv,
-                                     scale, out, None, ws, ws_bytes, None)
+                                     scale, out, out_dtype, None, ws, ws_bytes, None)
 
 
 def test_contiguous_workspace_query():
@@ -169,18 +169,19 @@ def test_contiguous_workspace_query():
     (dict(ws=FAKE + 16), L.CA_EINVAL),                 # workspace must be 256-byte aligned
     (dict(scale=-1.0), L.CA_EINVAL),
     (dict(max_blocks=0), L.CA_EINVAL),
+    (dict(out_dtype=7), L.CA_EINVAL),
 ])
 def test_varlen_rejections(kwargs, status):
     assert varlen(**kwargs) == status
 
 
 def varlen_noalloc(q=FAKE, cu=(0, 1, 2), kv=(10, 20), hq=8, hkv=2, d=128, dv=128, max_blocks=4, num_blocks=8,
-                   scale=0.1, out=FAKE, k=FAKE):
+                   scale=0.1, out=FAKE, k=FAKE, out_dtype=L.CA_BF16):
     cu_a = (ctypes.c_int32 * len(cu))(*cu)
     kv_a = (ctypes.c_int32 * len(kv))(*kv)
     return L.lib().chunk_attn_varlen_noalloc(q, k, FAKE, FAKE, max_blocks, num_blocks, FAKE, FAKE,
                                              ctypes.addressof(cu_a), ctypes.addressof(kv_a), len(kv), hq, hkv, d, dv,
-                                             scale, out, None, None)
+                                             scale, out, out_dtype, None, None)
 
 
 @pytest.mark.parametrize("kwargs,status", [
@@ -189,6 +190,7 @@ def varlen_noalloc(q=FAKE, cu=(0, 1, 2), kv=(10, 20), hq=8, hkv=2, d=128, dv=128
     (dict(kv=(10, 300)), L.CA_ERANGE),
     (dict(d=128, dv=64), L.CA_EUNSUPPORTED),
     (dict(scale=float("nan")), L.CA_EINVAL),
+    (dict(out_dtype=-1), L.CA_EINVAL),
 ])
 def test_varlen_noalloc_rejections(kwargs, status):
     """The allocation-free varlen entry validates like chunk_attn_varlen, before any HIP call."""

@@ -44,6 +44,32 @@ def test_mixed_small():
     check_batch([200, 1, 1, 1, 1], [1300, 1, 64, 65, 3000], 32, 8, 128, 128, 5000)
 
 
+@pytest.mark.parametrize("d,dv,hq,hkv", [(128, 128, 32, 8), (192, 128, 16, 16), (64, 64, 8, 2)])
+def test_fp32_output(d, dv, hq, hkv):
+    """out_dtype fp32: every row against the oracle at the plain bar (no bf16 store), and the bf16 output of
+    the same batch equals the fp32 output rounded to bf16 bit for bit (one rounding of the same value)."""
+    q_lens = [300, 1, 1, 3, 1, 0, 150]
+    kv_lens = [1000, 77, 4100, 600, 1, 9, 150]
+    pool, tables, cu, q_all, seqs = build_batch(q_lens, kv_lens, hq, hkv, d, dv, 5050 + d)
+    scale = 1.0 / math.sqrt(d)
+    log(f"varlen fp32 output d={d}/{dv} heads {hq}/{hkv}")
+    out32, lse32 = L.chunk_attn_varlen(q_all.cuda(), pool.k, pool.v, tables, cu, kv_lens, scale,
+                                       out_dtype=torch.float32, return_lse=True)
+    out16, lse16 = L.chunk_attn_varlen(q_all.cuda(), pool.k, pool.v, tables, cu, kv_lens, scale, return_lse=True)
+    assert out32.dtype == torch.float32 and out16.dtype == torch.bfloat16
+    assert torch.equal(out32.to(torch.bfloat16).view(torch.int16), out16.view(torch.int16))
+    assert torch.equal(lse32, lse16)
+    worst = worst_lse = 0.0
+    for s, (q, k, v) in enumerate(seqs):
+        if q_lens[s] == 0:
+            continue
+        ref, ref_lse = oracle_chunk(q, k, v, kv_lens[s] - q_lens[s], scale)
+        worst = max(worst, max_err(out32[cu[s]: cu[s + 1]], ref))
+        worst_lse = max(worst_lse, max_err(lse32[:, cu[s]: cu[s + 1]], ref_lse))
+    log(f"  max err {worst:.3e}, lse {worst_lse:.2e}")
+    assert worst <= BF16_TOL and worst_lse <= LSE_TOL
+
+
 def test_decode_only_ragged_contexts():
     rng = np.random.default_rng(3)
     kv = rng.integers(1, 5000, size=24).tolist()
