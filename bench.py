@@ -73,6 +73,8 @@ def parse():
     p.add_argument("--reps", type=int, default=10, help="repetitions for the decode-only / prefill-only timings")
     p.add_argument("--copy-calibration", action="store_true",
                    help="after the timed region, copy 1 GiB device to device (a known-size kernel for counter scaling)")
+    p.add_argument("--alp-only", action="store_true",
+                   help="time only the latency-predictor grid on the 128K prompt's cache (prints its JSON object)")
     p.add_argument("--mla-only", action="store_true",
                    help="time only the MLA latent decode batches and prompt (prints their JSON object)")
     p.add_argument("--chunk-reps", type=int, default=20, help="repetitions per chunk for the latency distribution")
@@ -731,20 +733,24 @@ def latency_predictor(L, loop, torch, reps=3):
     fits = {}
     # The times span three orders of magnitude and the score is relative, so each observation is
     # weighted by 1/T^2: the fit sees x / T with target 1 (relative least squares).
-    for name, feat in (("token_count_only", lambda q, kv: [1.0, sum(q) / 1e3, 0.0, 0.0]),
-                       ("alp_features", lambda q, kv: list(L.chunkattn_alp_features(q, kv)))):
+    H, G = w.heads, w.kv_heads
+    for name, feat in (("token_count_only", lambda q, kv: [1.0, sum(q) / 1e3, 0.0, 0.0, 0.0]),
+                       ("alp_features", lambda q, kv: list(L.chunkattn_alp_features(q, kv, H, G)[:4]) + [0.0]),
+                       ("alp_plus_fill", lambda q, kv: list(L.chunkattn_alp_features(q, kv, H, G)))):
         model = L.AlpPredictor(1.0, 1e6)
         for i in train:
             model.update([v / times[i] for v in feat(*cases[i])], 1.0)
         err = [abs(model.predict(feat(*cases[i])) - times[i]) / times[i] for i in test]
         fits[name] = {"mape_holdout": round(float(np.mean(err)), 4), "max_ape": round(float(np.max(err)), 4),
                       "theta": [round(t, 6) for t in model.theta]}
-    samples = [[sum(q), len(q)] + [round(v, 6) for v in L.chunkattn_alp_features(q, kv)[1:]] + [round(t, 5)]
+    samples = [[sum(q), len(q)] + [round(v, 6) for v in L.chunkattn_alp_features(q, kv, H, G)[1:]] + [round(t, 5)]
                for (q, kv), t in zip(cases, times)]
     return {"cases": len(cases), "train": len(train), "holdout": len(test), "unit": "ms",
-            "features": "[1, sum(L_past*L_pre)/1e6, sum(L_pre^2)/1e6, sum(L_dec)/1e3]",
+            "features": "[1, sum(L_past*L_pre)/1e6, sum(L_pre^2)/1e6, sum(L_dec)/1e3, fill]; alp_features fits the "
+                        "first four (the pages' model), alp_plus_fill all five (fill: idle fraction of the prefill "
+                        "launch's last round x its causal pairs / 1e6)",
             "fit": "recursive least squares on x/T -> 1 (relative error), lambda 1, delta 1e6", **fits,
-            "samples": {"columns": ["new_tokens", "sequences", "past_x_pre_M", "pre_sq_M", "dec_ctx_K", "ms"],
+            "samples": {"columns": ["new_tokens", "sequences", "past_x_pre_M", "pre_sq_M", "dec_ctx_K", "fill_M", "ms"],
                         "rows": samples}}
 
 
@@ -830,6 +836,9 @@ def main():
         return
     log("generating inputs in HBM")
     loop = PrefillLoop(L, inputs, torch)
+    if args.alp_only:
+        print(json.dumps({"latency_predictor": latency_predictor(L, loop, torch)}), flush=True)
+        return
     mixed = MixedBatch(L, inputs, torch)
     dec_only = MixedBatch(L, inputs, torch, decode_only=True, parent=mixed)
     pre_only = MixedBatch(L, inputs, torch, prefill_only=True, parent=mixed)
@@ -917,7 +926,8 @@ def main():
     log("timing the latency-predictor grid")
     alp = latency_predictor(L, loop, torch)
     log(f"latency predictor held-out MAPE: token count only {alp['token_count_only']['mape_holdout']:.3f}, "
-        f"ALP features {alp['alp_features']['mape_holdout']:.3f}")
+        f"ALP features {alp['alp_features']['mape_holdout']:.3f}, with the fill term "
+        f"{alp['alp_plus_fill']['mape_holdout']:.3f} (worst {alp['alp_plus_fill']['max_ape']:.3f})")
     sched = schedule_summary(L, per_chunk)
     log(f"schedules on the measured chunk latencies: CPP {sched['cpp']['makespan_ms']} ms, "
         f"VPP {sched['vpp']['makespan_ms']} ms, VPP-Async {sched['vpp_async']['makespan_ms']} ms")

@@ -55,7 +55,7 @@ class PrefillOpts(ctypes.Structure):
                 ("v_stride_head", ctypes.c_int64)]
 
 
-ALP_FEATURES = 4
+ALP_FEATURES = 5
 
 
 class AlpState(ctypes.Structure):
@@ -101,7 +101,7 @@ def lib() -> ctypes.CDLL:
     L.chunkattn_sched_simulate.restype = ctypes.c_int
     L.chunkattn_sched_drain_pack.argtypes = [i32, f64, i32, vp, vp]
     L.chunkattn_sched_drain_pack.restype = i32
-    L.chunkattn_alp_features.argtypes = [i32, vp, vp, vp]
+    L.chunkattn_alp_features.argtypes = [i32, vp, vp, i32, i32, vp]
     L.chunkattn_alp_features.restype = ctypes.c_int
     L.chunkattn_alp_init.argtypes = [ctypes.POINTER(AlpState), f64, f64]
     L.chunkattn_alp_init.restype = ctypes.c_int
@@ -189,15 +189,17 @@ def chunkattn_sched_simulate(kind: int, tau, comm: float = 0.0, request=None, pa
     return {"start": start, "end": end, "busy": busy, "makespan": span.value}
 
 
-def chunkattn_alp_features(q_lens, kv_lens):
-    """ALP feature vector of a batch (FastPP notes §2.3): [1, sum Lpast*Lpre/1e6, sum Lpre^2/1e6, sum Ldec/1e3]."""
+def chunkattn_alp_features(q_lens, kv_lens, heads: int, kv_heads: int):
+    """ALP feature vector of a batch (FastPP notes §2.3): [1, sum Lpast*Lpre/1e6, sum Lpre^2/1e6, sum Ldec/1e3]
+    and the prefill launch's fill term for ``heads`` / ``kv_heads``."""
     import numpy as np
 
     q = np.ascontiguousarray(q_lens, dtype=np.int32)
     kv = np.ascontiguousarray(kv_lens, dtype=np.int32)
     x = np.empty(ALP_FEATURES, dtype=np.float64)
     _check(lib().chunkattn_alp_features(q.shape[0], q.ctypes.data if q.shape[0] else None,
-                                        kv.ctypes.data if kv.shape[0] else None, x.ctypes.data))
+                                        kv.ctypes.data if kv.shape[0] else None, int(heads), int(kv_heads),
+                                        x.ctypes.data))
     return x
 
 

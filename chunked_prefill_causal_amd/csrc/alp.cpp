@@ -10,9 +10,14 @@
 // the place of the notes' offline token-linear term:
 //
 //   T = theta0 + theta1 * sum(L_past L_pre) / 1e6 + theta2 * sum(L_pre^2) / 1e6
-//       + theta3 * sum(L_dec) / 1e3
+//       + theta3 * sum(L_dec) / 1e3 + theta4 * fill
 //
-// (features scaled to millions / thousands of tokens).  The least-squares fit
+// (features scaled to millions / thousands of tokens).  The fill term is this
+// library's addition: a prefill launch of W workgroups (one per CU) on 256 CUs
+// runs ceil(W / 256) rounds, and a short chunk leaves most of its last round
+// idle, which no term linear in the pages' features expresses.  fill = (ceil(W /
+// 256) * 256 / W - 1) x the launch's causal pairs / 1e6: the work the idle CUs
+// stand for.  The least-squares fit
 // is recursive with a forgetting factor lambda, kept in information form: the
 // exponentially weighted normal equations
 //   R <- lambda R + x x',  b <- lambda b + x y,  R_0 = I / delta,
@@ -28,6 +33,8 @@
 namespace chunkattn {
 void set_error(const char* fmt, ...);
 void clear_error();
+int64_t varlen_prefill_workgroups(int q_len, int heads, int kv_heads);
+int num_cus();
 }
 
 using chunkattn::clear_error;
@@ -43,12 +50,17 @@ bool finite_vec(const double* x, int n) {
 }  // namespace
 
 extern "C" ca_status chunkattn_alp_features(int32_t num_seqs, const int32_t* q_lens, const int32_t* kv_lens,
-                                            double* x) {
+                                            int32_t heads, int32_t kv_heads, double* x) {
   if (num_seqs < 0 || !x || (num_seqs > 0 && (!q_lens || !kv_lens))) {
     set_error("chunkattn_alp_features: need num_seqs >= 0, q_lens, kv_lens and x");
     return CA_EINVAL;
   }
-  double past_pre = 0.0, pre_sq = 0.0, dec = 0.0;
+  if (heads <= 0 || kv_heads <= 0 || heads % kv_heads != 0) {
+    set_error("chunkattn_alp_features: heads (%d) must be a positive multiple of kv_heads (%d)", heads, kv_heads);
+    return CA_EINVAL;
+  }
+  double past_pre = 0.0, pre_sq = 0.0, dec = 0.0, fill_pairs = 0.0;
+  int64_t wgs = 0;
   for (int32_t s = 0; s < num_seqs; ++s) {
     const int64_t q = q_lens[s], kv = kv_lens[s];
     if (q < 0 || kv < q) {
@@ -62,11 +74,19 @@ extern "C" ca_status chunkattn_alp_features(int32_t num_seqs, const int32_t* q_l
       past_pre += (double)(kv - q) * (double)q;
       pre_sq += (double)q * (double)q;
     }
+    const int64_t w = chunkattn::varlen_prefill_workgroups((int)q, heads, kv_heads);
+    if (w) {
+      wgs += w;
+      fill_pairs += (double)(kv - q) * (double)q + (double)q * (double)(q + 1) / 2.0;
+    }
   }
+  const int64_t cus = chunkattn::num_cus();
+  const double idle = wgs ? (double)((wgs + cus - 1) / cus * cus) / (double)wgs - 1.0 : 0.0;
   x[0] = 1.0;
   x[1] = past_pre / 1e6;
   x[2] = pre_sq / 1e6;
   x[3] = dec / 1e3;
+  x[4] = idle * fill_pairs / 1e6;
   clear_error();
   return CA_OK;
 }

@@ -107,12 +107,9 @@ struct BatchPlan {
   }
 };
 
-BatchPlan plan_batch(const int32_t* cu, const int32_t* kv, int num_seqs, int heads, int kv_heads, int dv,
-                     int paged_rows) {
+BatchPlan plan_batch(const int32_t* cu, const int32_t* kv, int num_seqs, int heads, int kv_heads, int dv) {
   BatchPlan p;
   const int group = heads / kv_heads;
-  const int hpw = heads_per_wg(group, kWavesPaged);
-  const int tok_wg = paged_rows / hpw;
   p.split_tokens = decode_split_tokens(cu, kv, num_seqs, kv_heads, group);
   for (int s = 0; s < num_seqs; ++s) {
     const int q_len = cu[s + 1] - cu[s];
@@ -122,7 +119,7 @@ BatchPlan plan_batch(const int32_t* cu, const int32_t* kv, int num_seqs, int hea
       if (ns > p.max_splits) p.max_splits = ns;
       ++p.n_decode;
     } else if (q_len > 0) {
-      p.prefill_wgs += (int64_t)((q_len + tok_wg - 1) / tok_wg) * (heads / hpw);
+      p.prefill_wgs += varlen_prefill_workgroups(q_len, heads, kv_heads);
       ++p.n_prefill;
     }
   }
@@ -158,6 +155,16 @@ ca_status check_dtype(int d) {
 }  // namespace
 
 namespace chunkattn {
+// Workgroups chunk_attn_varlen launches for one sequence's prefill-path rows (0 for a decode-path
+// sequence); the latency predictor's fill feature uses the same count.
+int64_t varlen_prefill_workgroups(int q_len, int heads, int kv_heads) {
+  const int group = heads / kv_heads;
+  if (q_len < 1 || q_len * group <= 32) return 0;
+  const int hpw = heads_per_wg(group, kWavesPaged);
+  const int tok_wg = prefill_paged_rows(0, 0) / hpw;
+  return (int64_t)((q_len + tok_wg - 1) / tok_wg) * (heads / hpw);
+}
+int num_cus() { return kNumCUs; }
 // Error string of the calling thread, shared with the host-only entry points.
 void set_error(const char* fmt, ...) {
   va_list ap;
@@ -409,7 +416,7 @@ size_t chunkattn_varlen_workspace_size(const int32_t* cu, const int32_t* kv, int
                                        int32_t kv_heads, int32_t head_dim_v) {
   if (!cu || !kv || num_seqs <= 0 || heads <= 0 || kv_heads <= 0 || heads % kv_heads || head_dim_v <= 0) return 0;
   // the workspace does not depend on the prefill launch geometry
-  return plan_batch(cu, kv, num_seqs, heads, kv_heads, head_dim_v, prefill_paged_rows(128, 128)).total();
+  return plan_batch(cu, kv, num_seqs, heads, kv_heads, head_dim_v).total();
 }
 
 // Scratch of the allocation-free varlen entry: one array per device, in the
@@ -563,7 +570,7 @@ static ca_status varlen_run(const void* q, const void* k_pool, const void* v_poo
   const int64_t total_q = cu[num_seqs];
   const int group = heads / kv_heads;
   const int paged_rows = prefill_paged_rows(head_dim, head_dim_v);
-  const BatchPlan plan = plan_batch(cu, kv, num_seqs, heads, kv_heads, head_dim_v, paged_rows);
+  const BatchPlan plan = plan_batch(cu, kv, num_seqs, heads, kv_heads, head_dim_v);
   if (static_scratch) {
     if (plan.total() > kNoAllocScratchBytes)
       return fail(CA_EWORKSPACE, "this batch needs %zu scratch bytes; the allocation-free entry holds %zu",

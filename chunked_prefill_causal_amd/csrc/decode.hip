@@ -21,6 +21,8 @@
 //    computes each sequence's first slot (and each prefill-path sequence's
 //    first workgroup) from the device copies of the sequence lengths, so the
 //    host never uploads a plan.
+#include <algorithm>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -228,7 +230,10 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeArgs a) {
   if (hl == 0) *(float2*)(a.ws_ml + slot * 2) = make_float2(m_run == -INFINITY ? -INFINITY : m_run * cs, l_tot);
 }
 
-// ---- merge: one workgroup per sequence, DV/4 threads per row ------------------------
+// ---- merge: workgroup (sequence, block of 256 / (DV/4) rows), DV/4 threads per row ----
+// A long context has hundreds of splits per row; spreading rows over workgroups
+// and loading four splits at a time keeps the merge from becoming a serial
+// chain of loads when the batch has few sequences.
 template <int DV>
 __global__ __launch_bounds__(256) void decode_merge_kernel(const DecodeArgs a) {
   const int s = blockIdx.x;
@@ -236,20 +241,40 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const DecodeArgs a) {
   const int q_len = a.cu_seqlens_q[s + 1] - q0;
   if (!is_decode_seq(q_len, a.group)) return;
   const int nsplit = (a.kv_lens[s] + a.split_tokens - 1) / a.split_tokens;
-  constexpr int TPR = DV / 4;
+  constexpr int TPR = DV / 4, RPW = 256 / TPR;
   const int rows = q_len * a.heads;
-  for (int idx = threadIdx.x; idx < rows * TPR; idx += 256) {
-    const int row = idx / TPR, q4 = idx % TPR;
+  const int q4 = threadIdx.x % TPR;
+  for (int row = blockIdx.y * RPW + threadIdx.x / TPR; row < rows; row += gridDim.y * RPW) {
     const int i = row / a.heads, h = row % a.heads;
     const int64_t slot0 = a.ws_off[s] + (int64_t)row * nsplit;
     if (slot0 < 0 || slot0 + nsplit > a.total_slots) continue;
-    float M, L;
-    merge_weights(a.ws_ml + slot0 * 2, nsplit, 1, M, L);
+    float M = -INFINITY;
+    for (int s0 = 0; s0 < nsplit; s0 += 4) {
+      float m[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) m[j] = s0 + j < nsplit ? a.ws_ml[(slot0 + s0 + j) * 2] : -INFINITY;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) M = fmaxf(M, m[j]);
+    }
+    float L = 0.f;
     f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    for (int sp = 0; sp < nsplit; ++sp) {
-      const float m = a.ws_ml[(slot0 + sp) * 2];
-      if (m == -INFINITY) continue;
-      acc += *(const f32x4_t*)(a.ws_o + (slot0 + sp) * DV + 4 * q4) * fast_exp2(m - M);
+    for (int s0 = 0; s0 < nsplit; s0 += 4) {
+      float m[4], l[4];
+      f32x4_t v[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t sl = slot0 + min(s0 + j, nsplit - 1);
+        m[j] = s0 + j < nsplit ? a.ws_ml[sl * 2] : -INFINITY;
+        l[j] = a.ws_ml[sl * 2 + 1];
+        v[j] = *(const f32x4_t*)(a.ws_o + sl * DV + 4 * q4);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (m[j] == -INFINITY) continue;             // no visible key: no weight, O never written
+        const float wgt = fast_exp2(m[j] - M);
+        L += l[j] * wgt;
+        acc += v[j] * wgt;
+      }
     }
     acc *= 1.f / L;
     const int64_t o_off = ((int64_t)(q0 + i) * a.heads + h) * DV + 4 * q4;
@@ -284,8 +309,12 @@ hipError_t launch_decode(int D, int DV, const DecodeArgs& args, int max_splits, 
 }
 
 hipError_t launch_decode_merge(int DV, const DecodeArgs& a, hipStream_t stream) {
-  if (DV == 64) hipLaunchKernelGGL((decode_merge_kernel<64>), dim3(a.num_seqs), dim3(256), 0, stream, a);
-  else hipLaunchKernelGGL((decode_merge_kernel<128>), dim3(a.num_seqs), dim3(256), 0, stream, a);
+  // a decode-path sequence has q_len * group <= 32, so at most 32 * kv_heads rows; larger counts loop
+  const int max_rows = 32 * a.kv_heads;
+  const int rpw = DV == 64 ? 16 : 8;
+  const dim3 grid(a.num_seqs, std::min((max_rows + rpw - 1) / rpw, 4096));
+  if (DV == 64) hipLaunchKernelGGL((decode_merge_kernel<64>), grid, dim3(256), 0, stream, a);
+  else hipLaunchKernelGGL((decode_merge_kernel<128>), grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

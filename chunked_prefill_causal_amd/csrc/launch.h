@@ -79,6 +79,9 @@ hipError_t launch_prefill(DType in, DType out, int D, int DV, bool paged, const 
 hipError_t launch_prefill_merge(DType out, int DV, const PrefillArgs& a, hipStream_t stream);
 // Paged bf16 path: 8-wave workgroups (256 query rows), direct-to-LDS tiles.
 bool prefill_paged_supported(int D, int DV);
+// Workgroups chunk_attn_varlen launches for one sequence's prefill-path rows
+// (0 for a sequence that takes the decode path); defined with the host API.
+int64_t varlen_prefill_workgroups(int q_len, int heads, int kv_heads);
 // Query rows per workgroup of the paged bf16 kernel for these head dims.
 int prefill_paged_rows(int D, int DV);
 hipError_t launch_prefill_paged(DType out, int D, int DV, const PrefillArgs& a, int grid, hipStream_t stream);

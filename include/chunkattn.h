@@ -321,11 +321,17 @@ int32_t chunkattn_sched_drain_pack(int32_t n_chunks, double t, int32_t n_next, c
  * decode request — with coefficients adapted online by recursive least
  * squares with a forgetting factor.  For the kernel alone a constant term
  * replaces the notes' offline token-linear part:
- *   x = [1, sum(L_past * L_pre) / 1e6, sum(L_pre^2) / 1e6, sum(L_dec) / 1e3]
+ *   x = [1, sum(L_past * L_pre) / 1e6, sum(L_pre^2) / 1e6, sum(L_dec) / 1e3, fill]
  * where a sequence with q_len > 1 is a prefill chunk (L_pre = q_len,
  * L_past = kv_len - q_len) and one with q_len == 1 a decode (L_dec = kv_len).
+ * The fifth feature, this library's addition, is the GPU fill of the batch's
+ * prefill launch: with W the workgroups chunk_attn_varlen launches for its
+ * prefill-path sequences (256 query rows each, one per CU) and 256 CUs,
+ *   fill = (ceil(W / 256) * 256 / W - 1) * sum over them of causal pairs / 1e6,
+ * causal pairs = L_past * L_pre + L_pre (L_pre + 1) / 2: the work the idle
+ * CUs of the last round stand for (0 when W fills whole rounds).
  */
-#define CA_ALP_FEATURES 4
+#define CA_ALP_FEATURES 5
 typedef struct {
   double theta[CA_ALP_FEATURES];                     /* coefficients, time unit of the measurements */
   double info[CA_ALP_FEATURES * CA_ALP_FEATURES];    /* weighted normal matrix R (inverse covariance), row-major */
@@ -335,8 +341,11 @@ typedef struct {
 } ca_alp_state;
 
 /* Feature vector x[CA_ALP_FEATURES] of a batch (host arrays q_lens, kv_lens of
- * num_seqs sequences, kv_len >= q_len >= 0).  CA_OK or CA_EINVAL. */
-ca_status chunkattn_alp_features(int32_t num_seqs, const int32_t* q_lens, const int32_t* kv_lens, double* x);
+ * num_seqs sequences, kv_len >= q_len >= 0) run with heads query heads over
+ * kv_heads KV heads (they size the prefill launch of the fill feature).
+ * CA_OK or CA_EINVAL. */
+ca_status chunkattn_alp_features(int32_t num_seqs, const int32_t* q_lens, const int32_t* kv_lens, int32_t heads,
+                                 int32_t kv_heads, double* x);
 
 /* Start a recursive least-squares fit: theta = 0, R = I / delta (covariance delta * I), b = 0.
  * CA_OK or CA_EINVAL. */

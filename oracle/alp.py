@@ -24,14 +24,37 @@ Readings (also in the design notes):
       theta_n = (sum_i lam^(n-i) x_i x_i' + lam^n / delta I)^-1  sum_i lam^(n-i) x_i y_i
 
   so that solution, written out, is the reference here (not the recursion).
+* Fifth feature (this library's addition, not the notes'): the fill of the
+  batch's prefill launch.  The varlen entry sends a sequence to its prefill
+  kernel when q_len x (heads / kv_heads) > 32; that kernel runs 256 query
+  rows per workgroup — h consecutive heads of one KV group (h = the largest
+  of 8, 4, 2, 1 dividing the group) times 256 / h tokens — one workgroup per
+  CU on 256 CUs.  With W its workgroups, fill = (ceil(W / 256) * 256 / W - 1)
+  x its causal pairs (L_past L_pre + L_pre (L_pre + 1) / 2) / 1e6.
 """
 from __future__ import annotations
 
 import numpy as np
 
 
-def features(q_lens, kv_lens) -> list[float]:
-    past_pre = pre_sq = dec = 0.0
+CUS, ROWS_PER_WORKGROUP = 256, 256
+
+
+def prefill_workgroups(q: int, heads: int, kv_heads: int) -> int:
+    """Workgroups of one sequence's prefill-path launch (0 when it takes the decode path)."""
+    group = heads // kv_heads
+    if q < 1 or q * group <= 32:
+        return 0
+    h = next(h for h in (8, 4, 2, 1) if group % h == 0)
+    tokens = ROWS_PER_WORKGROUP // h
+    return -(-q // tokens) * (heads // h)
+
+
+def features(q_lens, kv_lens, heads: int, kv_heads: int) -> list[float]:
+    if heads <= 0 or kv_heads <= 0 or heads % kv_heads:
+        raise ValueError("heads must be a positive multiple of kv_heads")
+    past_pre = pre_sq = dec = fill_pairs = 0.0
+    wgs = 0
     for q, kv in zip(q_lens, kv_lens):
         q, kv = int(q), int(kv)
         if q < 0 or kv < q:
@@ -41,7 +64,12 @@ def features(q_lens, kv_lens) -> list[float]:
         elif q > 1:
             past_pre += (kv - q) * q
             pre_sq += q * q
-    return [1.0, past_pre / 1e6, pre_sq / 1e6, dec / 1e3]
+        w = prefill_workgroups(q, heads, kv_heads)
+        if w:
+            wgs += w
+            fill_pairs += (kv - q) * q + q * (q + 1) / 2
+    idle = (-(-wgs // CUS) * CUS) / wgs - 1.0 if wgs else 0.0
+    return [1.0, past_pre / 1e6, pre_sq / 1e6, dec / 1e3, idle * fill_pairs / 1e6]
 
 
 def weighted_ridge(xs, ys, lam: float = 1.0, delta: float = 1e6) -> np.ndarray:

@@ -32,18 +32,19 @@ def test_features_match():
     rng = np.random.default_rng(4)
     for _ in range(500):
         q, kv = random_batch(rng)
-        assert list(L.chunkattn_alp_features(q, kv)) == A.features(q, kv)
+        for heads, kv_heads in ((64, 8), (32, 8), (48, 8), (16, 16)):
+            assert list(L.chunkattn_alp_features(q, kv, heads, kv_heads)) == A.features(q, kv, heads, kv_heads)
 
 
 @pytest.mark.parametrize("lam,delta", [(1.0, 1e6), (0.99, 1e6), (0.9, 1e3), (1.0, 1e2)])
 def test_rls_matches_closed_form(lam, delta):
     rng = np.random.default_rng(int(lam * 1000) + int(delta))
-    theta_true = np.array([0.08, 0.011, 0.0055, 0.0021])
+    theta_true = np.array([0.08, 0.011, 0.0055, 0.0021, 0.004])
     p = L.AlpPredictor(lam, delta)
     xs, ys = [], []
     for i in range(120):
         q, kv = random_batch(rng)
-        x = A.features(q, kv)
+        x = A.features(q, kv, 64, 8)
         y = float(np.dot(theta_true, x)) * float(rng.uniform(0.95, 1.05))
         before = p.predict(x)
         err = p.update(x, y)
@@ -60,12 +61,14 @@ def test_rls_matches_closed_form(lam, delta):
 
 def test_rejections():
     with pytest.raises(L.ChunkAttnError):
-        L.chunkattn_alp_features([5], [4])
+        L.chunkattn_alp_features([5], [4], 64, 8)
+    with pytest.raises(L.ChunkAttnError):
+        L.chunkattn_alp_features([5], [5], 64, 0)
     with pytest.raises(L.ChunkAttnError):
         L.AlpPredictor(1.5, 1e6)
     with pytest.raises(L.ChunkAttnError):
         L.AlpPredictor(1.0, 0.0)
     p = L.AlpPredictor()
     with pytest.raises(L.ChunkAttnError):
-        p.update([1.0, np.nan, 0, 0], 1.0)
+        p.update([1.0, np.nan, 0, 0, 0], 1.0)
     assert p.state.n_obs == 0

@@ -12,20 +12,30 @@ from oracle import alp as A
 
 
 def test_features_by_hand():
-    # one 16384-token chunk after 49152 cached tokens
-    assert A.features([16384], [65536]) == [1.0, 49152 * 16384 / 1e6, 16384 ** 2 / 1e6, 0.0]
+    # one 16384-token chunk after 49152 cached tokens, 64 q / 8 KV heads: 16384 / 32 x 8 = 4096 workgroups,
+    # exactly 16 rounds of 256, so no fill term
+    assert A.features([16384], [65536], 64, 8) == [1.0, 49152 * 16384 / 1e6, 16384 ** 2 / 1e6, 0.0, 0.0]
     # two decodes (contexts 5000 and 20000) and an empty sequence
-    assert A.features([1, 1, 0], [5000, 20000, 7]) == [1.0, 0.0, 0.0, 25.0]
-    # a prefill from scratch has no past term
-    assert A.features([3], [3]) == [1.0, 0.0, 9e-6, 0.0]
+    assert A.features([1, 1, 0], [5000, 20000, 7], 64, 8) == [1.0, 0.0, 0.0, 25.0, 0.0]
+    # a prefill from scratch has no past term; 3 tokens x group 8 = 24 rows per KV head take the decode path
+    assert A.features([3], [3], 64, 8) == [1.0, 0.0, 9e-6, 0.0, 0.0]
+    # 512 tokens: 16 x 8 = 128 workgroups fill half of one round: idle fraction 1, pairs 1000*512 + 512*513/2
+    assert A.features([512], [1512], 64, 8)[4] == (1000 * 512 + 512 * 513 / 2) / 1e6
+    # 1056 tokens: 33 x 8 = 264 workgroups, two rounds: idle 512/264 - 1
+    assert A.features([1056], [1056], 64, 8)[4] == (512 / 264 - 1) * (1056 * 1057 / 2) / 1e6
+    # group 6 (48 q / 8 KV heads): 2 heads per workgroup, 128 tokens: 1000 tokens -> 8 x 24 = 192 workgroups
+    assert A.features([1000], [1000], 48, 8)[4] == (256 / 192 - 1) * (1000 * 1001 / 2) / 1e6
     with pytest.raises(ValueError):
-        A.features([5], [4])
+        A.features([5], [4], 64, 8)
+    with pytest.raises(ValueError):
+        A.features([5], [5], 64, 7)
 
 
 def test_noise_free_recovery():
     rng = np.random.default_rng(1)
-    theta = np.array([0.05, 0.9, 0.45, 0.002])
-    xs = np.column_stack([np.ones(40), rng.uniform(0, 2000, 40), rng.uniform(0, 300, 40), rng.uniform(0, 5000, 40)])
+    theta = np.array([0.05, 0.9, 0.45, 0.002, 0.3])
+    xs = np.column_stack([np.ones(40), rng.uniform(0, 2000, 40), rng.uniform(0, 300, 40), rng.uniform(0, 5000, 40),
+                          rng.uniform(0, 50, 40)])
     for lam in (1.0, 0.98, 0.9):
         got = A.weighted_ridge(xs, xs @ theta, lam, 1e14)
         assert np.allclose(got, theta, rtol=1e-7, atol=1e-9)
