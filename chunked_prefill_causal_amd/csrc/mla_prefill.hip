@@ -167,13 +167,19 @@ __global__ __launch_bounds__(256, 1) void mla_prefill_kernel(const MlaPrefillArg
   const __attribute__((address_space(4))) int32_t* bt4 = (const __attribute__((address_space(4))) int32_t*)a.block_table;
   const uint32_t smem_base = lds_addr(smem);
   const uint32_t lane_off = (uint32_t)(wave * 64 + lane) * 16;
-  auto issue = [&](int j, int st) {
+  // The next tile's loads go out one after every eighth QK MFMA (18 of them over
+  // the 144): issued as a burst they would hold the wave at issue while the
+  // direct-to-LDS path drains them.  Only the first tile, with no matrix phase
+  // before it, goes as a burst.
+  const unsigned char* pend_b = a.pool;
+  uint32_t pend_lds = 0;
+  auto prep = [&](int j, int st) {
     const int phys = a.block_table ? clamp_block(bt4[j], a.num_blocks) : j;   // null table: logical order
-    const unsigned char* b = a.pool + (int64_t)phys * kTileBytes;
-    const uint32_t lds = smem_base + st * kTileBytes + wave * 1024;
-#pragma unroll
-    for (int n = 0; n < kLoads; ++n)
-      dma16(b + n * kThreads * 16, lane_off, __builtin_amdgcn_readfirstlane(lds + n * kThreads * 16));
+    pend_b = a.pool + (int64_t)phys * kTileBytes;
+    pend_lds = smem_base + st * kTileBytes + wave * 1024;
+  };
+  auto dma_one = [&](int n) {
+    dma16(pend_b + n * kThreads * 16, lane_off, __builtin_amdgcn_readfirstlane(pend_lds + n * kThreads * 16));
   };
 
   f32x4_t o[kNDB][2];
@@ -190,7 +196,7 @@ __global__ __launch_bounds__(256, 1) void mla_prefill_kernel(const MlaPrefillArg
   // the block's 16, i.e. run 2 bb + (lc % 4) / 2, half lc % 2.
   const int v_lane = (4 * lg + (lc >> 2)) * 16 + (lc & 1) * 8 + ((lc & 3) >> 1) * 1024;
 
-  auto tile = [&](int j, int st, bool first) {
+  auto tile = [&](int j, int st, bool first, bool with_dma) {
     const unsigned char* stage = smem + st * kTileBytes;
     // ---- S^T = K Q^T ----
     f32x4_t s[4][2];
@@ -211,7 +217,13 @@ __global__ __launch_bounds__(256, 1) void mla_prefill_kernel(const MlaPrefillArg
           mfma16_vgpr(s[k & 3][1], rd[k], qreg[1][k >> 2]);
         }
         if (k + kAhead < kOps) rd[k + kAhead] = *k_ptr(k + kAhead);
+        if ((k & 3) == 3) {
+          __builtin_amdgcn_sched_barrier(0);
+          if (with_dma) dma_one(k >> 2);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
+      static_assert(kOps / 4 == kLoads, "one load per four K operands");
     }
     // the asm MFMAs wrote S^T: 18+ wait states before vector code reads it
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
@@ -323,11 +335,14 @@ __global__ __launch_bounds__(256, 1) void mla_prefill_kernel(const MlaPrefillArg
   };
 
   // ---- key loop: tile t in stage t % 2; tile t + 1 loads while tile t runs ----
-  issue(0, 0);
+  prep(0, 0);
+#pragma unroll
+  for (int n = 0; n < kLoads; ++n) dma_one(n);
   for (int t = 0; t < n_tiles; ++t) {
     wait_all_vmem();
     barrier();                                     // tile t landed everywhere; stage (t + 1) % 2 is free
-    if (t + 1 < n_tiles) issue(t + 1, (t + 1) & 1);
+    const bool pend = t + 1 < n_tiles;
+    if (pend) prep(t + 1, (t + 1) & 1);
     const int key0 = t * kBlock;
     if (key0 + kBlock > kv_len32) {
       // keys past the sequence end: zero their latent values (0 * NaN would poison O)
@@ -339,7 +354,7 @@ __global__ __launch_bounds__(256, 1) void mla_prefill_kernel(const MlaPrefillArg
       }
       barrier();
     }
-    tile(t, t & 1, t == 0);
+    tile(t, t & 1, t == 0, pend);
   }
 
   // ---- epilogue: lane (lg, lc) holds latent values 16 bb + 4 lg .. +3 of its rows ----
