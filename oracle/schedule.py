@@ -103,44 +103,52 @@ def simulate(kind: int, tau, comm: float = 0.0, request=None, pack: bool = True)
 
     ``tau[k]`` is chunk k's per-virtual-stage latency; ``request[k]`` (non-
     decreasing) groups chunks into requests for the packing rule.
+
+    With each rank's order fixed, the schedule is a precedence graph: an op
+    starts once its rank has finished the op before it, once the chunk's
+    previous stage has ended and been handed over, and (without packing) once
+    the previous request has ended (each a constraint "start >= end of an
+    earlier op + its hand-off delay").  The earliest start of every op is then
+    the longest path to it from time 0, computed here in topological order
+    (Kahn); a cycle means the orders cannot be run and is reported.
     """
     n = len(tau)
     request = list(request) if request is not None else [0] * n
     ranks = RANK_OF_STAGE[kind]
-    last_of = {}                              # request -> its last chunk
-    first_of = {}
+    last_of, first_of = {}, {}
     for k, r in enumerate(request):
         last_of[r] = k
         first_of.setdefault(r, k)
     orders = multi_orders(kind, tau, request, pack)
-    start, end = {}, {}
-    pos = [0, 0]                              # next op of each rank
-    free = [0.0, 0.0]
-    while pos[0] < len(orders[0]) or pos[1] < len(orders[1]):
-        progressed = False
-        for rank in (0, 1):
-            if pos[rank] >= len(orders[rank]):
-                continue
-            k, s = orders[rank][pos[rank]]
-            ready = free[rank]
-            if s > 0:                         # the chunk's previous stage
-                if (k, s - 1) not in end:
-                    continue
-                hop = comm if ranks[s - 1] != ranks[s] else 0.0
-                ready = max(ready, end[(k, s - 1)] + hop)
-            r = request[k]
-            if s == 0 and not pack and k == first_of[r] and r != request[0]:
-                prev_last = last_of[request[k - 1]]
-                if (prev_last, 3) not in end:
-                    continue
-                ready = max(ready, end[(prev_last, 3)])
-            start[(k, s)] = ready
-            end[(k, s)] = ready + tau[k]
-            free[rank] = end[(k, s)]
-            pos[rank] += 1
-            progressed = True
-        if not progressed:
-            raise RuntimeError("schedule deadlocked")
+    preds = {op: [] for order in orders for op in order}   # op -> [(earlier op, delay after its end)]
+    for order in orders:
+        for u, v in zip(order, order[1:]):
+            preds[v].append((u, 0.0))                       # the rank is busy with u first
+    for (k, s) in preds:
+        if s > 0:
+            hop = comm if ranks[s - 1] != ranks[s] else 0.0
+            preds[(k, s)].append(((k, s - 1), hop))
+        elif not pack and k == first_of[request[k]] and request[k] != request[0]:
+            prev_last = last_of[request[k - 1]]
+            preds[(k, s)].append(((prev_last, 3), 0.0))
+    succs = {op: [] for op in preds}
+    indeg = {op: len(p) for op, p in preds.items()}
+    for v, plist in preds.items():
+        for u, w in plist:
+            succs[u].append((v, w))
+    start = {op: 0.0 for op in preds}
+    end = {}
+    ready = [op for op, d in indeg.items() if d == 0]
+    while ready:
+        u = ready.pop()
+        end[u] = start[u] + tau[u[0]]
+        for v, w in succs[u]:
+            start[v] = max(start[v], end[u] + w)
+            indeg[v] -= 1
+            if indeg[v] == 0:
+                ready.append(v)
+    if len(end) != len(preds):
+        raise RuntimeError("schedule deadlocked")
     busy = [0.0, 0.0]
     for (k, s), e in end.items():
         busy[ranks[s]] += e - start[(k, s)]

@@ -168,29 +168,36 @@ def bf16_half_ulp(x) -> np.ndarray:
 
 
 def check_decode(fmt, kv_lens, heads, seed, sample=None, out_dtype=torch.bfloat16):
-    """Every output against the oracle: fp32 output within the bar; bf16 output within the bar plus what its
-    one rounding store may add (half a bf16 spacing, up to 0.0156 for |o| in [4, 8))."""
+    """Every output against the oracle.  The batch always runs with fp32 output, held to the plain bar.  A
+    bf16-output run must equal that fp32 output rounded once to bf16, bit for bit (the same value stored
+    twice), so its error beyond the store's own rounding is the fp32 output's; it is also reported against
+    the bar plus half a bf16 spacing (up to 0.0156 for |o| in [4, 8))."""
     pool, tables, q, seqs = build_batch(fmt, kv_lens, heads, seed)
     log(f"mla decode fmt={fmt} heads={heads} out={out_dtype} kv={list(kv_lens)[:12]} n={len(kv_lens)} seed={seed}")
-    out, lse = L.chunk_mla_decode(q.cuda(), pool, FMTS[fmt], tables, kv_lens, SCALE, return_lse=True,
-                                  out_dtype=out_dtype)
+    out32, lse32 = L.chunk_mla_decode(q.cuda(), pool, FMTS[fmt], tables, kv_lens, SCALE, return_lse=True,
+                                      out_dtype=torch.float32)
+    if out_dtype == torch.bfloat16:
+        out16, lse16 = L.chunk_mla_decode(q.cuda(), pool, FMTS[fmt], tables, kv_lens, SCALE, return_lse=True)
+        assert torch.equal(out32.to(torch.bfloat16).view(torch.int16), out16.view(torch.int16))
+        assert torch.equal(lse32, lse16)
+        out16 = out16.float().cpu().numpy().astype(np.float64)
     torch.cuda.synchronize()
-    out, lse = out.float().cpu().numpy().astype(np.float64), lse.cpu()
+    out, lse = out32.cpu().numpy().astype(np.float64), lse32.cpu()
     assert np.all(np.isfinite(out)), "non-finite GPU output"
     qb = bits(q)
     worst = worst_excess = worst_lse = 0.0
     for s in (range(len(kv_lens)) if sample is None else sample):
         ref, ref_lse = mla.decode(qb[s], mla.records(*seqs[s], fmt), SCALE)
-        err = np.abs(out[s] - ref)
-        # the pre-store value rounds to out within its own binade, which |ref| or |out| bounds from above
-        store = bf16_half_ulp(np.maximum(np.abs(ref), np.abs(out[s]))) if out_dtype == torch.bfloat16 else 0.0
-        worst = max(worst, float(err.max()))
-        worst_excess = max(worst_excess, float((err - store).max()))
+        worst = max(worst, float(np.abs(out[s] - ref).max()))
+        if out_dtype == torch.bfloat16:
+            err = np.abs(out16[s] - ref)
+            # the pre-store value rounds to out within its own binade, which |ref| or |out| bounds from above
+            store = bf16_half_ulp(np.maximum(np.abs(ref), np.abs(out16[s])))
+            worst_excess = max(worst_excess, float((err - store).max()))
         worst_lse = max(worst_lse, max_err(lse[:, s], ref_lse))
-    log(f"  max abs err {worst:.3e} (beyond the store's rounding {worst_excess:.3e})  lse {worst_lse:.3e}")
-    assert worst_excess <= BF16_TOL and worst_lse <= LSE_TOL
-    if out_dtype == torch.float32:
-        assert worst <= BF16_TOL
+    log(f"  fp32 output max abs err {worst:.3e}  bf16 output beyond its store's rounding {worst_excess:.3e}  "
+        f"lse {worst_lse:.3e}")
+    assert worst <= BF16_TOL and worst_excess <= BF16_TOL and worst_lse <= LSE_TOL
 
 
 @pytest.mark.parametrize("fmt", ["bf16", "fp8"])

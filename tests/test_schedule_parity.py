@@ -1,9 +1,13 @@
 """The library's schedule simulator (host code behind the C ABI) against the
 plain oracle (oracle/schedule.py), which shares no code with it.
 
-Both compute every stage time with the same additions and maxima, so the
-comparison is exact; busy times are sums taken in different orders and are
-compared to 1e-12 relative.  These are host-only calls: no GPU is involved.
+The two compute the timing differently: the library walks the ranks' op
+orders as an event loop, the oracle builds the precedence graph (rank order,
+stage hand-offs, request barriers) and takes longest paths in topological
+order.  Every stage time comes from the same additions (end + hand-off) and
+maxima either way, so the comparison is exact; busy times are sums taken in
+different orders and are compared to 1e-12 relative.  Host-only calls: no GPU
+is involved.
 """
 import math
 import random
