@@ -470,13 +470,14 @@ def mla_decode_summary(L, inputs, torch, timed, reps, warmup):
 def contiguous_cache_summary(L, loop, torch, timed, reps):
     """Chunks 3 and 7 read from a bf16 contiguous [tokens, kv_heads, d] cache holding the same logical K/V
     as the paged pool.  With workspace room the library re-lays the prefix for the paged kernel; that copy
-    is inside the timed call.  The paged pool's time for the same chunk is measured beside it."""
+    is inside the timed call.  With no workspace it reads the cache in place (the 8-wave kernel on
+    token-major tiles).  The paged pool's time for the same chunk is measured beside both."""
     w = loop.w
     last = w.n_chunks - 1
     ws = torch.empty(L.chunkattn_prefill_contiguous_workspace_size(last * w.chunk_len, w.chunk_len, w.heads,
                                                                    w.kv_heads, w.head_dim, w.head_dim_v, 0),
                      dtype=torch.uint8, device="cuda")
-    res = {"chunks": [], "ms": [], "tflops": [], "paged_ms": []}
+    res = {"chunks": [], "ms": [], "tflops": [], "in_place_ms": [], "in_place_tflops": [], "paged_ms": []}
     for c in (3, last):
         past = c * w.chunk_len
         kc, vc = loop.k_logical[: past + w.chunk_len], loop.v_logical[: past + w.chunk_len]
@@ -484,13 +485,20 @@ def contiguous_cache_summary(L, loop, torch, timed, reps):
         f()
         torch.cuda.synchronize()
         t = timed(f, reps)
+        g = lambda: L.chunk_prefill_attn(loop.q[c], kc, vc, past, w.scale, out=loop.out, relayout=False)
+        g()
+        torch.cuda.synchronize()
+        ti = timed(g, reps)
         tp = timed(lambda: loop.run_chunk(L, c), reps)
         res["chunks"].append(c)
         res["ms"].append(round(t, 3))
         res["tflops"].append(round(loop.flops[c] / (t / 1e3) / 1e12, 1))
+        res["in_place_ms"].append(round(ti, 3))
+        res["in_place_tflops"].append(round(loop.flops[c] / (ti / 1e3) / 1e12, 1))
         res["paged_ms"].append(round(tp, 3))
-    res["note"] = ("bf16 contiguous cache re-laid into the workspace (identity block table) and read by the paged "
-                   "kernel; the copy is timed")
+    res["note"] = ("ms: bf16 contiguous cache re-laid into the workspace (identity block table) and read by the "
+                   "paged kernel, the copy timed; in_place_ms: no workspace, the 8-wave kernel reads the cache in "
+                   "place (token-major tiles, V^T by transposing LDS reads)")
     return res
 
 
@@ -896,8 +904,8 @@ def main():
     dec_gbps = dec_only.decode_bytes / (dec_ms / 1e3) / 1e9
     log(f"decode-only {dec_ms:.3f} ms = {dec_gbps:.0f} GB/s; mixed prefill-only {pre_ms:.3f} ms")
     contig = contiguous_cache_summary(L, loop, torch, timed, args.reps)
-    log(f"contiguous cache, chunks {contig['chunks']}: {contig['ms']} ms ({contig['tflops']} TFLOP/s); "
-        f"paged pool {contig['paged_ms']} ms")
+    log(f"contiguous cache, chunks {contig['chunks']}: re-laid {contig['ms']} ms ({contig['tflops']} TFLOP/s), "
+        f"in place {contig['in_place_ms']} ms ({contig['in_place_tflops']} TFLOP/s); paged pool {contig['paged_ms']} ms")
     log("copy-bandwidth sanity figure")
     bw = copy_bandwidth(torch)
     log(f"1 GiB copy {bw['copy_gbps']} GB/s, read {bw['read_gbps']} GB/s")

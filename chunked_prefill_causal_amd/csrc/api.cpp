@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <mutex>
 #include <cstdarg>
@@ -317,7 +318,9 @@ ca_status chunk_prefill_attn(const void* q, const void* k, const void* v, int64_
   if (o.num_splits < 0) return fail(CA_EINVAL, "num_splits must be >= 0");
 
   const int group = heads / kv_heads;
-  // bf16 contiguous cache + room in the workspace: re-lay the prefix and run the paged kernel
+  // bf16 contiguous cache: with room in the workspace, re-lay the prefix and run the paged kernel (the
+  // fastest path); without it, d = d_v = 128 runs the same 8-wave kernel on the cache in place (its
+  // per-lane load offsets, up to 63 token strides, are 32-bit), other head dims the 4-wave kernel
   const bool paged_dims = din == DType::BF16 && prefill_paged_supported(head_dim, dv);
   Relayout rl;
   bool relay = false;
@@ -332,7 +335,9 @@ ca_status chunk_prefill_attn(const void* q, const void* k, const void* v, int64_
   // split partials follow the re-laid pools in the workspace
   void* const ws_split = relay ? (void*)((char*)o.workspace + rl.bytes) : o.workspace;
   const size_t ws_split_bytes = relay ? o.workspace_bytes - rl.bytes : o.workspace_bytes;
-  const bool use_paged_kernel = (paged || relay) && paged_dims;
+  const bool contig_native = !paged && !relay && prefill_contig_supported(din, head_dim, dv) &&
+                             std::max(ks_tok, vs_tok) * 2 * kBlock < ((int64_t)1 << 31);
+  const bool use_paged_kernel = (paged || relay || contig_native) && paged_dims;
   const int hpw = heads_per_wg(group, use_paged_kernel ? kWavesPaged : kWavesSmall);
   const int paged_rows = prefill_paged_rows(head_dim, dv);
   const int tok_wg = (use_paged_kernel ? paged_rows : 128) / hpw;
@@ -402,8 +407,9 @@ ca_status chunk_prefill_attn(const void* q, const void* k, const void* v, int64_
     a.block_table = table;
     a.num_blocks = (int)rl.blocks;
   }
-  hipError_t e = use_paged_kernel ? launch_prefill_paged(dout, head_dim, dv, a, (int)(base * splits), s)
-                                  : launch_prefill(din, dout, head_dim, dv, paged, a, (int)(base * splits), s);
+  hipError_t e = contig_native      ? launch_prefill_contig(dout, a, (int)(base * splits), s)
+                 : use_paged_kernel ? launch_prefill_paged(dout, head_dim, dv, a, (int)(base * splits), s)
+                                    : launch_prefill(din, dout, head_dim, dv, paged, a, (int)(base * splits), s);
   if (e != hipSuccess) return hip_status(e, "prefill launch");
   if (splits > 1) {
     e = launch_prefill_merge(dout, dv, a, s);

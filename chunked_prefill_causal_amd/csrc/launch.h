@@ -79,6 +79,10 @@ hipError_t launch_prefill(DType in, DType out, int D, int DV, bool paged, const 
 hipError_t launch_prefill_merge(DType out, int DV, const PrefillArgs& a, hipStream_t stream);
 // Paged bf16 path: 8-wave workgroups (256 query rows), direct-to-LDS tiles.
 bool prefill_paged_supported(int D, int DV);
+// The 8-wave kernel on a token-major contiguous bf16 cache (k/v strides in
+// PrefillArgs), read in place: d = d_v = 128.
+bool prefill_contig_supported(DType in, int D, int DV);
+hipError_t launch_prefill_contig(DType out, const PrefillArgs& a, int grid, hipStream_t stream);
 // Workgroups chunk_attn_varlen launches for one sequence's prefill-path rows
 // (0 for a sequence that takes the decode path); defined with the host API.
 int64_t varlen_prefill_workgroups(int q_len, int heads, int kv_heads);

@@ -78,6 +78,9 @@ struct PagedCfg {
   static_assert(VF <= KF, "PV operands interleave with QK operands");
 };
 
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16;
+
 __device__ __forceinline__ uint32_t lds_address(const void* p) {
   return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) void*)p);
 }
@@ -145,9 +148,10 @@ __device__ __forceinline__ int key_of_slot(int s) {
 // Key offset (before the lane group's 8g) of register r of QK block b.
 __host__ __device__ constexpr int key_of_reg(int b, int r) { return 32 * (b >> 1) + 4 * (b & 1) + r; }
 
-template <typename EO, int D, int DV, bool kVarlen>
+template <typename EO, int D, int DV, bool kVarlen, bool kContig = false>
 __global__ __launch_bounds__(512, 1) void prefill_paged_kernel(const PrefillArgs a) {
   using C = PagedCfg<D, DV>;
+  static_assert(!kContig || (D == 128 && DV == 128 && !kVarlen), "token-major tiles are laid out for d = 128");
   __shared__ __attribute__((aligned(16))) unsigned char smem[C::kStages * C::Stage];
 
   const int tid = threadIdx.x;
@@ -247,7 +251,13 @@ __global__ __launch_bounds__(512, 1) void prefill_paged_kernel(const PrefillArgs
   // fetches key key_of_slot(s) into slot s.  V keeps the pool's order.
   // Loop-local bases (this split's first block-table entry, this KV head's
   // first tile), so the key loop holds none of the argument block.
-  const __attribute__((address_space(4))) int32_t* bt4 = (const __attribute__((address_space(4))) int32_t*)(btab + j_lo);
+  const __attribute__((address_space(4))) int32_t* bt4 =
+      kContig ? nullptr : (const __attribute__((address_space(4))) int32_t*)(btab + j_lo);
+  // Tile handle: the block id of tile j_lo + idx (paged) or its index (contiguous cache).
+  auto tile_id = [&](int idx) -> int32_t {
+    if constexpr (kContig) return j_lo + idx;
+    else return bt4[idx];
+  };
   const unsigned char* kpool = (const unsigned char*)a.k + (int64_t)g * C::KBytes;
   const unsigned char* vpool = (const unsigned char*)a.v + (int64_t)g * C::VBytes;
   const int64_t kstride = (int64_t)a.kv_heads * C::KBytes, vstride = (int64_t)a.kv_heads * C::VBytes;
@@ -256,8 +266,45 @@ __global__ __launch_bounds__(512, 1) void prefill_paged_kernel(const PrefillArgs
   // i-th load adds i * kLoaders * 16 to the base).
   const uint32_t k_off_lane = wave * 64 * 16 + key_of_slot(lane) * 16;
   const uint32_t v_off_lane = (wave * 64 + lane) * 16;
+  // Contiguous cache ([tokens][kv_heads][128], token-major): the tiles are laid
+  // out token-major in LDS, one 256-byte row per key, its 16-byte units
+  // permuted per row so that operand reads meet no bank conflict.
+  //  * K: LDS row s holds key key_of_slot(s) (the order the S^T registers need);
+  //    unit u of row s holds feature run u ^ (s & 15).
+  //  * V: row = key; unit u of row key holds value run u ^ fv(key),
+  //    fv(key) = 2 (key & 3) + 8 ((key >> 3) & 1).
+  // Each direct load then moves whole 256-byte rows of four keys; a lane's
+  // load i of a tile reads K key kc_lane + kio(i), V key vkey_lane + 16 i, at
+  // fixed units.  Keys past the sequence end read its last row (finite,
+  // masked), so no slot past the cache is touched and nothing needs zeroing.
+  const unsigned char* kcont = (const unsigned char*)a.k + (int64_t)g * a.k_stride_head * 2;
+  const unsigned char* vcont = (const unsigned char*)a.v + (int64_t)g * a.v_stride_head * 2;
+  const uint32_t ktok = (uint32_t)(a.k_stride_tok * 2), vtok = (uint32_t)(a.v_stride_tok * 2);
+  const int mslot = 4 * (wave & 3) + (lane >> 4);
+  const int kc_lane = 8 * (mslot >> 2) + (mslot & 3);
+  const uint32_t krun_off = (uint32_t)(((lane & 15) ^ mslot) * 16);
+  const int vkey_lane = mslot;
+  const uint32_t vunit_off = (uint32_t)(((lane & 15) ^ (2 * ((lane >> 4) & 3) + 8 * ((vkey_lane >> 3) & 1))) * 16);
+  auto kio = [](int i) { return 32 * (i >> 1) + 4 * (i & 1); };
+  auto k_cont_off = [&](int i, int lim) { return (uint32_t)min(kc_lane + kio(i), lim) * ktok + krun_off; };
+  auto v_cont_off = [&](int i, int lim) { return (uint32_t)min(vkey_lane + 16 * i, lim) * vtok + vunit_off; };
   auto issue = [&](int32_t block_id, int st) {
     if (wave >= 4) return;
+    if constexpr (kContig) {
+      const int key0 = block_id * kBlock;
+      const int lim = min(kBlock - 1, kv_len32 - 1 - key0);
+      const unsigned char* kb = kcont + (int64_t)key0 * ktok;
+      const unsigned char* vb = vcont + (int64_t)key0 * vtok;
+      const uint32_t ks = smem_base + st * C::Stage;
+#pragma unroll
+      for (int i = 0; i < C::KPT; ++i)
+        load_to_lds16(kb, k_cont_off(i, lim), __builtin_amdgcn_readfirstlane(ks + (wave * 64 + i * C::kLoaders) * 16));
+#pragma unroll
+      for (int i = 0; i < C::VPT; ++i)
+        load_to_lds16(vb, v_cont_off(i, lim),
+                      __builtin_amdgcn_readfirstlane(ks + C::KBytes + (wave * 64 + i * C::kLoaders) * 16));
+      return;
+    }
     const int phys = clamp_block(block_id, a.num_blocks);
     const unsigned char* kb = kpool + phys * kstride;
     const unsigned char* vb = vpool + phys * vstride;
@@ -281,18 +328,34 @@ __global__ __launch_bounds__(512, 1) void prefill_paged_kernel(const PrefillArgs
   const unsigned char* pend_k = kpool;
   const unsigned char* pend_v = vpool;
   uint32_t pend_lds = 0;
+  int pend_lim = 0;                              // contiguous cache: last key of the pending tile
   auto prep = [&](int32_t block_id, int st) {
-    const int phys = clamp_block(block_id, a.num_blocks);
-    pend_k = kpool + phys * kstride;
-    pend_v = vpool + phys * vstride;
+    if constexpr (kContig) {
+      const int key0 = block_id * kBlock;
+      pend_lim = min(kBlock - 1, kv_len32 - 1 - key0);
+      pend_k = kcont + (int64_t)key0 * ktok;
+      pend_v = vcont + (int64_t)key0 * vtok;
+    } else {
+      const int phys = clamp_block(block_id, a.num_blocks);
+      pend_k = kpool + phys * kstride;
+      pend_v = vpool + phys * vstride;
+    }
     pend_lds = smem_base + st * C::Stage + wave * 64 * 16;
   };
   auto dma_one = [&](int j) {
-    if (j < C::KPT)
-      load_to_lds16(pend_k + j * C::kLoaders * 16, k_off_lane, __builtin_amdgcn_readfirstlane(pend_lds + j * C::kLoaders * 16));
-    else
-      load_to_lds16(pend_v + (j - C::KPT) * C::kLoaders * 16, v_off_lane,
-                    __builtin_amdgcn_readfirstlane(pend_lds + C::KBytes + (j - C::KPT) * C::kLoaders * 16));
+    if constexpr (kContig) {
+      if (j < C::KPT)
+        load_to_lds16(pend_k, k_cont_off(j, pend_lim), __builtin_amdgcn_readfirstlane(pend_lds + j * C::kLoaders * 16));
+      else
+        load_to_lds16(pend_v, v_cont_off(j - C::KPT, pend_lim),
+                      __builtin_amdgcn_readfirstlane(pend_lds + C::KBytes + (j - C::KPT) * C::kLoaders * 16));
+    } else {
+      if (j < C::KPT)
+        load_to_lds16(pend_k + j * C::kLoaders * 16, k_off_lane, __builtin_amdgcn_readfirstlane(pend_lds + j * C::kLoaders * 16));
+      else
+        load_to_lds16(pend_v + (j - C::KPT) * C::kLoaders * 16, v_off_lane,
+                      __builtin_amdgcn_readfirstlane(pend_lds + C::KBytes + (j - C::KPT) * C::kLoaders * 16));
+    }
   };
 
   f32x4_t o[C::NDB][2];
@@ -319,6 +382,34 @@ __global__ __launch_bounds__(512, 1) void prefill_paged_kernel(const PrefillArgs
   const int v_lane = C::KBytes + (lg * DV + lc) * 16;
   auto k_off = [](int q) { return (256 * (q >> 2) + 16 * (q & 3)) * 16; };            // QK operand q = 4 i + b
   auto v_off = [](int u) { return (4 * (u / C::NDB) * DV + 16 * (u % C::NDB)) * 16; };   // PV operand u = NDB ks + db
+  // Contiguous-cache tiles (token-major rows, see above): K operand (step i, block b)
+  // at row 16 b + lc, unit (4 i + lg) ^ lc; the V^T operand (step ks, block db) is
+  // two transposing reads: lane c of group lg at row 32 ks + 8 lg + c / 4 (then 4
+  // rows on), value run 2 db + (c % 4) / 2 (permuted), half c % 2.
+  int kq[4], vq[8];
+  if constexpr (kContig) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) kq[i] = lc * 256 + ((4 * i + lg) ^ lc) * 16;
+    const int fv = 2 * (lc >> 2) + 8 * (lg & 1);
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+      vq[db] = C::KBytes + (8 * lg + (lc >> 2)) * 256 + ((2 * db + ((lc & 3) >> 1)) ^ fv) * 16 + (lc & 1) * 8;
+  }
+  auto k_read = [&](const unsigned char* stage, int q) -> u32x4_t {
+    if constexpr (kContig) return *(const u32x4_t*)(stage + kq[q >> 2] + 4096 * (q & 3));
+    else return *(const u32x4_t*)(stage + k_lane + k_off(q));
+  };
+  auto v_read = [&](const unsigned char* stage, int u) -> u32x4_t {
+    if constexpr (kContig) {
+      const unsigned char* pp = stage + vq[u % C::NDB] + 32 * 256 * (u / C::NDB);
+      const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)pp);
+      const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(pp + 4 * 256));
+      const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo), h2 = __builtin_bit_cast(u32x2_t, hi);
+      return u32x4_t{l2[0], l2[1], h2[0], h2[1]};
+    } else {
+      return *(const u32x4_t*)(stage + v_lane + v_off(u));
+    }
+  };
   auto qk_mfma = [&](int q, u32x4_t kf, f32x4_t (&n)[4][2]) {
     n[q & 3][0] = mfma16(kf, qreg[0][q >> 2], n[q & 3][0]);
     n[q & 3][1] = mfma16(kf, qreg[1][q >> 2], n[q & 3][1]);
@@ -331,12 +422,12 @@ __global__ __launch_bounds__(512, 1) void prefill_paged_kernel(const PrefillArgs
 
   // S^T = K Q^T for one 64-key tile.
   auto qk = [&](int st) {
-    const unsigned char* kb = stage_ptr(st) + k_lane;
+    const unsigned char* stg = stage_ptr(st);
     f32x4_t n[4][2];
 #pragma unroll
     for (int b = 0; b < 4; ++b) n[b][0] = n[b][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int q = 0; q < C::KF; ++q) qk_mfma(q, *(const u32x4_t*)(kb + k_off(q)), n);
+    for (int q = 0; q < C::KF; ++q) qk_mfma(q, k_read(stg, q), n);
 #pragma unroll
     for (int b = 0; b < 4; ++b) s[b][0] = n[b][0], s[b][1] = n[b][1];
   };
@@ -438,9 +529,9 @@ __global__ __launch_bounds__(512, 1) void prefill_paged_kernel(const PrefillArgs
 
   // O^T += V^T P^T for one tile.
   auto pv = [&](int st) {
-    const unsigned char* vb = stage_ptr(st) + v_lane;
+    const unsigned char* stg = stage_ptr(st);
 #pragma unroll
-    for (int u = 0; u < C::VF; ++u) pv_mfma(u, *(const u32x4_t*)(vb + v_off(u)));
+    for (int u = 0; u < C::VF; ++u) pv_mfma(u, v_read(stg, u));
   };
 
   // Operand order of the combined matrix phase: PV and QK operands alternate
@@ -453,15 +544,15 @@ __global__ __launch_bounds__(512, 1) void prefill_paged_kernel(const PrefillArgs
 
   // PV of the previous tile and QK of the current one (trailing waves).
   auto pv_qk = [&](int st_prev, int st_cur) {
-    const unsigned char* vb = stage_ptr(st_prev) + v_lane;
-    const unsigned char* kb = stage_ptr(st_cur) + k_lane;
+    const unsigned char* vs = stage_ptr(st_prev);
+    const unsigned char* kst = stage_ptr(st_cur);
     f32x4_t n[4][2];
 #pragma unroll
     for (int b = 0; b < 4; ++b) n[b][0] = n[b][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int k = 0; k < kOps; ++k) {
-      if (is_pv(k)) pv_mfma(k >> 1, *(const u32x4_t*)(vb + v_off(k >> 1)));
-      else qk_mfma(qk_index(k), *(const u32x4_t*)(kb + k_off(qk_index(k))), n);
+      if (is_pv(k)) pv_mfma(k >> 1, v_read(vs, k >> 1));
+      else qk_mfma(qk_index(k), k_read(kst, qk_index(k)), n);
     }
 #pragma unroll
     for (int b = 0; b < 4; ++b) s[b][0] = n[b][0], s[b][1] = n[b][1];
@@ -482,24 +573,24 @@ __global__ __launch_bounds__(512, 1) void prefill_paged_kernel(const PrefillArgs
   // load goes out after every fourth operand (eighth MFMA), fenced so the
   // order stays as written.
   auto pv_qk_dma = [&](int st_prev, int st_cur, bool with_dma) {
-    const unsigned char* vb = stage_ptr(st_prev) + v_lane;
-    const unsigned char* kb = stage_ptr(st_cur) + k_lane;
+    const unsigned char* vs = stage_ptr(st_prev);
+    const unsigned char* kst = stage_ptr(st_cur);
     constexpr int kAhead = 8;
-    auto op_ptr = [&](int k) -> const u32x4_t* {
-      if (is_pv(k)) return (const u32x4_t*)(vb + v_off(k >> 1));
-      return (const u32x4_t*)(kb + k_off(qk_index(k)));
+    auto op_read = [&](int k) -> u32x4_t {
+      if (is_pv(k)) return v_read(vs, k >> 1);
+      return k_read(kst, qk_index(k));
     };
     f32x4_t n[4][2];
 #pragma unroll
     for (int b = 0; b < 4; ++b) n[b][0] = n[b][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     u32x4_t rd[kOps];
 #pragma unroll
-    for (int k = 0; k < kAhead; ++k) rd[k] = *op_ptr(k);
+    for (int k = 0; k < kAhead; ++k) rd[k] = op_read(k);
 #pragma unroll
     for (int k = 0; k < kOps; ++k) {
       if (is_pv(k)) pv_mfma(k >> 1, rd[k]);
       else qk_mfma(qk_index(k), rd[k], n);
-      if (k + kAhead < kOps) rd[k + kAhead] = *op_ptr(k + kAhead);
+      if (k + kAhead < kOps) rd[k + kAhead] = op_read(k + kAhead);
       if ((k & 3) == 3 && (k >> 2) < C::LPT) {
         __builtin_amdgcn_sched_barrier(0);
         if (with_dma) dma_one(k >> 2);
@@ -524,8 +615,8 @@ __global__ __launch_bounds__(512, 1) void prefill_paged_kernel(const PrefillArgs
   const int n = j_hi - j_lo;
 #pragma unroll
   for (int p = 0; p < NS - 2; ++p)
-    if (p < n) issue(bt4[p], p);
-  int32_t block_ahead = (NS - 2 < n) ? bt4[NS - 2] : 0;
+    if (p < n) issue(tile_id(p), p);
+  int32_t block_ahead = (NS - 2 < n) ? tile_id(NS - 2) : 0;
   // Start of interval i: tile i must have landed (tiles i+1 .. i+NS-3 may
   // still be in flight); after the barrier the stage of tile i-2 is free and
   // receives tile i+NS-2.
@@ -541,9 +632,9 @@ __global__ __launch_bounds__(512, 1) void prefill_paged_kernel(const PrefillArgs
       if (i == 0) issue(block_ahead, NS - 2);          // no matrix phase to hide it in
       else if (wave < 4) prep(block_ahead, (i + NS - 2) % NS);   // issued inside pv_qk_dma
     }
-    block_ahead = (i + NS - 1 < n) ? bt4[i + NS - 1] : 0;
+    block_ahead = (i + NS - 1 < n) ? tile_id(i + NS - 1) : 0;
     const int key0 = (j_lo + i) * kBlock;
-    if (i < n && key0 + kBlock > kv_len32) {
+    if (!kContig && i < n && key0 + kBlock > kv_len32) {
       // The tile holding the sequence end: zero its values of keys >= kv_len
       // in LDS (a masked key has probability 0, but 0 * NaN would poison the
       // sum).  Nobody reads this V before the next barrier.
@@ -651,6 +742,16 @@ static hipError_t launch_paged_dims(int D, int DV, const PrefillArgs& a, int gri
 hipError_t launch_prefill_paged(DType out, int D, int DV, const PrefillArgs& a, int grid, hipStream_t stream) {
   if (out == DType::BF16) return launch_paged_dims<uint16_t, false>(D, DV, a, grid, stream);
   return launch_paged_dims<float, false>(D, DV, a, grid, stream);
+}
+
+bool prefill_contig_supported(DType in, int D, int DV) { return in == DType::BF16 && D == 128 && DV == 128; }
+
+hipError_t launch_prefill_contig(DType out, const PrefillArgs& a, int grid, hipStream_t stream) {
+  if (out == DType::BF16)
+    hipLaunchKernelGGL((prefill_paged_kernel<uint16_t, 128, 128, false, true>), dim3(grid), dim3(512), 0, stream, a);
+  else
+    hipLaunchKernelGGL((prefill_paged_kernel<float, 128, 128, false, true>), dim3(grid), dim3(512), 0, stream, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_prefill_paged_varlen(DType out, int D, int DV, const PrefillArgs& a, int grid, hipStream_t stream) {

@@ -136,9 +136,13 @@ void ca_prefill_opts_init(ca_prefill_opts* opts);
  * chunkattn_prefill_contiguous_workspace_size, the prefix [0, past_len +
  * chunk_len) of K and V is first copied into the paged tile layout inside the
  * workspace (an identity block table), and the paged kernel runs on that copy:
- * its output is then bitwise that of the paged layout.  Without that room the
- * contiguous kernel reads the cache in place (same result within bf16
- * rounding, ~3x slower at 128K).  Split-KV partials, if any, follow the copy.
+ * its output is then bitwise that of the paged layout.  Without that room
+ * (no workspace, or split partials only) the cache is read in place: at
+ * (head_dim, head_dim_v) = (128, 128) by the same 8-wave kernel, laying each
+ * tile out token-major in LDS (bitwise the paged result; ~9% slower, as V^T
+ * then takes two transposing LDS reads per operand), at the other pairs by
+ * the 4-wave contiguous kernel (same result within bf16 rounding, ~3x
+ * slower at 128K).  Split-KV partials, if any, follow the copy.
  */
 ca_status chunk_prefill_attn(const void* q_chunk, const void* k_cache, const void* v_cache,
                              int64_t past_len, int64_t chunk_len,

@@ -219,20 +219,25 @@ def _paged_run(q, pool, table, past, d, **kw):
                                 block_table=table, **kw)
 
 
-def test_paged_matches_contiguous():
-    """A bf16 contiguous cache re-laid into the workspace runs the paged kernel: bitwise the paged
-    result.  Read in place (no room to re-lay), the contiguous kernel (32x32x16 MFMAs) sums in a
-    different fp32 order from the paged one (16x16x32), so bf16 outputs may differ where a value sits
-    at a rounding edge: by at most 2 units in the last place (unit 2^-7 relative), on few elements."""
-    c, past, hq, hkv, d = 160, 390, 16, 4, 128
+@pytest.mark.parametrize("d", [128, 64])
+def test_paged_matches_contiguous(d):
+    """A bf16 contiguous cache re-laid into the workspace runs the paged kernel: bitwise the paged result.
+    Read in place (no room to re-lay), d = 128 runs the same 8-wave kernel on the cache (bitwise the paged
+    result too); d = 64 runs the contiguous kernel (32x32x16 MFMAs), which sums in a different fp32 order
+    from the paged one (16x16x32), so bf16 outputs may differ where a value sits at a rounding edge: by at
+    most 2 units in the last place (unit 2^-7 relative), on few elements."""
+    c, past, hq, hkv = 160, 390, 16, 4
     k, v = seq_kv(past + c, hkv, d, d, "bf16", 101)
     q = inputs.normal((c, hq, d), 102, "bf16").cuda()
     pool, table = single_seq_pool(k, v, 103)
     a = _paged_run(q, pool, table, past, d, num_splits=1)
     r = L.chunk_prefill_attn(q, k.cuda(), v.cuda(), past, 1 / math.sqrt(d), num_splits=1)
     assert torch.equal(a.view(torch.int16), r.view(torch.int16))
-    a = a.float()
-    b = L.chunk_prefill_attn(q, k.cuda(), v.cuda(), past, 1 / math.sqrt(d), num_splits=1, relayout=False).float()
+    b = L.chunk_prefill_attn(q, k.cuda(), v.cuda(), past, 1 / math.sqrt(d), num_splits=1, relayout=False)
+    if d == 128:
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+        return
+    a, b = a.float(), b.float()
     diff = (a - b).abs()
     ulp = torch.exp2(torch.floor(torch.log2(torch.maximum(a.abs(), b.abs()).clamp_min(2.0 ** -126))) - 7)
     same = (diff == 0).float().mean().item()
@@ -424,3 +429,30 @@ def test_contiguous_split_workspace_larger_than_relayout_runs_in_place():
     e = max_err(got, ref)
     log(f"split-only workspace {need} B (re-layout {relay} B), 2 splits in place: max err {e:.3e}")
     assert e <= BF16_TOL
+
+
+@pytest.mark.parametrize("splits", [1, 3])
+def test_contiguous_d128_in_place_equals_paged_bitwise(splits):
+    """With no room to re-lay (no workspace, or split partials only), the 8-wave kernel reads a bf16
+    contiguous cache at d = d_v = 128 in place (token-major tiles in LDS, transposing reads for V^T).  It
+    computes every product in the paged kernel's order, so its output equals the paged pool's bit for bit;
+    the chunk ends mid-tile and the cache holds NaN past kv_len, which must stay unread."""
+    c, past, hq, hkv, d = 300, 1000, 32, 8, 128
+    n = past + c
+    k, v = seq_kv(n, hkv, d, d, "bf16", 171)
+    q = inputs.normal((c, hq, d), 172, "bf16")
+    scale = 1 / math.sqrt(d)
+    cap = n + 100
+    kc = torch.full((cap, hkv, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    vc = torch.full((cap, hkv, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    kc[:n] = k.cuda()
+    vc[:n] = v.cuda()
+    log(f"contiguous d128 in place, {splits} split(s)")
+    out, lse = L.chunk_prefill_attn(q.cuda(), kc, vc, past, scale, return_lse=True, num_splits=splits,
+                                    kv_capacity=cap, relayout=False)
+    pool, table = single_seq_pool(k, v, 173)
+    paged, paged_lse = _paged_run(q.cuda(), pool, table, past, d, num_splits=splits, return_lse=True)
+    assert torch.equal(out.view(torch.int16), paged.view(torch.int16))
+    assert torch.equal(lse, paged_lse)
+    ref, ref_lse = oracle_chunk(q, k, v, past, scale)
+    assert max_err(out, ref) <= BF16_TOL and max_err(lse, ref_lse) <= LSE_TOL
