@@ -202,7 +202,7 @@ __global__ __launch_bounds__(256, 1) void mla_prefill_kernel(const MlaPrefillArg
     f32x4_t s[4][2];
     {
       const unsigned char* kbase = stage + k_lane;
-      constexpr int kOps = 4 * kQS, kAhead = 8;
+      constexpr int kOps = 4 * kQS, kAhead = 4;
       auto k_ptr = [&](int k) { return (const u32x4_t*)(kbase + (256 * (k >> 2) + 16 * (k & 3)) * 16); };
       u32x4_t rd[kOps];
 #pragma unroll
@@ -313,7 +313,7 @@ __global__ __launch_bounds__(256, 1) void mla_prefill_kernel(const MlaPrefillArg
     // ---- O^T += V^T P^T ----
     {
       const unsigned char* vbase = stage + v_lane;
-      constexpr int kOps = 2 * kNDB, kAhead = 6;
+      constexpr int kOps = 2 * kNDB, kAhead = 4;
       auto v_read = [&](int k) -> u32x4_t {       // op k: 32-key step k / kNDB, value block k % kNDB
         const unsigned char* pp = vbase + (k / kNDB) * 32 * 16 + (k % kNDB) * 2048;
         const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)pp);
