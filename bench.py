@@ -44,8 +44,8 @@ PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 matrix peak: 256 CUs x 4096 flop
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 METRIC = "causal-effective attn TFLOP/s & per-chunk latency vs chunk index (1 MI355X)"
 DOMINANT = "prefill_paged_kernel<bf16 out, d 128, d_v 128> (chunk loop launches)"
-DOMINANT_NAMES = ("prefill_paged_kernel<unsigned short, 128, 128, false>",   # rocprofv3, demangled
-                  "prefill_paged_kernelItLi128ELi128ELb0E")                # mangled
+DOMINANT_NAMES = ("prefill_paged_kernel<unsigned short, 128, 128, false, false>",   # rocprofv3, demangled
+                  "prefill_paged_kernelItLi128ELi128ELb0ELb0E")              # mangled
 KERNEL_SOURCES = ["chunked_prefill_causal_amd/csrc/prefill_paged.hip",
                   "chunked_prefill_causal_amd/csrc/device_common.h", "chunked_prefill_causal_amd/csrc/launch.h"]
 TRAFFIC_SUMMARY = "profiles/prefill_paged_gqa128k_traffic.md"
@@ -78,6 +78,9 @@ def parse():
     p.add_argument("--mla-only", action="store_true",
                    help="time only the MLA latent decode batches and prompt (prints their JSON object)")
     p.add_argument("--chunk-reps", type=int, default=20, help="repetitions per chunk for the latency distribution")
+    p.add_argument("--summarize-mla-profile", nargs=2, metavar="DIR",
+                   help="TRACE_DIR MFMA_DIR: summarize rocprofv3 output of --mla-only for the latent prefill "
+                        "kernel (no GPU needed)")
     p.add_argument("--summarize-profile", nargs="+", metavar="DIR",
                    help="TRACE_DIR FETCH_DIR WRITE_DIR [MFMA_DIR]: write the profile summary from rocprofv3 "
                         "output of this script (no GPU needed)")
@@ -161,18 +164,27 @@ def summarize_profile(trace_dir, fetch_dir, write_dir, mfma_dir=None):
         short = re.sub(r"\(.*", "", r["Name"]).replace("void ", "")
         lines.append(f"| `{short}` | {r['Calls']} | {float(r['AverageNs']) / 1e6:.4f} | "
                      f"{float(r['MinNs']) / 1e6:.4f} | {float(r['MaxNs']) / 1e6:.4f} |")
-    durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e6 for r in trace
+    durs = [(int(r["Dispatch_Id"]), (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e6) for r in trace
             if any(n in r["Kernel_Name"] for n in DOMINANT_NAMES)]
+    durs = [t for _, t in sorted(durs)]
+    # the trace run is the default command: 2 warmup steps, then the 5 timed steps' chunk loops (8 launches each)
+    timed = durs[2 * 8: 7 * 8]
     lines += ["", f"Dominant kernel `{DOMINANT}`: {len(durs)} dispatches in the trace, average "
-              f"{sum(durs) / len(durs):.4f} ms."]
+              f"{sum(durs) / len(durs):.4f} ms over all of them; the {len(timed)} launches of the 5 timed steps "
+              f"(after the 2 warmup steps) average {sum(timed) / len(timed):.4f} ms."]
     out = {"kernel_sha256": kernel_source_hash()}
     for counter, directory in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         vals, names, _ = _counter_per_dispatch(directory, counter)
-        calib = [d for d in vals if "copyBuffer" in names[d] or "copy" in names[d].lower()]
+        # the runtime's device-to-device copy (16-byte lanes, like every kernel here); torch's elementwise
+        # copy kernels count differently per byte and are not used
+        calib = [d for d in vals if "copyBuffer" in names[d]]
+        if not calib:
+            raise SystemExit(f"{directory}: no __amd_rocclr_copyBuffer dispatch (run with --copy-calibration)")
         cal = max(calib, key=lambda d: vals[d])
         factor = CALIB_BYTES / (vals[cal] * 1024)
-        # the counter passes run one step without warmup: its chunk loop is the first 8 launches
-        dom = sorted(d for d in vals if any(n in names[d] for n in DOMINANT_NAMES))[:8]
+        # the counter passes run one warmup step and one timed step: the timed chunk loop is launches 9-16
+        # (the first loop of a process runs its first chunks several times slower)
+        dom = sorted(d for d in vals if any(n in names[d] for n in DOMINANT_NAMES))[8:16]
         per = [vals[d] * 1024 * factor for d in dom]
         out[counter] = {"calibration_kib": vals[cal], "factor": round(factor, 4), "dispatches": len(dom),
                         "bytes_per_launch": sum(per) / len(per), "bytes_by_chunk": [round(x) for x in per]}
@@ -222,7 +234,7 @@ def mfma_counter_summary(mfma_dir):
     dur = {}
     for r in _csv_rows(mfma_dir, "counter_collection.csv"):
         dur[int(r["Dispatch_Id"])] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
-    dom = sorted(d for d in mops if any(n in names[d] for n in DOMINANT_NAMES))[:8]
+    dom = sorted(d for d in mops if any(n in names[d] for n in DOMINANT_NAMES))[8:16]
     w = inputs.WORKLOADS["gqa_128k"]
     simds, clock = 1024, 2.4e9
     lines = ["", "Chunk-loop launches, one pass of SQ_INSTS_VALU_MFMA_MOPS_BF16 and SQ_VALU_MFMA_BUSY_CYCLES. Executed "
@@ -238,6 +250,58 @@ def mfma_counter_summary(mfma_dir):
         lines.append(f"| {k} | {ex / 1e12:.2f} | {eff / 1e12:.2f} | {ex / eff:.3f} | {dur[d] * 1e3:.3f} | "
                      f"{per_simd / 1e6:.2f} | {100 * per_simd / (dur[d] * clock):.1f} |")
     return lines
+
+
+def summarize_mla_prefill_profile(trace_dir, mfma_dir):
+    """Markdown summary of `--mla-only` under a kernel trace and under one matrix-counter pass: the latent
+    prefill kernel per cache format and chunk.  Each format runs every chunk once warm, then `reps` times
+    timed (bf16 first, then fp8), so a format's launches are its first 16 plus 16 x reps."""
+    sys.path.insert(0, ROOT)
+    from chunked_prefill_causal_amd import inputs
+
+    w = inputs.WORKLOADS["mla_prefill"]
+    n = w.n_chunks
+    eff = [w.heads * causal_pairs(k * w.chunk_len, w.chunk_len) * 2 * (w.head_dim + w.head_dim_v)
+           for k in range(n)]
+
+    def split(ds):
+        ds = sorted(ds)
+        half = len(ds) // 2
+        return {"bf16": ds[n:half], "fp8": ds[half + n:]}     # the timed launches of each format
+
+    trace = {int(r["Dispatch_Id"]): (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e6
+             for r in _csv_rows(trace_dir, "kernel_trace.csv") if "mla_prefill_kernel" in r["Kernel_Name"]}
+    deq = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e6
+           for r in _csv_rows(trace_dir, "kernel_trace.csv") if "mla_dequant_kernel" in r["Kernel_Name"]]
+    mops, _, _ = _counter_per_dispatch(mfma_dir, "SQ_INSTS_VALU_MFMA_MOPS_BF16")
+    busy, names, _ = _counter_per_dispatch(mfma_dir, "SQ_VALU_MFMA_BUSY_CYCLES")
+    dur = {int(r["Dispatch_Id"]): (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+           for r in _csv_rows(mfma_dir, "counter_collection.csv")}
+    mla = split(d for d in mops if "mla_prefill_kernel" in names[d])
+    tr = split(trace)
+    lines = ["## Kernel trace", "",
+             f"`mla_prefill_kernel` launches in the trace: {len(trace)}; the widening pass `mla_dequant_kernel` "
+             f"(fp8 cache): {len(deq)} launches, average {sum(deq) / max(1, len(deq)):.4f} ms.", "",
+             "| Cache | Timed launches | Chunk-loop sum of per-chunk means (ms) | Average launch (ms) | "
+             "Causal-effective TFLOP/s | of 2516.6 |", "|---|---|---|---|---|---|"]
+    for fmt, ds in tr.items():
+        per = [sum(trace[d] for d in ds[k::n]) / len(ds[k::n]) for k in range(n)]
+        tf = sum(eff) / (sum(per) / 1e3) / 1e12
+        lines.append(f"| {fmt} | {len(ds)} | {sum(per):.3f} | {sum(per) / n:.4f} | {tf:.1f} | "
+                     f"{100 * tf / PEAK_BF16_TFLOPS:.1f} % |")
+    lines += ["", "## Matrix-core counters (SQ_INSTS_VALU_MFMA_MOPS_BF16, SQ_VALU_MFMA_BUSY_CYCLES)", "",
+              "Timed launch of each chunk.  Executed flops = MOPS x 512; busy % = matrix-pipe busy cycles per "
+              "SIMD (1024 SIMDs) / (launch duration under counting x 2.4 GHz).", "",
+              "| Chunk | Executed TFLOP | Causal-effective TFLOP | Executed / effective | bf16 cache: ms, busy % | "
+              "fp8 cache: ms, busy % |", "|---|---|---|---|---|---|"]
+    for k in range(n):
+        cells = []
+        for fmt in ("bf16", "fp8"):
+            d = mla[fmt][k]
+            cells.append(f"{dur[d] * 1e3:.3f}, {100 * busy[d] / 1024 / (dur[d] * 2.4e9):.1f}")
+        ex = mops[mla["bf16"][k]] * 512
+        lines.append(f"| {k} | {ex / 1e12:.3f} | {eff[k] / 1e12:.3f} | {ex / eff[k]:.3f} | {cells[0]} | {cells[1]} |")
+    return "\n".join(lines) + "\n"
 
 
 class PrefillLoop:
@@ -809,6 +873,9 @@ def cpu_baseline(args, loop, torch):
 
 def main():
     args = parse()
+    if args.summarize_mla_profile:
+        sys.stdout.write(summarize_mla_prefill_profile(*args.summarize_mla_profile))
+        return
     if args.summarize_profile:
         if len(args.summarize_profile) not in (3, 4):
             sys.exit("--summarize-profile takes TRACE_DIR FETCH_DIR WRITE_DIR [MFMA_DIR]")
