@@ -562,7 +562,7 @@ def contiguous_cache_summary(L, loop, torch, timed, reps):
         res["paged_ms"].append(round(tp, 3))
     res["note"] = ("ms: bf16 contiguous cache re-laid into the workspace (identity block table) and read by the "
                    "paged kernel, the copy timed; in_place_ms: no workspace, the 8-wave kernel reads the cache in "
-                   "place (token-major tiles, V^T by transposing LDS reads)")
+                   "place (token-major tiles, V transposed once per workgroup in LDS)")
     return res
 
 

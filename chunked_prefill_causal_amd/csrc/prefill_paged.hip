@@ -152,7 +152,17 @@ template <typename EO, int D, int DV, bool kVarlen, bool kContig = false>
 __global__ __launch_bounds__(512, 1) void prefill_paged_kernel(const PrefillArgs a) {
   using C = PagedCfg<D, DV>;
   static_assert(!kContig || (D == 128 && DV == 128 && !kVarlen), "token-major tiles are laid out for d = 128");
-  __shared__ __attribute__((aligned(16))) unsigned char smem[C::kStages * C::Stage];
+  // Raw tile stages, and the intervals a tile's stage is read in: two on the
+  // paged pool (K by QK(t), V by PV(t) one interval later); one on a
+  // contiguous cache, whose V tile is transposed into one of two V^T buffers
+  // in its own interval and read by PV from there.
+  constexpr int NS = kContig ? 3 : C::kStages;
+  constexpr int kReads = kContig ? 1 : 2;
+  constexpr int NA = NS - kReads;                // tiles in flight ahead of the current one
+  static_assert(NA == 1 || NA == 2, "at most one tile in flight past the one awaited");
+  constexpr int kSmem = NS * C::Stage + (kContig ? 2 * C::VBytes : 0);
+  static_assert(kSmem <= 131072, "LDS budget");
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kSmem];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -375,41 +385,70 @@ __global__ __launch_bounds__(512, 1) void prefill_paged_kernel(const PrefillArgs
   for (int qb = 0; qb < 2; ++qb) pkv[qb][0] = pkv[qb][1] = u32x4_t{0u, 0u, 0u, 0u};
 
   auto stage_ptr = [&](int st) { return smem + st * C::Stage; };
+  // Where PV reads the V operands of tile i: the stage's V part (paged pool)
+  // or V^T buffer i & 1 (contiguous cache); both hold the pool's V block order.
+  auto v_base = [&](int i) -> const unsigned char* {
+    if constexpr (kContig) return smem + NS * C::Stage + (i & 1) * C::VBytes;
+    else return stage_ptr(i % NS) + C::KBytes;
+  };
 
   // Operand offsets: K operand (key block b, feature step i) at k_lane + (256 i + 16 b) * 16,
   // V operand (key step ks, value block db) at v_lane + (4 ks DV + 16 db) * 16.
   const int k_lane = (lg * kBlock + lc) * 16;
-  const int v_lane = C::KBytes + (lg * DV + lc) * 16;
+  const int v_lane = (lg * DV + lc) * 16;
   auto k_off = [](int q) { return (256 * (q >> 2) + 16 * (q & 3)) * 16; };            // QK operand q = 4 i + b
   auto v_off = [](int u) { return (4 * (u / C::NDB) * DV + 16 * (u % C::NDB)) * 16; };   // PV operand u = NDB ks + db
   // Contiguous-cache tiles (token-major rows, see above): K operand (step i, block b)
-  // at row 16 b + lc, unit (4 i + lg) ^ lc; the V^T operand (step ks, block db) is
-  // two transposing reads: lane c of group lg at row 32 ks + 8 lg + c / 4 (then 4
-  // rows on), value run 2 db + (c % 4) / 2 (permuted), half c % 2.
-  int kq[4], vq[8];
+  // at row 16 b + lc, unit (4 i + lg) ^ lc; the V^T operand (step ks, block db) of
+  // the raw V tile is two transposing reads: lane c of group lg at row
+  // 32 ks + 8 lg + c / 4 (then 4 rows on), value run 2 db + (c % 4) / 2
+  // (permuted), half c % 2.
+  // This wave transposes V^T operands u = 2 wave and 2 wave + 1 (step u / 8, block u % 8).
+  int kq[4], vq[2];
   if constexpr (kContig) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) kq[i] = lc * 256 + ((4 * i + lg) ^ lc) * 16;
     const int fv = 2 * (lc >> 2) + 8 * (lg & 1);
 #pragma unroll
-    for (int db = 0; db < 8; ++db)
-      vq[db] = C::KBytes + (8 * lg + (lc >> 2)) * 256 + ((2 * db + ((lc & 3) >> 1)) ^ fv) * 16 + (lc & 1) * 8;
+    for (int e = 0; e < 2; ++e) {
+      const int u = 2 * wave + e, ks = u / C::NDB, db = u % C::NDB;
+      vq[e] = (32 * ks + 8 * lg + (lc >> 2)) * 256 + ((2 * db + ((lc & 3) >> 1)) ^ fv) * 16 + (lc & 1) * 8;
+    }
   }
   auto k_read = [&](const unsigned char* stage, int q) -> u32x4_t {
     if constexpr (kContig) return *(const u32x4_t*)(stage + kq[q >> 2] + 4096 * (q & 3));
     else return *(const u32x4_t*)(stage + k_lane + k_off(q));
   };
-  auto v_read = [&](const unsigned char* stage, int u) -> u32x4_t {
+  auto v_read = [&](const unsigned char* vb, int u) -> u32x4_t {
+    return *(const u32x4_t*)(vb + v_lane + v_off(u));
+  };
+  // Contiguous cache: this wave's two V^T operands (u = 2 wave, 2 wave + 1) of
+  // tile i, read from the raw token-major tile and written to V^T buffer i & 1
+  // at the place PV reads them, so the eight waves transpose the tile once.
+  // All four transposing reads go out before the first write waits on them.
+  auto vt_fill = [&](int i) {
     if constexpr (kContig) {
-      const unsigned char* pp = stage + vq[u % C::NDB] + 32 * 256 * (u / C::NDB);
-      const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)pp);
-      const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(pp + 4 * 256));
-      const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo), h2 = __builtin_bit_cast(u32x2_t, hi);
-      return u32x4_t{l2[0], l2[1], h2[0], h2[1]};
-    } else {
-      return *(const u32x4_t*)(stage + v_lane + v_off(u));
+      const unsigned char* raw = stage_ptr(i % NS) + C::KBytes;
+      unsigned char* dst = smem + NS * C::Stage + (i & 1) * C::VBytes + v_lane;
+      v4i16_t lo[2], hi[2];
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const unsigned char* pp = raw + vq[e];
+        lo[e] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)pp);
+        hi[e] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(pp + 4 * 256));
+      }
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo[e]), h2 = __builtin_bit_cast(u32x2_t, hi[e]);
+        *(u32x4_t*)(dst + v_off(2 * wave + e)) = u32x4_t{l2[0], l2[1], h2[0], h2[1]};
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);   // the four LDS reads, then
+      __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);   // the two LDS writes
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
+  static_assert(!kContig || 2 * 8 == C::VF, "two V^T operands per wave cover the tile");
   auto qk_mfma = [&](int q, u32x4_t kf, f32x4_t (&n)[4][2]) {
     n[q & 3][0] = mfma16(kf, qreg[0][q >> 2], n[q & 3][0]);
     n[q & 3][1] = mfma16(kf, qreg[1][q >> 2], n[q & 3][1]);
@@ -528,10 +567,10 @@ __global__ __launch_bounds__(512, 1) void prefill_paged_kernel(const PrefillArgs
   };
 
   // O^T += V^T P^T for one tile.
-  auto pv = [&](int st) {
-    const unsigned char* stg = stage_ptr(st);
+  auto pv = [&](int i) {
+    const unsigned char* vb = v_base(i);
 #pragma unroll
-    for (int u = 0; u < C::VF; ++u) pv_mfma(u, v_read(stg, u));
+    for (int u = 0; u < C::VF; ++u) pv_mfma(u, v_read(vb, u));
   };
 
   // Operand order of the combined matrix phase: PV and QK operands alternate
@@ -543,9 +582,9 @@ __global__ __launch_bounds__(512, 1) void prefill_paged_kernel(const PrefillArgs
   auto qk_index = [](int k) { return k < 2 * C::VF ? (k >> 1) : k - C::VF; };
 
   // PV of the previous tile and QK of the current one (trailing waves).
-  auto pv_qk = [&](int st_prev, int st_cur) {
-    const unsigned char* vs = stage_ptr(st_prev);
-    const unsigned char* kst = stage_ptr(st_cur);
+  auto pv_qk = [&](int i) {
+    const unsigned char* vs = v_base(i - 1);
+    const unsigned char* kst = stage_ptr(i % NS);
     f32x4_t n[4][2];
 #pragma unroll
     for (int b = 0; b < 4; ++b) n[b][0] = n[b][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -572,9 +611,9 @@ __global__ __launch_bounds__(512, 1) void prefill_paged_kernel(const PrefillArgs
   // operand reads are software-pipelined by hand (kAhead in flight) and one
   // load goes out after every fourth operand (eighth MFMA), fenced so the
   // order stays as written.
-  auto pv_qk_dma = [&](int st_prev, int st_cur, bool with_dma) {
-    const unsigned char* vs = stage_ptr(st_prev);
-    const unsigned char* kst = stage_ptr(st_cur);
+  auto pv_qk_dma = [&](int i, bool with_dma) {
+    const unsigned char* vs = v_base(i - 1);
+    const unsigned char* kst = stage_ptr(i % NS);
     constexpr int kAhead = 8;
     auto op_read = [&](int k) -> u32x4_t {
       if (is_pv(k)) return v_read(vs, k >> 1);
@@ -608,31 +647,31 @@ __global__ __launch_bounds__(512, 1) void prefill_paged_kernel(const PrefillArgs
   // "PV(i-1), QK(i), softmax(i)"; waves 4-7 run "softmax(i-1), PV(i-1), QK(i)".
   // Waves w and w+4 share a SIMD, so while one streams matrix-core work the
   // other runs its softmax on the vector ALUs, and they swap halfway.
-  // Tile t is read in intervals t and t+1; its stage is refilled with tile
-  // t + kStages, issued in interval t + 2, which leaves kStages - 2 intervals
-  // for the load to land.
-  constexpr int NS = C::kStages;
+  // Tile t's stage is read in intervals t .. t + kReads - 1 and refilled with
+  // tile t + NS, issued in interval t + kReads, which leaves NA = NS - kReads
+  // intervals for the load to land.  On a contiguous cache every wave also
+  // transposes its share of V(t) in interval t (vt_fill), before its phases.
   const int n = j_hi - j_lo;
 #pragma unroll
-  for (int p = 0; p < NS - 2; ++p)
+  for (int p = 0; p < NA; ++p)
     if (p < n) issue(tile_id(p), p);
-  int32_t block_ahead = (NS - 2 < n) ? tile_id(NS - 2) : 0;
-  // Start of interval i: tile i must have landed (tiles i+1 .. i+NS-3 may
-  // still be in flight); after the barrier the stage of tile i-2 is free and
-  // receives tile i+NS-2.
+  int32_t block_ahead = (NA < n) ? tile_id(NA) : 0;
+  // Start of interval i: tile i must have landed (tile i+1 may still be in
+  // flight); after the barrier the stage of tile i-kReads is free and
+  // receives tile i+NA.
   bool pending = false;
   auto interval_start = [&](int i) {
     if (i < n) {
-      if (min(NS - 3, n - 1 - i) >= 1) wait_vmem<C::LPT>();
+      if (min(NA - 1, n - 1 - i) >= 1) wait_vmem<C::LPT>();
       else wait_vmem<0>();
     }
     workgroup_barrier();
-    pending = i + NS - 2 < n;
+    pending = i + NA < n;
     if (pending) {
-      if (i == 0) issue(block_ahead, NS - 2);          // no matrix phase to hide it in
-      else if (wave < 4) prep(block_ahead, (i + NS - 2) % NS);   // issued inside pv_qk_dma
+      if (i == 0) issue(block_ahead, NA % NS);         // no matrix phase to hide it in
+      else if (wave < 4) prep(block_ahead, (i + NA) % NS);   // issued inside pv_qk_dma
     }
-    block_ahead = (i + NS - 1 < n) ? tile_id(i + NS - 1) : 0;
+    block_ahead = (i + NA + 1 < n) ? tile_id(i + NA + 1) : 0;
     const int key0 = (j_lo + i) * kBlock;
     if (!kContig && i < n && key0 + kBlock > kv_len32) {
       // The tile holding the sequence end: zero its values of keys >= kv_len
@@ -646,6 +685,7 @@ __global__ __launch_bounds__(512, 1) void prefill_paged_kernel(const PrefillArgs
         vt[((key >> 3) * DV + dv) * 8 + (key & 7)] = 0;
       }
     }
+    if (i < n) vt_fill(i);
   };
   // Each group has its own copy of the loop, so only P (leading waves) or
   // only S (trailing waves) stays live across the barrier.  Every wave runs
@@ -662,13 +702,13 @@ __global__ __launch_bounds__(512, 1) void prefill_paged_kernel(const PrefillArgs
     __builtin_amdgcn_sched_barrier(0);
     for (int i = 1; i < n; ++i) {
       interval_start(i);
-      pv_qk_dma((i - 1) % NS, i % NS, pending);
+      pv_qk_dma(i, pending);
       __builtin_amdgcn_sched_barrier(0);
       softmax(j_lo + i, false);
       __builtin_amdgcn_sched_barrier(0);
     }
     interval_start(n);
-    pv((n - 1) % NS);
+    pv(n - 1);
   } else {
     interval_start(0);
     qk(0);
@@ -677,13 +717,13 @@ __global__ __launch_bounds__(512, 1) void prefill_paged_kernel(const PrefillArgs
       interval_start(i);
       softmax(j_lo + i - 1, i == 1);
       __builtin_amdgcn_sched_barrier(0);
-      pv_qk((i - 1) % NS, i % NS);
+      pv_qk(i);
       __builtin_amdgcn_sched_barrier(0);
     }
     interval_start(n);
     softmax(j_lo + n - 1, n == 1);
     __builtin_amdgcn_sched_barrier(0);
-    pv((n - 1) % NS);
+    pv(n - 1);
   }
 
   // ---- epilogue ------------------------------------------------------------------
