@@ -144,6 +144,42 @@ def _stream(stream) -> int | None:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
 
 
+def _nbytes(t) -> int:
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+# The C calls take bare pointers and sizes, so they cannot see a tensor's
+# shape, dtype or strides; these checks refuse, before the library is called,
+# a tensor laid out other than the call assumes (the kernels would read or
+# write outside it).
+def _expect(t, name: str, shape=None, dtype=None, dense: bool = True) -> None:
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None:
+        allowed = dtype if isinstance(dtype, tuple) else (dtype,)
+        if t.dtype not in allowed:
+            raise ValueError(f"{name}: dtype {t.dtype}, expected {' or '.join(str(a) for a in allowed)}")
+    if dense and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _expect_on_gpu(**tensors) -> None:
+    for name, t in tensors.items():
+        if t is not None and not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+
+
+def _expect_paged_pool(k_pool, v_pool, kv_heads: int, head_dim: int, head_dim_v: int, dtype) -> None:
+    """The pools :func:`paged_pool` makes: K ``[nb, kv_heads, d/x, 64, x]``, V ``[nb, kv_heads, 64/x, dv, x]``
+    with x values per 16 bytes."""
+    x = elems_per_16b(dtype)
+    nb = k_pool.shape[0]
+    _expect(k_pool, "k_pool", (nb, kv_heads, head_dim // x, BLOCK_SIZE, x), dtype)
+    _expect(v_pool, "v_pool", (nb, kv_heads, BLOCK_SIZE // x, head_dim_v, x), dtype)
+
+
 def _dtype_code(dt: torch.dtype) -> int:
     if dt == torch.bfloat16:
         return CA_BF16
@@ -274,14 +310,25 @@ def chunk_prefill_attn(q, k_cache, v_cache, past_len: int, scale: float | None =
     sizes it for split partials only, so the cache is read in place).
     Returns ``out`` (and ``lse [heads, chunk_len]`` when requested).
     """
+    if q.dim() != 3:
+        raise ValueError(f"q: expected [chunk_len, heads, head_dim], got shape {tuple(q.shape)}")
+    _expect(q, "q", dtype=(torch.bfloat16, torch.float32))
     c, heads, d = q.shape
     paged = kv_layout == "paged"
     if paged:
         nb, hkv = k_cache.shape[0], k_cache.shape[1]
         dv = v_cache.shape[3]
+        _expect_paged_pool(k_cache, v_cache, hkv, d, dv, q.dtype)
+        _expect(block_table, "block_table", dtype=torch.int32)
     else:
+        if k_cache.dim() != 3 or v_cache.dim() != 3:
+            raise ValueError("contiguous caches are [capacity, kv_heads, head_dim(_v)]")
         hkv, dv = k_cache.shape[1], v_cache.shape[2]
         nb = 0
+        if k_cache.shape[2] != d or v_cache.shape[1] != hkv:
+            raise ValueError("k_cache / v_cache disagree with q's head_dim or with each other's kv_heads")
+        _expect(k_cache, "k_cache", dtype=q.dtype, dense=False)
+        _expect(v_cache, "v_cache", dtype=q.dtype, dense=False)
     if kv_heads is not None and kv_heads != hkv:
         raise ValueError("kv_heads disagrees with the cache shape")
     if head_dim_v is not None and head_dim_v != dv:
@@ -290,8 +337,11 @@ def chunk_prefill_attn(q, k_cache, v_cache, past_len: int, scale: float | None =
     out_dtype = q.dtype if out_dtype is None else out_dtype
     if out is None:
         out = torch.empty((c, heads, dv), dtype=out_dtype, device=q.device)
+    _expect(out, "out", (c, heads, dv), (torch.bfloat16, torch.float32))
     if return_lse and lse is None:
         lse = torch.empty((heads, c), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _expect(lse, "lse", (heads, c), torch.float32)
     if workspace is None and not paged and relayout and c > 0:
         need = chunkattn_prefill_contiguous_workspace_size(past_len, c, heads, hkv, d, dv, num_splits,
                                                            _dtype_code(q.dtype))
@@ -326,8 +376,10 @@ def chunk_prefill_attn(q, k_cache, v_cache, past_len: int, scale: float | None =
     o.lse_out = _ptr(lse)
     if workspace is not None:
         o.workspace = _ptr(workspace)
-        o.workspace_bytes = workspace.numel() * workspace.element_size()
+        o.workspace_bytes = _nbytes(workspace)
     o.num_splits = num_splits
+    _expect_on_gpu(q=q, k_cache=k_cache, v_cache=v_cache, block_table=block_table if paged else None, out=out,
+                   lse=lse, workspace=workspace)
     _check(lib().chunk_prefill_attn(_ptr(q), _ptr(k_cache), _ptr(v_cache), past_len, c, heads, hkv, d,
                                     float(scale), _ptr(out), ctypes.byref(o), _stream(stream)))
     return (out, lse) if return_lse else out
@@ -365,27 +417,41 @@ def chunk_attn_varlen(q, k_pool, v_pool, block_tables, cu_seqlens_q, kv_lens, sc
     are made unless given.  ``block_tables`` is ``[num_seqs, max_blocks]`` int32
     on the device.  The output is bf16 or fp32 (``out_dtype``, or that of ``out``).
     """
+    if q.dim() != 3:
+        raise ValueError(f"q: expected [total_q, heads, head_dim], got shape {tuple(q.shape)}")
+    _expect(q, "q", dtype=torch.bfloat16)
     total_q, heads, d = q.shape
     hkv, dv = k_pool.shape[1], v_pool.shape[3]
+    _expect_paged_pool(k_pool, v_pool, hkv, d, dv, q.dtype)
     cu, kv = _host_i32(cu_seqlens_q), _host_i32(kv_lens)
+    if cu.numel() != kv.numel() + 1:
+        raise ValueError("cu_seqlens_q needs one more entry than kv_lens")
+    _expect(block_tables, "block_tables", (kv.numel(), block_tables.shape[-1]), torch.int32)
     n = kv.numel()
     scale = 1.0 / math.sqrt(d) if scale is None else scale
     if cu_seqlens_q_dev is None:
         cu_seqlens_q_dev = cu.to(q.device)
     if kv_lens_dev is None:
         kv_lens_dev = kv.to(q.device)
+    _expect(cu_seqlens_q_dev, "cu_seqlens_q_dev", (n + 1,), torch.int32)
+    _expect(kv_lens_dev, "kv_lens_dev", (n,), torch.int32)
     if out is None:
         out = torch.empty((total_q, heads, dv), dtype=out_dtype or q.dtype, device=q.device)
+    _expect(out, "out", (total_q, heads, dv), (torch.bfloat16, torch.float32))
     if return_lse and lse is None:
         lse = torch.empty((heads, total_q), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _expect(lse, "lse", (heads, total_q), torch.float32)
     if workspace is None:
         need = lib().chunkattn_varlen_workspace_size(cu.data_ptr(), kv.data_ptr(), n, heads, hkv, dv)
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _expect_on_gpu(q=q, k_pool=k_pool, v_pool=v_pool, block_tables=block_tables, cu_seqlens_q_dev=cu_seqlens_q_dev,
+                   kv_lens_dev=kv_lens_dev, out=out, lse=lse, workspace=workspace)
     _check(lib().chunk_attn_varlen(
         _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables), block_tables.shape[1],
         k_pool.shape[0] if num_blocks is None else num_blocks, _ptr(cu_seqlens_q_dev), _ptr(kv_lens_dev),
         cu.data_ptr(), kv.data_ptr(), n, heads, hkv, d, dv, float(scale), _ptr(out), _dtype_code(out.dtype),
-        _ptr(lse), _ptr(workspace), workspace.numel(), _stream(stream)))
+        _ptr(lse), _ptr(workspace), _nbytes(workspace), _stream(stream)))
     return (out, lse) if return_lse else out
 
 
@@ -399,9 +465,24 @@ def chunk_attn_varlen_noalloc(q, k_pool, v_pool, block_tables, cu_seqlens_q, kv_
     none.  ``cu_seqlens_q`` and ``kv_lens`` are host sequences (int32); the
     output dtype (bf16 or fp32) is that of ``out``.
     """
+    if q.dim() != 3:
+        raise ValueError(f"q: expected [total_q, heads, head_dim], got shape {tuple(q.shape)}")
+    _expect(q, "q", dtype=torch.bfloat16)
     total_q, heads, d = q.shape
     hkv, dv = k_pool.shape[1], v_pool.shape[3]
+    _expect_paged_pool(k_pool, v_pool, hkv, d, dv, q.dtype)
     cu, kv = _host_i32(cu_seqlens_q), _host_i32(kv_lens)
+    if cu.numel() != kv.numel() + 1:
+        raise ValueError("cu_seqlens_q needs one more entry than kv_lens")
+    _expect(block_tables, "block_tables", (kv.numel(), block_tables.shape[-1]), torch.int32)
+    n = kv.numel()
+    _expect(cu_seqlens_q_dev, "cu_seqlens_q_dev", (n + 1,), torch.int32)
+    _expect(kv_lens_dev, "kv_lens_dev", (n,), torch.int32)
+    _expect(out, "out", (total_q, heads, dv), (torch.bfloat16, torch.float32))
+    if lse is not None:
+        _expect(lse, "lse", (heads, total_q), torch.float32)
+    _expect_on_gpu(q=q, k_pool=k_pool, v_pool=v_pool, block_tables=block_tables, cu_seqlens_q_dev=cu_seqlens_q_dev,
+                   kv_lens_dev=kv_lens_dev, out=out, lse=lse)
     scale = 1.0 / math.sqrt(d) if scale is None else scale
     _check(lib().chunk_attn_varlen_noalloc(
         _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables), block_tables.shape[1],
@@ -416,13 +497,22 @@ def chunkattn_kv_append(k_new, v_new, start_pos: int, block_table, k_pool, v_poo
     """Write ``k_new [n, kv_heads, d]`` / ``v_new [n, kv_heads, dv]`` at positions start_pos..
 
     Either may be a strided view (e.g. sliced out of a fused QKV tensor) with a dense last dim."""
+    if k_new.dim() != 3 or v_new.dim() != 3:
+        raise ValueError("k_new / v_new are [n, kv_heads, head_dim(_v)]")
     n, hkv, d = k_new.shape
     dv = v_new.shape[2]
+    if v_new.shape[:2] != (n, hkv):
+        raise ValueError("k_new and v_new disagree on tokens or kv_heads")
+    _expect(k_new, "k_new", dtype=(torch.bfloat16, torch.float32), dense=False)
+    _expect(v_new, "v_new", dtype=k_new.dtype, dense=False)
+    _expect_paged_pool(k_pool, v_pool, hkv, d, dv, k_new.dtype)
+    _expect(block_table, "block_table", dtype=torch.int32)
     strides = None
     if not (k_new.is_contiguous() and v_new.is_contiguous()):
         if k_new.stride(2) != 1 or v_new.stride(2) != 1:
             raise ValueError("k_new / v_new: the head dim must be dense")
         strides = (ctypes.c_int64 * 4)(_stride(k_new, 0), _stride(k_new, 1), _stride(v_new, 0), _stride(v_new, 1))
+    _expect_on_gpu(k_new=k_new, v_new=v_new, block_table=block_table, k_pool=k_pool, v_pool=v_pool)
     _check(lib().chunkattn_kv_append(_ptr(k_new), _ptr(v_new), start_pos, n, hkv, d, dv, _dtype_code(k_new.dtype),
                                      _ptr(block_table), block_table.numel(),
                                      k_pool.shape[0] if num_blocks is None else num_blocks,
@@ -441,10 +531,22 @@ def mla_pool(num_blocks: int, fmt: int, device="cuda"):
     return torch.empty((num_blocks, nbytes), dtype=torch.uint8, device=device)
 
 
+def _expect_mla_pool(pool, fmt: int) -> None:
+    nbytes = chunkattn_mla_block_bytes(fmt)
+    if nbytes == 0:
+        raise ValueError(f"unknown MLA cache format {fmt}")
+    _expect(pool, "pool", (pool.shape[0], nbytes), torch.uint8)
+
+
 def chunkattn_mla_kv_append(latent, rope, start_pos: int, block_table, pool, fmt: int, *,
                             num_blocks: int | None = None, stream=None) -> None:
     """Write ``latent [n, 512]`` / ``rope [n, 64]`` (bf16) at positions start_pos.. of one sequence."""
     n = latent.shape[0]
+    _expect(latent, "latent", (n, MLA_LATENT), torch.bfloat16)
+    _expect(rope, "rope", (n, MLA_ROPE), torch.bfloat16)
+    _expect_mla_pool(pool, fmt)
+    _expect(block_table, "block_table", dtype=torch.int32)
+    _expect_on_gpu(latent=latent, rope=rope, block_table=block_table, pool=pool)
     _check(lib().chunkattn_mla_kv_append(_ptr(latent), _ptr(rope), start_pos, n, fmt, _ptr(block_table),
                                          block_table.numel(), pool.shape[0] if num_blocks is None else num_blocks,
                                          _ptr(pool), _stream(stream)))
@@ -461,21 +563,34 @@ def chunk_mla_decode(q, pool, fmt: int, block_tables, kv_lens, scale: float, *, 
     """Absorbed MLA decode: ``q [num_seqs, heads, 576]`` bf16 against the latent pool; returns
     ``out [num_seqs, heads, 512]`` in ``out_dtype`` (bf16 or fp32; that of ``out`` when given) and
     ``lse [heads, num_seqs]`` fp32."""
+    if q.dim() != 3:
+        raise ValueError(f"q: expected [num_seqs, heads, {MLA_LATENT + MLA_ROPE}], got shape {tuple(q.shape)}")
     n, heads, _ = q.shape
+    _expect(q, "q", (n, heads, MLA_LATENT + MLA_ROPE), torch.bfloat16)
+    _expect_mla_pool(pool, fmt)
     kv = _host_i32(kv_lens)
+    if kv.numel() != n:
+        raise ValueError(f"kv_lens has {kv.numel()} entries for {n} sequences")
+    _expect(block_tables, "block_tables", (n, block_tables.shape[-1]), torch.int32)
     if kv_lens_dev is None:
         kv_lens_dev = kv.to(q.device)
+    _expect(kv_lens_dev, "kv_lens_dev", (n,), torch.int32)
     if out is None:
         out = torch.empty((n, heads, MLA_LATENT), dtype=out_dtype, device=q.device)
+    _expect(out, "out", (n, heads, MLA_LATENT), (torch.bfloat16, torch.float32))
     if return_lse and lse is None:
         lse = torch.empty((heads, n), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _expect(lse, "lse", (heads, n), torch.float32)
     if workspace is None:
         need = lib().chunkattn_mla_decode_workspace_size(kv.data_ptr(), n, heads, fmt)
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _expect_on_gpu(q=q, pool=pool, block_tables=block_tables, kv_lens_dev=kv_lens_dev, out=out, lse=lse,
+                   workspace=workspace)
     _check(lib().chunk_mla_decode(
         _ptr(q), _ptr(pool), fmt, _ptr(block_tables), block_tables.shape[1],
         pool.shape[0] if num_blocks is None else num_blocks, _ptr(kv_lens_dev), kv.data_ptr(), n, heads,
-        float(scale), _ptr(out), _dtype_code(out.dtype), _ptr(lse), _ptr(workspace), workspace.numel(),
+        float(scale), _ptr(out), _dtype_code(out.dtype), _ptr(lse), _ptr(workspace), _nbytes(workspace),
         _stream(stream)))
     return (out, lse) if return_lse else out
 
@@ -491,17 +606,25 @@ def chunk_mla_prefill(q, pool, fmt: int, block_table, past_len: int, scale: floa
     ``past_len ..`` of the sequence whose latent records the pool holds through ``block_table``;
     returns ``out [chunk_len, heads, 512]`` (``out_dtype``, or that of ``out``) and
     ``lse [heads, chunk_len]`` fp32.  An fp8 pool needs a workspace (allocated when not given)."""
+    if q.dim() != 3:
+        raise ValueError(f"q: expected [chunk_len, heads, {MLA_LATENT + MLA_ROPE}], got shape {tuple(q.shape)}")
     c, heads, _ = q.shape
+    _expect(q, "q", (c, heads, MLA_LATENT + MLA_ROPE), torch.bfloat16)
+    _expect_mla_pool(pool, fmt)
+    _expect(block_table, "block_table", dtype=torch.int32)
     if out is None:
         out = torch.empty((c, heads, MLA_LATENT), dtype=out_dtype, device=q.device)
+    _expect(out, "out", (c, heads, MLA_LATENT), (torch.bfloat16, torch.float32))
     if return_lse and lse is None:
         lse = torch.empty((heads, c), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _expect(lse, "lse", (heads, c), torch.float32)
     if workspace is None:
         need = chunkattn_mla_prefill_workspace_size(past_len, c, fmt)
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device) if need else None
+    _expect_on_gpu(q=q, pool=pool, block_table=block_table, out=out, lse=lse, workspace=workspace)
     _check(lib().chunk_mla_prefill(
         _ptr(q), _ptr(pool), fmt, _ptr(block_table), block_table.shape[-1],
         pool.shape[0] if num_blocks is None else num_blocks, int(past_len), c, heads, float(scale), _ptr(out),
-        _dtype_code(out.dtype), _ptr(lse), _ptr(workspace), 0 if workspace is None else workspace.numel(),
-        _stream(stream)))
+        _dtype_code(out.dtype), _ptr(lse), _ptr(workspace), _nbytes(workspace), _stream(stream)))
     return (out, lse) if return_lse else out

@@ -364,3 +364,67 @@ def test_broadcast_cache_view_is_refused_before_the_library():
     q = torch.empty((3, 8, 64), dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="broadcast"):
         L.chunk_prefill_attn(q, k, k, 6, relayout=False)
+
+
+def test_binding_refuses_mislaid_tensors_before_the_library():
+    """The C calls take bare pointers, so the binding checks every tensor's shape, dtype and layout against
+    what the call assumes, and refuses a host tensor, before the library is called (torch CPU tensors)."""
+    bf, f32 = torch.bfloat16, torch.float32
+    c, hq, hkv, d = 8, 8, 2, 128
+    q = torch.zeros((c, hq, d), dtype=bf)
+    kp, vp = L.paged_pool(4, hkv, d, d, bf, device="cpu")
+    table = torch.zeros(4, dtype=torch.int32)
+    run = lambda **kw: L.chunk_prefill_attn(**{**dict(q=q, k_cache=kp, v_cache=vp, past_len=0,
+                                                      kv_layout="paged", block_table=table), **kw})
+    with pytest.raises(ValueError, match="q: expected"):
+        run(q=q[0])
+    with pytest.raises(ValueError, match="k_pool: shape"):
+        run(k_cache=L.paged_pool(4, hkv, 64, d, bf, device="cpu")[0])          # head dim 64 against q's 128
+    with pytest.raises(ValueError, match="k_pool must be contiguous"):
+        run(k_cache=torch.empty((4, 4, 16, 64, 8), dtype=bf)[:, ::2])
+    with pytest.raises(ValueError, match="v_pool: dtype"):
+        run(v_cache=vp.float())
+    with pytest.raises(ValueError, match="block_table: dtype"):
+        run(block_table=table.long())
+    with pytest.raises(ValueError, match="out: shape"):
+        run(out=torch.empty((c, hq, 64), dtype=bf))
+    with pytest.raises(ValueError, match="out must be contiguous"):
+        run(out=torch.empty((hq, c, d), dtype=bf).transpose(0, 1))
+    with pytest.raises(ValueError, match="lse: dtype"):
+        run(lse=torch.empty((hq, c), dtype=bf))
+    with pytest.raises(ValueError, match="must be a GPU tensor"):
+        run()
+    kc = torch.zeros((c, hkv, d), dtype=bf)
+    with pytest.raises(ValueError, match="k_cache: dtype"):
+        L.chunk_prefill_attn(q, kc.float(), kc, 0, relayout=False)
+    with pytest.raises(ValueError, match="disagree"):
+        L.chunk_prefill_attn(q, kc[:, :, :64], kc, 0, relayout=False)
+    # mixed batch
+    cu, kv = [0, 4, 5], [4, 70]
+    tables = torch.zeros((2, 2), dtype=torch.int32)
+    qv = torch.zeros((5, hq, d), dtype=bf)
+    with pytest.raises(ValueError, match="block_tables: shape"):
+        L.chunk_attn_varlen(qv, kp, vp, tables[:1], cu, kv)
+    with pytest.raises(ValueError, match="one more entry"):
+        L.chunk_attn_varlen(qv, kp, vp, tables, cu[:2], kv)
+    with pytest.raises(ValueError, match="q: dtype"):
+        L.chunk_attn_varlen(qv.float(), kp, vp, tables, cu, kv)
+    # cache writes
+    with pytest.raises(ValueError, match="disagree"):
+        L.chunkattn_kv_append(kc, kc[:4], 0, table, kp, vp)
+    with pytest.raises(ValueError, match="k_pool: shape"):                     # fp32 rows against a bf16 pool
+        L.chunkattn_kv_append(kc.float(), kc.float(), 0, table, kp, vp)
+    # MLA latent calls
+    pool = L.mla_pool(4, L.CA_MLA_BF16, device="cpu")
+    qm = torch.zeros((c, 16, L.MLA_LATENT + L.MLA_ROPE), dtype=bf)
+    with pytest.raises(ValueError, match="q: shape"):
+        L.chunk_mla_prefill(qm[:, :, :L.MLA_LATENT], pool, L.CA_MLA_BF16, table, 0, 0.1)
+    with pytest.raises(ValueError, match="pool: shape"):
+        L.chunk_mla_prefill(qm, pool, L.CA_MLA_FP8, table, 0, 0.1)
+    with pytest.raises(ValueError, match="must be a GPU tensor"):
+        L.chunk_mla_prefill(qm, pool, L.CA_MLA_BF16, table, 0, 0.1)
+    with pytest.raises(ValueError, match="kv_lens has"):
+        L.chunk_mla_decode(qm, pool, L.CA_MLA_BF16, tables, [4], 0.1)
+    with pytest.raises(ValueError, match="rope: shape"):
+        L.chunkattn_mla_kv_append(torch.zeros((3, L.MLA_LATENT), dtype=bf), torch.zeros((3, 32), dtype=bf), 0,
+                                  table, pool, L.CA_MLA_BF16)
