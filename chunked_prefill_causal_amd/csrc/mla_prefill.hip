@@ -68,12 +68,13 @@ __device__ __forceinline__ f32x4_t mfma16(u32x4_t a, u32x4_t b, f32x4_t c) {
 // S^T += K Q^T with the accumulator pinned to VGPRs: the 32 x 512 output
 // tile takes all 256 AGPRs, and the compiler would otherwise put S^T there too
 // and spill.  The compiler cannot see hazards through the asm; the caller waits
-// 18+ states before vector code reads S^T.
+// 18+ states before vector code reads S^T.  The first product's result is
+// early-clobber: it must not take the registers of an operand that dies there.
 __device__ __forceinline__ void mfma16_vgpr(f32x4_t& c, const u32x4_t& a, const u32x4_t& b) {
   asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
 }
 __device__ __forceinline__ void mfma16_vgpr_first(f32x4_t& c, const u32x4_t& a, const u32x4_t& b) {
-  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=v"(c) : "v"(a), "v"(b));
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "v"(b));
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
