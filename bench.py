@@ -66,7 +66,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=5)
     p.add_argument("--warmup", type=int, default=2)
-    p.add_argument("--cpu-rows", type=int, default=4096, help="oracle rows sampled per chunk for the CPU baseline")
+    p.add_argument("--cpu-rows", type=int, default=6144, help="oracle rows sampled per chunk for the CPU baseline (about 10 s on 16 host cores)")
     p.add_argument("--curve-reps", type=int, default=3,
                    help="repetitions per chunk for the 32K and 512K MLA-shaped prompt curves")
     p.add_argument("--no-cpu-baseline", action="store_true")
