@@ -39,6 +39,8 @@
 //    1.8 KB per visible token, well under 1% of a chunk's matrix time, where
 //    widening inside the kernel would put ~256 vector ops per lane and tile on
 //    the only wave of each SIMD.
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -197,7 +199,8 @@ __global__ __launch_bounds__(256, 1) void mla_prefill_kernel(const MlaPrefillArg
   // the block's 16, i.e. run 2 bb + (lc % 4) / 2, half lc % 2.
   const int v_lane = (4 * lg + (lc >> 2)) * 16 + (lc & 1) * 8 + ((lc & 3) >> 1) * 1024;
 
-  auto tile = [&](int j, int st, bool first, bool with_dma) {
+  auto tile = [&](int j, int st, bool first, auto with_dma_tag) {
+    constexpr bool with_dma = decltype(with_dma_tag)::value;
     const unsigned char* stage = smem + st * kTileBytes;
     // ---- S^T = K Q^T ----
     f32x4_t s[4][2];
@@ -220,7 +223,7 @@ __global__ __launch_bounds__(256, 1) void mla_prefill_kernel(const MlaPrefillArg
         if (k + kAhead < kOps) rd[k + kAhead] = *k_ptr(k + kAhead);
         if ((k & 3) == 3) {
           __builtin_amdgcn_sched_barrier(0);
-          if (with_dma) dma_one(k >> 2);
+          if constexpr (with_dma) dma_one(k >> 2);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -339,11 +342,12 @@ __global__ __launch_bounds__(256, 1) void mla_prefill_kernel(const MlaPrefillArg
   prep(0, 0);
 #pragma unroll
   for (int n = 0; n < kLoads; ++n) dma_one(n);
-  for (int t = 0; t < n_tiles; ++t) {
+  // Every tile but the last moves the next one; that is a compile-time tag of
+  // the tile body, so no load point in the QK phase carries a branch.
+  auto step = [&](int t, auto with_dma_tag) {
     wait_all_vmem();
     barrier();                                     // tile t landed everywhere; stage (t + 1) % 2 is free
-    const bool pend = t + 1 < n_tiles;
-    if (pend) prep(t + 1, (t + 1) & 1);
+    if constexpr (decltype(with_dma_tag)::value) prep(t + 1, (t + 1) & 1);
     const int key0 = t * kBlock;
     if (key0 + kBlock > kv_len32) {
       // keys past the sequence end: zero their latent values (0 * NaN would poison O)
@@ -355,8 +359,10 @@ __global__ __launch_bounds__(256, 1) void mla_prefill_kernel(const MlaPrefillArg
       }
       barrier();
     }
-    tile(t, t & 1, t == 0, pend);
-  }
+    tile(t, t & 1, t == 0, with_dma_tag);
+  };
+  for (int t = 0; t < n_tiles - 1; ++t) step(t, std::true_type{});
+  if (n_tiles > 0) step(n_tiles - 1, std::false_type{});
 
   // ---- epilogue: lane (lg, lc) holds latent values 16 bb + 4 lg .. +3 of its rows ----
 #pragma unroll

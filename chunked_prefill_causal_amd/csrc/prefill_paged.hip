@@ -50,6 +50,8 @@
 //  * Values of keys past the sequence end are zeroed in LDS once the tile
 //    holding the sequence end has landed, logits past a row's position are
 //    masked with a select, so NaN in unused pool slots never reaches an output.
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -610,8 +612,11 @@ __global__ __launch_bounds__(512, 1) void prefill_paged_kernel(const PrefillArgs
   // pv_qk for the leading waves with the pending tile's loads interleaved: the
   // operand reads are software-pipelined by hand (kAhead in flight) and one
   // load goes out after every fourth operand (eighth MFMA), fenced so the
-  // order stays as written.
-  auto pv_qk_dma = [&](int i, bool with_dma) {
+  // order stays as written.  Whether the interval moves a tile is a
+  // compile-time tag: a runtime test at each load point put branches into the
+  // matrix phase and cost ~3.5 % of the loop.
+  auto pv_qk_dma = [&](int i, auto with_dma_tag) {
+    constexpr bool with_dma = decltype(with_dma_tag)::value;
     const unsigned char* vs = v_base(i - 1);
     const unsigned char* kst = stage_ptr(i % NS);
     constexpr int kAhead = 8;
@@ -632,7 +637,7 @@ __global__ __launch_bounds__(512, 1) void prefill_paged_kernel(const PrefillArgs
       if (k + kAhead < kOps) rd[k + kAhead] = op_read(k + kAhead);
       if ((k & 3) == 3 && (k >> 2) < C::LPT) {
         __builtin_amdgcn_sched_barrier(0);
-        if (with_dma) dma_one(k >> 2);
+        if constexpr (with_dma) dma_one(k >> 2);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -700,9 +705,18 @@ __global__ __launch_bounds__(512, 1) void prefill_paged_kernel(const PrefillArgs
     __builtin_amdgcn_sched_barrier(0);
     softmax(j_lo, true);
     __builtin_amdgcn_sched_barrier(0);
-    for (int i = 1; i < n; ++i) {
+    // intervals 1 .. n-NA-1 each move a tile (i + NA < n); the last NA do not
+    int i = 1;
+    for (; i < n - NA; ++i) {
       interval_start(i);
-      pv_qk_dma(i, pending);
+      pv_qk_dma(i, std::true_type{});
+      __builtin_amdgcn_sched_barrier(0);
+      softmax(j_lo + i, false);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    for (; i < n; ++i) {
+      interval_start(i);
+      pv_qk_dma(i, std::false_type{});
       __builtin_amdgcn_sched_barrier(0);
       softmax(j_lo + i, false);
       __builtin_amdgcn_sched_barrier(0);
