@@ -483,9 +483,9 @@ __global__ __launch_bounds__(512, 1) void prefill_paged_kernel(const PrefillArgs
   // 4 lanes of a row, and a row whose maximum passed the threshold is rescaled
   // and its exps redone.  Otherwise each exp stays below kPsumCap, which keeps
   // the fp32 sums far from overflow, so the result is the same softmax.
-  auto softmax = [&](int j, bool first) {
+  auto softmax = [&](int j, bool first, auto maskable_tag) {
     const int key0 = j * kBlock;                 // positions stay below 2^30 (the boundary checks it)
-    if (key0 + kBlock - 1 > wave_first_pos32) {
+    if (decltype(maskable_tag)::value && key0 + kBlock - 1 > wave_first_pos32) {
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
         const int lim = (int)(pos[qb] - key0) - 8 * lg;   // register offsets past lim are invisible
@@ -699,26 +699,38 @@ __global__ __launch_bounds__(512, 1) void prefill_paged_kernel(const PrefillArgs
   // unchanged and keeps one straight-line loop body.  Scheduling fences keep
   // the matrix and vector phases in one piece each, so the two waves of a
   // SIMD stay interleaved as written.
+  // Tiles from j_mask on hold keys past this wave's first row and need the
+  // causal mask; the tiles before them never do.  Both splits below are
+  // compile-time tags of the loop bodies (wave-uniform bounds; every wave still
+  // runs n + 1 intervals).
+  const int i_mask = max(0, (wave_first_pos32 + 1) / kBlock - j_lo);
   if (wave < 4) {
     interval_start(0);
     qk(0);
     __builtin_amdgcn_sched_barrier(0);
-    softmax(j_lo, true);
+    softmax(j_lo, true, std::true_type{});
     __builtin_amdgcn_sched_barrier(0);
     // intervals 1 .. n-NA-1 each move a tile (i + NA < n); the last NA do not
     int i = 1;
+    for (const int i_a = min(n - NA, i_mask); i < i_a; ++i) {
+      interval_start(i);
+      pv_qk_dma(i, std::true_type{});
+      __builtin_amdgcn_sched_barrier(0);
+      softmax(j_lo + i, false, std::false_type{});
+      __builtin_amdgcn_sched_barrier(0);
+    }
     for (; i < n - NA; ++i) {
       interval_start(i);
       pv_qk_dma(i, std::true_type{});
       __builtin_amdgcn_sched_barrier(0);
-      softmax(j_lo + i, false);
+      softmax(j_lo + i, false, std::true_type{});
       __builtin_amdgcn_sched_barrier(0);
     }
     for (; i < n; ++i) {
       interval_start(i);
       pv_qk_dma(i, std::false_type{});
       __builtin_amdgcn_sched_barrier(0);
-      softmax(j_lo + i, false);
+      softmax(j_lo + i, false, std::true_type{});
       __builtin_amdgcn_sched_barrier(0);
     }
     interval_start(n);
@@ -727,15 +739,23 @@ __global__ __launch_bounds__(512, 1) void prefill_paged_kernel(const PrefillArgs
     interval_start(0);
     qk(0);
     __builtin_amdgcn_sched_barrier(0);
-    for (int i = 1; i < n; ++i) {
+    int i = 1;
+    for (const int i_t = min(n, i_mask + 1); i < i_t; ++i) {   // softmax of tile i - 1 < j_mask
       interval_start(i);
-      softmax(j_lo + i - 1, i == 1);
+      softmax(j_lo + i - 1, i == 1, std::false_type{});
+      __builtin_amdgcn_sched_barrier(0);
+      pv_qk(i);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    for (; i < n; ++i) {
+      interval_start(i);
+      softmax(j_lo + i - 1, i == 1, std::true_type{});
       __builtin_amdgcn_sched_barrier(0);
       pv_qk(i);
       __builtin_amdgcn_sched_barrier(0);
     }
     interval_start(n);
-    softmax(j_lo + n - 1, n == 1);
+    softmax(j_lo + n - 1, n == 1, std::true_type{});
     __builtin_amdgcn_sched_barrier(0);
     pv(n - 1);
   }
