@@ -702,8 +702,9 @@ __global__ __launch_bounds__(512, 1) void prefill_paged_kernel(const PrefillArgs
   // Tiles from j_mask on hold keys past this wave's first row and need the
   // causal mask; the tiles before them never do.  Both splits below are
   // compile-time tags of the loop bodies (wave-uniform bounds; every wave still
-  // runs n + 1 intervals).
-  const int i_mask = max(0, (wave_first_pos32 + 1) / kBlock - j_lo);
+  // runs n + 1 intervals).  The contiguous-cache kernel keeps the mask test in
+  // every body (measured faster there: its registers are nearly all in use).
+  const int i_mask = kContig ? 0 : max(0, (wave_first_pos32 + 1) / kBlock - j_lo);
   if (wave < 4) {
     interval_start(0);
     qk(0);
