@@ -55,7 +55,8 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 
 // 16 bytes per lane from global memory straight into LDS at m0 + 16 * lane.
 __device__ __forceinline__ void dma16(const void* g, uint32_t lds_wave_base) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_wave_base), "v"(g) : "memory", "m0");
+  // one wait state between the M0 write and the load that reads it (a GFX9 hazard)
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_wave_base), "v"(g) : "memory", "m0");
 }
 
 template <int N>

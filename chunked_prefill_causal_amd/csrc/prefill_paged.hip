@@ -90,7 +90,8 @@ __device__ __forceinline__ uint32_t lds_address(const void* p) {
 // 16 bytes per lane from global memory (uniform base + this lane's 32-bit
 // offset) straight into LDS at m0 + 16 * lane.
 __device__ __forceinline__ void load_to_lds16(const void* base, uint32_t lane_off, uint32_t lds_wave_base) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_wave_base), "v"(lane_off), "s"(base)
+  // one wait state between the M0 write and the load that reads it (a GFX9 hazard)
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_wave_base), "v"(lane_off), "s"(base)
                : "memory", "m0");
 }
 
