@@ -140,7 +140,7 @@ void ca_prefill_opts_init(ca_prefill_opts* opts);
  * (no workspace, or split partials only) the cache is read in place: at
  * (head_dim, head_dim_v) = (128, 128) by the same 8-wave kernel, laying each
  * tile out token-major in LDS and transposing its V once per workgroup into
- * the paged order (bitwise the paged result; ~10% slower), at the other pairs by
+ * the paged order (bitwise the paged result; 7-11% slower), at the other pairs by
  * the 4-wave contiguous kernel (same result within bf16 rounding, ~3x
  * slower at 128K).  Split-KV partials, if any, follow the copy.
  */
