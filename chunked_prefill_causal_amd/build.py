@@ -4,6 +4,12 @@ Every HIP source compiles to an object under ``_build/`` (in parallel), then
 one hipcc link produces ``chunked_prefill_causal_amd/libchunkattn.so``.
 Packed-FP32 instructions are disabled for all device code.
 
+The two prefill kernels write m0 (the LDS destination of a direct-to-LDS load)
+in one inline-asm statement and issue the load in a later one, with MFMAs in
+between as the wait state the GFX9 m0 hazard needs.  That is sound only while
+no code the compiler emits writes m0, so their device assembly is generated
+beside the objects and checked before the link (``check_m0``).
+
 ``python chunked_prefill_causal_amd/build.py --sanitize`` builds a host-side
 ASan + UBSan copy of the library and of the CPU oracle under ``_build/san``
 and runs the CPU test suite against them.
@@ -37,6 +43,9 @@ FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-
 # registers would be copied out and back on every loop iteration.
 EXTRA = {"mla.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
+# Sources whose loads read an m0 written by an earlier asm statement.
+M0_SPLIT = ["prefill_paged.hip", "mla_prefill.hip"]
+
 
 # Host-only AddressSanitizer + UndefinedBehaviorSanitizer build (device code is built as usual).  It
 # links against clang's shared sanitizer runtime, which the process must preload (see `sanitizer_env`).
@@ -65,12 +74,65 @@ def _compile(src: str, sanitize: bool = False) -> str:
     return obj
 
 
+def _device_asm(src: str) -> str:
+    """The gfx950 assembly of one source, as the object build compiles it."""
+    out = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".s")
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), "--cuda-device-only", "-S", "-x", "hip", os.path.join(CSRC, src),
+           "-o", out]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc -S failed on {src}:\n{r.stderr}")
+    with open(out) as f:
+        return f.read()
+
+
+def check_m0(asm: str, name: str) -> int:
+    """Check the two rules the split direct-to-LDS loads rely on, over every function of ``asm``: each write
+    of m0 comes from an inline-asm statement of ours (so none lands between our m0 write and the load that
+    reads it), and each direct-to-LDS load has at least one instruction between it and the last m0 write
+    (the wait state of the GFX9 hazard).  Returns the number of loads checked; raises on a violation."""
+    in_asm = False
+    since_m0 = None                                  # instructions since the last m0 write
+    loads = 0
+    for lineno, raw in enumerate(asm.splitlines(), 1):
+        line = raw.split(";")[0].strip() if not raw.lstrip().startswith(";;#ASM") else raw.strip()
+        if line.startswith(";;#ASMSTART"):
+            in_asm = True
+            continue
+        if line.startswith(";;#ASMEND"):
+            in_asm = False
+            continue
+        if not line or line.startswith(".") or line.endswith(":"):
+            if line.endswith(":") and not line.startswith("."):
+                since_m0 = None                      # a label: the path into it is not this one
+            continue
+        op, _, rest = line.partition(" ")
+        dst = rest.split(",")[0].strip()
+        if dst == "m0" and not op.startswith(("global_", "buffer_", "ds_")):
+            if not in_asm:
+                raise RuntimeError(f"{name}:{lineno}: the compiler writes m0 ({line}); the split direct-to-LDS "
+                                   "loads would read the wrong LDS destination")
+            since_m0 = 0
+            continue
+        if op.startswith("global_load_lds"):
+            if since_m0 == 0:
+                raise RuntimeError(f"{name}:{lineno}: direct-to-LDS load right after an m0 write")
+            loads += 1
+        if since_m0 is not None:
+            since_m0 += 1
+    return loads
+
+
 def build(verbose: bool = False, sanitize: bool = False) -> str:
     """Build libchunkattn.so in place; with ``sanitize`` a host-sanitized copy under _build/san instead."""
     out_dir = SAN_DIR if sanitize else BUILD_DIR
     os.makedirs(out_dir, exist_ok=True)
-    with ThreadPoolExecutor(len(SOURCES)) as ex:
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    with ThreadPoolExecutor(len(SOURCES) + len(M0_SPLIT)) as ex:
+        asm_jobs = [(src, ex.submit(_device_asm, src)) for src in M0_SPLIT]
         objs = list(ex.map(lambda src: _compile(src, sanitize), SOURCES))
+        for src, job in asm_jobs:
+            check_m0(job.result(), src)
     lib = os.path.join(SAN_DIR, "libchunkattn.so") if sanitize else LIB
     tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *(SAN_FLAGS if sanitize else []), "-o", tmp, *objs]

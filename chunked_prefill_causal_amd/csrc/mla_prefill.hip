@@ -90,6 +90,17 @@ __device__ __forceinline__ void dma16(const void* base, uint32_t lane_off, uint3
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_wave_base), "v"(lane_off), "s"(base)
                : "memory", "m0");
 }
+// The same load split in two for the QK phase: set_m0 writes the LDS
+// destination, and load_at_m0, issued two K operands (four MFMAs) later,
+// reads it.  The MFMAs between them are the wait state the M0 hazard needs,
+// so neither carries an s_nop.  Sound only because nothing the compiler emits
+// in this kernel writes m0: every m0 write is one of these asm statements.
+__device__ __forceinline__ void set_m0(uint32_t lds_wave_base) {
+  asm volatile("s_mov_b32 m0, %0" ::"s"(lds_wave_base) : "m0");
+}
+__device__ __forceinline__ void load_at_m0(const void* base, uint32_t lane_off) {
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(lane_off), "s"(base) : "memory");
+}
 
 __device__ __forceinline__ void wait_all_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ void barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
@@ -185,6 +196,8 @@ __global__ __launch_bounds__(256, 1) void mla_prefill_kernel(const MlaPrefillArg
   auto dma_one = [&](int n) {
     dma16(pend_b + n * kThreads * 16, lane_off, __builtin_amdgcn_readfirstlane(pend_lds + n * kThreads * 16));
   };
+  auto dma_m0 = [&](int n) { set_m0(__builtin_amdgcn_readfirstlane(pend_lds + n * kThreads * 16)); };
+  auto dma_load = [&](int n) { load_at_m0(pend_b + n * kThreads * 16, lane_off); };
 
   f32x4_t o[kNDB][2];
 #pragma unroll
@@ -222,9 +235,16 @@ __global__ __launch_bounds__(256, 1) void mla_prefill_kernel(const MlaPrefillArg
           mfma16_vgpr(s[k & 3][1], rd[k], qreg[1][k >> 2]);
         }
         if (k + kAhead < kOps) rd[k + kAhead] = *k_ptr(k + kAhead);
+        if constexpr (with_dma) {
+          if ((k & 3) == 1) {
+            __builtin_amdgcn_sched_barrier(0);
+            dma_m0(k >> 2);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
         if ((k & 3) == 3) {
           __builtin_amdgcn_sched_barrier(0);
-          if constexpr (with_dma) dma_one(k >> 2);
+          if constexpr (with_dma) dma_load(k >> 2);
           __builtin_amdgcn_sched_barrier(0);
         }
       }

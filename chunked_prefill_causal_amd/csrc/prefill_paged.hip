@@ -95,6 +95,18 @@ __device__ __forceinline__ void load_to_lds16(const void* base, uint32_t lane_of
                : "memory", "m0");
 }
 
+// The same load split in two for the matrix phase: set_m0 writes the LDS
+// destination, and load_at_m0, issued two MFMAs later, reads it.  The MFMAs
+// between them are the wait state the M0 hazard needs, so neither carries an
+// s_nop.  Sound only because nothing the compiler emits in this kernel writes
+// m0: every m0 write is one of these asm statements.
+__device__ __forceinline__ void set_m0(uint32_t lds_wave_base) {
+  asm volatile("s_mov_b32 m0, %0" ::"s"(lds_wave_base) : "m0");
+}
+__device__ __forceinline__ void load_at_m0(const void* base, uint32_t lane_off) {
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(lane_off), "s"(base) : "memory");
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmem() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
@@ -290,8 +302,11 @@ __global__ __launch_bounds__(512, 1) void prefill_paged_kernel(const PrefillArgs
   for (int i = 0; i < C::KPT; ++i) k_off_lane[i] = (kUnits * i + wave) * 1024 + key_of_slot(lane) * 16;
 #pragma unroll
   for (int i = 0; i < C::VPT; ++i) v_off_lane[i] = (kUnits * i + wave) * 1024 + lane * 16;
+  auto pool_m0 = [&](uint32_t lds_part, int i) {
+    return __builtin_amdgcn_readfirstlane(lds_part + (kUnits * i + wave) * 1024);
+  };
   auto pool_load = [&](const unsigned char* blk, uint32_t lane_off, uint32_t lds_part, int i) {
-    load_to_lds16(blk, lane_off, __builtin_amdgcn_readfirstlane(lds_part + (kUnits * i + wave) * 1024));
+    load_to_lds16(blk, lane_off, pool_m0(lds_part, i));
   };
   // Contiguous cache ([tokens][kv_heads][128], token-major): the tiles are laid
   // out token-major in LDS, one 256-byte row per key, its 16-byte units
@@ -363,16 +378,23 @@ __global__ __launch_bounds__(512, 1) void prefill_paged_kernel(const PrefillArgs
     }
     pend_lds = smem_base + st * C::Stage + (kContig ? wave * 64 * 16 : 0);
   };
-  auto dma_one = [&](int j) {
+  // dma_m0(j) then dma_load(j): the LDS destination and the load of chunk j.
+  auto dma_m0 = [&](int j) {
     if constexpr (kContig) {
-      if (j < C::KPT)
-        load_to_lds16(pend_k, k_cont_off(j, pend_lim), __builtin_amdgcn_readfirstlane(pend_lds + j * C::kLoaders * 16));
-      else
-        load_to_lds16(pend_v, v_cont_off(j - C::KPT, pend_lim),
-                      __builtin_amdgcn_readfirstlane(pend_lds + C::KBytes + (j - C::KPT) * C::kLoaders * 16));
+      if (j < C::KPT) set_m0(__builtin_amdgcn_readfirstlane(pend_lds + j * C::kLoaders * 16));
+      else set_m0(__builtin_amdgcn_readfirstlane(pend_lds + C::KBytes + (j - C::KPT) * C::kLoaders * 16));
     } else {
-      if (j < C::KPT) pool_load(pend_k, k_off_lane[j], pend_lds, j);
-      else pool_load(pend_v, v_off_lane[j - C::KPT], pend_lds + C::KBytes, j - C::KPT);
+      if (j < C::KPT) set_m0(pool_m0(pend_lds, j));
+      else set_m0(pool_m0(pend_lds + C::KBytes, j - C::KPT));
+    }
+  };
+  auto dma_load = [&](int j) {
+    if constexpr (kContig) {
+      if (j < C::KPT) load_at_m0(pend_k, k_cont_off(j, pend_lim));
+      else load_at_m0(pend_v, v_cont_off(j - C::KPT, pend_lim));
+    } else {
+      if (j < C::KPT) load_at_m0(pend_k, k_off_lane[j]);
+      else load_at_m0(pend_v, v_off_lane[j - C::KPT]);
     }
   };
 
@@ -641,9 +663,16 @@ __global__ __launch_bounds__(512, 1) void prefill_paged_kernel(const PrefillArgs
       if (is_pv(k)) pv_mfma(k >> 1, rd[k]);
       else qk_mfma(qk_index(k), rd[k], n);
       if (k + kAhead < kOps) rd[k + kAhead] = op_read(k + kAhead);
+      if constexpr (with_dma) {
+        if ((k & 3) == 1 && (k >> 2) < C::LPT) {
+          __builtin_amdgcn_sched_barrier(0);
+          dma_m0(k >> 2);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
       if ((k & 3) == 3 && (k >> 2) < C::LPT) {
         __builtin_amdgcn_sched_barrier(0);
-        if constexpr (with_dma) dma_one(k >> 2);
+        if constexpr (with_dma) dma_load(k >> 2);
         __builtin_amdgcn_sched_barrier(0);
       }
     }

@@ -428,3 +428,59 @@ def test_binding_refuses_mislaid_tensors_before_the_library():
     with pytest.raises(ValueError, match="rope: shape"):
         L.chunkattn_mla_kv_append(torch.zeros((3, L.MLA_LATENT), dtype=bf), torch.zeros((3, 32), dtype=bf), 0,
                                   table, pool, L.CA_MLA_BF16)
+
+
+# ---- the build's check of the split direct-to-LDS loads --------------------------------------------------
+
+_M0_OK = """\
+kernel:
+\t;;#ASMSTART
+\ts_mov_b32 m0, s9
+\t;;#ASMEND
+\tv_mfma_f32_16x16x32_bf16 v[94:97], v[118:121], v[106:109], v[94:97]
+\t;;#ASMSTART
+\tglobal_load_lds_dwordx4 v148, s[6:7]
+\t;;#ASMEND
+\t;;#ASMSTART
+\ts_mov_b32 m0, s10
+\ts_nop 0
+\tglobal_load_lds_dwordx4 v149, s[6:7]
+\t;;#ASMEND
+\ts_endpgm
+"""
+
+
+def test_m0_check_accepts_the_split_and_the_combined_load():
+    from chunked_prefill_causal_amd import build as B
+    assert B.check_m0(_M0_OK, "ok") == 2
+
+
+def test_m0_check_rejects_a_compiler_m0_write():
+    from chunked_prefill_causal_amd import build as B
+    bad = _M0_OK.replace("\tv_mfma_f32_16x16x32_bf16", "\ts_mov_b32 m0, -1\n\tv_mfma_f32_16x16x32_bf16")
+    with pytest.raises(RuntimeError, match="the compiler writes m0"):
+        B.check_m0(bad, "bad")
+
+
+def test_m0_check_rejects_a_load_right_after_the_m0_write():
+    from chunked_prefill_causal_amd import build as B
+    bad = _M0_OK.replace("\ts_nop 0\n", "")
+    with pytest.raises(RuntimeError, match="right after an m0 write"):
+        B.check_m0(bad, "bad")
+    # the split form with nothing between the two statements
+    bad = _M0_OK.replace("\tv_mfma_f32_16x16x32_bf16 v[94:97], v[118:121], v[106:109], v[94:97]\n", "")
+    with pytest.raises(RuntimeError, match="right after an m0 write"):
+        B.check_m0(bad, "bad")
+
+
+def test_m0_check_holds_on_the_built_kernels():
+    """The device assembly the last build checked (written beside the objects) passes again, and holds
+    the loads of both kernels."""
+    import os
+    from chunked_prefill_causal_amd import build as B
+    for src, at_least in (("prefill_paged", 100), ("mla_prefill", 20)):
+        path = os.path.join(B.BUILD_DIR, src + ".s")
+        if not os.path.exists(path):
+            pytest.skip("no build under _build/ yet")
+        with open(path) as f:
+            assert B.check_m0(f.read(), src) >= at_least
