@@ -378,24 +378,24 @@ __global__ __launch_bounds__(512, 1) void prefill_paged_kernel(const PrefillArgs
     }
     pend_lds = smem_base + st * C::Stage + (kContig ? wave * 64 * 16 : 0);
   };
-  // dma_m0(j) then dma_load(j): the LDS destination and the load of chunk j.
+  // Pool tiles: dma_m0(j) then dma_load(j), the LDS destination and the load
+  // of chunk j.  The contiguous cache keeps the single-statement load: its
+  // registers are nearly all in use, and the extra scheduling fences of the
+  // split form cost it ~5 %.
   auto dma_m0 = [&](int j) {
-    if constexpr (kContig) {
-      if (j < C::KPT) set_m0(__builtin_amdgcn_readfirstlane(pend_lds + j * C::kLoaders * 16));
-      else set_m0(__builtin_amdgcn_readfirstlane(pend_lds + C::KBytes + (j - C::KPT) * C::kLoaders * 16));
-    } else {
-      if (j < C::KPT) set_m0(pool_m0(pend_lds, j));
-      else set_m0(pool_m0(pend_lds + C::KBytes, j - C::KPT));
-    }
+    if (j < C::KPT) set_m0(pool_m0(pend_lds, j));
+    else set_m0(pool_m0(pend_lds + C::KBytes, j - C::KPT));
   };
   auto dma_load = [&](int j) {
-    if constexpr (kContig) {
-      if (j < C::KPT) load_at_m0(pend_k, k_cont_off(j, pend_lim));
-      else load_at_m0(pend_v, v_cont_off(j - C::KPT, pend_lim));
-    } else {
-      if (j < C::KPT) load_at_m0(pend_k, k_off_lane[j]);
-      else load_at_m0(pend_v, v_off_lane[j - C::KPT]);
-    }
+    if (j < C::KPT) load_at_m0(pend_k, k_off_lane[j]);
+    else load_at_m0(pend_v, v_off_lane[j - C::KPT]);
+  };
+  auto dma_one_contig = [&](int j) {
+    if (j < C::KPT)
+      load_to_lds16(pend_k, k_cont_off(j, pend_lim), __builtin_amdgcn_readfirstlane(pend_lds + j * C::kLoaders * 16));
+    else
+      load_to_lds16(pend_v, v_cont_off(j - C::KPT, pend_lim),
+                    __builtin_amdgcn_readfirstlane(pend_lds + C::KBytes + (j - C::KPT) * C::kLoaders * 16));
   };
 
   f32x4_t o[C::NDB][2];
@@ -663,7 +663,7 @@ __global__ __launch_bounds__(512, 1) void prefill_paged_kernel(const PrefillArgs
       if (is_pv(k)) pv_mfma(k >> 1, rd[k]);
       else qk_mfma(qk_index(k), rd[k], n);
       if (k + kAhead < kOps) rd[k + kAhead] = op_read(k + kAhead);
-      if constexpr (with_dma) {
+      if constexpr (with_dma && !kContig) {
         if ((k & 3) == 1 && (k >> 2) < C::LPT) {
           __builtin_amdgcn_sched_barrier(0);
           dma_m0(k >> 2);
@@ -672,7 +672,10 @@ __global__ __launch_bounds__(512, 1) void prefill_paged_kernel(const PrefillArgs
       }
       if ((k & 3) == 3 && (k >> 2) < C::LPT) {
         __builtin_amdgcn_sched_barrier(0);
-        if constexpr (with_dma) dma_load(k >> 2);
+        if constexpr (with_dma) {
+          if constexpr (kContig) dma_one_contig(k >> 2);
+          else dma_load(k >> 2);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
