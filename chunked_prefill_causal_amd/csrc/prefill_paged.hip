@@ -357,8 +357,8 @@ __global__ __launch_bounds__(512, 1) void prefill_paged_kernel(const PrefillArgs
     for (int i = 0; i < C::VPT; ++i) pool_load(vb, v_off_lane[i], ks + C::KBytes, i);
   };
   // The same transfer spread over the leading waves' matrix phase: prep() fixes
-  // the tile and stage, dma_one(j) moves this thread's j-th 16-byte chunk
-  // (K chunks first, then V).  Issued in a burst, the loads would hold the wave
+  // the tile and stage, and load j moves this thread's j-th 16-byte chunk (K
+  // chunks first, then V).  Issued in a burst, the loads would hold the wave
   // for as long as the direct-to-LDS path needs to drain a tile; one load per
   // eight MFMAs stays under that rate, so the wave never waits at issue.
   const unsigned char* pend_k = kpool;
@@ -639,8 +639,8 @@ __global__ __launch_bounds__(512, 1) void prefill_paged_kernel(const PrefillArgs
 
   // pv_qk for the leading waves with the pending tile's loads interleaved: the
   // operand reads are software-pipelined by hand (kAhead in flight) and one
-  // load goes out after every fourth operand (eighth MFMA), fenced so the
-  // order stays as written.  Whether the interval moves a tile is a
+  // load goes out after every fourth operand (eighth MFMA), its m0 written
+  // two operands before (pool tiles), fenced so the order stays as written.  Whether the interval moves a tile is a
   // compile-time tag: a runtime test at each load point put branches into the
   // matrix phase and cost ~3.5 % of the loop.
   auto pv_qk_dma = [&](int i, auto with_dma_tag) {

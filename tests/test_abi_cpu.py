@@ -484,3 +484,16 @@ def test_m0_check_holds_on_the_built_kernels():
             pytest.skip("no build under _build/ yet")
         with open(path) as f:
             assert B.check_m0(f.read(), src) >= at_least
+
+
+def test_kernel_hash_ignores_comments_but_not_code():
+    """The counter summary stays valid across comment edits and goes stale on any code edit."""
+    import sys
+    sys.path.insert(0, ROOT)
+    import bench
+    src = 'int f(int a) {  // the sum\n  return a + 1; /* one\n more */ }\nasm("s_nop 0\\n");\n'
+    same = 'int f(int a) {\n  // the sum, said differently\n  return a + 1;\n}\nasm("s_nop 0\\n");\n'
+    other = 'int f(int a) {  // the sum\n  return a + 2; /* one\n more */ }\nasm("s_nop 0\\n");\n'
+    assert bench.strip_comments(src) == bench.strip_comments(same)
+    assert bench.strip_comments(src) != bench.strip_comments(other)
+    assert "s_nop 0" in bench.strip_comments(src)
