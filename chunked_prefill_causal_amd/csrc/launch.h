@@ -103,8 +103,11 @@ bool decode_supported(int D, int DV);
 // latent + 64 rotary values per token, shared by every query head).
 constexpr int kMlaLatent = 512, kMlaRope = 64, kMlaRecord = 576, kMlaStepKeys = 32;
 // A decode work unit holds at most this many steps, so a segment spans at most
-// 64 cache blocks (the kernel keeps their ids one per lane).
-constexpr int kMlaMaxUnitSteps = 127;
+// 64 * kMlaBtRegs cache blocks (the kernel keeps their ids one per lane in
+// kMlaBtRegs registers): a segment of U steps starting on either half of a
+// block covers at most (U + 1) / 2 blocks.
+constexpr int kMlaBtRegs = 3;
+constexpr int kMlaMaxUnitSteps = 2 * 64 * kMlaBtRegs - 1;
 // Block bytes (64 tokens): bf16 [72 runs][64][16 B].  fp8: two 32-token halves,
 // each one contiguous region of codes [32 runs][32][16 B], scales [32][4 fp32]
 // and rotary [8 runs][32][16 B], so a 32-key decode step is a single region.

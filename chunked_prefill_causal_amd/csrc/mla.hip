@@ -174,21 +174,34 @@ __global__ __launch_bounds__(128) void mla_decode_kernel(const MlaArgs a) {
       for (int j = 0; j < 8; ++j) qb[j] = *(const u32x4_t*)(qrow + 32 * (8 * w + j));
       qb[8] = *(const u32x4_t*)(qrow + 32 * (16 + w));
     }
-    // The segment's block ids, lane l holding the (l+1)-th (a segment spans at
-    // most 64 blocks): the step loop then makes no load the compiler tracks,
-    // so none of its waits can stall on the direct loads in flight.
+    // The segment's block ids, lane l of register r holding the (64r + l + 1)-th
+    // (a segment spans at most 64 * kMlaBtRegs blocks): the step loop then makes
+    // no load the compiler tracks, so none of its waits can stall on the direct
+    // loads in flight.
     const int blk0 = key_lo >> 6;
     const int n_blk = ((key_hi - 1) >> 6) - blk0 + 1;
-    const int bt_lane = lane < n_blk ? a.block_tables[(int64_t)s * a.max_blocks + blk0 + lane] : 0;
+    int bt_lane[kMlaBtRegs];
+#pragma unroll
+    for (int r = 0; r < kMlaBtRegs; ++r)
+      bt_lane[r] = 64 * r + lane < n_blk ? a.block_tables[(int64_t)s * a.max_blocks + blk0 + 64 * r + lane] : 0;
 #pragma unroll
     for (int j = 0; j < 9; ++j) asm volatile("" ::"v"(qb[j]));
-    asm volatile("" ::"v"(bt_lane));
+#pragma unroll
+    for (int r = 0; r < kMlaBtRegs; ++r) asm volatile("" ::"v"(bt_lane[r]));
+    // id of the segment's idx-th block (idx wave-uniform)
+    auto block_of = [&](int idx) -> int {
+      int id = __builtin_amdgcn_readlane(bt_lane[0], idx & 63);
+#pragma unroll
+      for (int r = 1; r < kMlaBtRegs; ++r)
+        if ((idx >> 6) == r) id = __builtin_amdgcn_readlane(bt_lane[r], idx & 63);
+      return id;
+    };
 
     // step t covers keys key_lo + 32t .. +31: half (key / 32) & 1 of block key / 64.
     // Load n moves runs 2n and 2n+1 (32 tokens each); the wave issues only its own.
     auto issue = [&](int t, int st) {
       const int key0 = key_lo + kMlaStepKeys * t;
-      const int blk = clamp_block(__builtin_amdgcn_readlane(bt_lane, (key0 >> 6) - blk0), a.num_blocks);
+      const int blk = clamp_block(block_of((key0 >> 6) - blk0), a.num_blocks);
       const uint32_t lds = smem_base + st * C::kStage;
       if constexpr (FP8) {
         // the step is one contiguous half-block: each load moves 1 KiB of it

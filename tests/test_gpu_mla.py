@@ -219,6 +219,14 @@ def test_decode_most_heads(fmt):
 
 
 @pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_decode_units_spanning_many_blocks(fmt):
+    # 1024 heads keep the plan at 8 units per head block, so the 70000-key context is cut into
+    # segments of ~274 steps (up to 138 cache blocks): their block ids fill all three of the
+    # kernel's lane-indexed id registers
+    check_decode(fmt, [70000, 3, 65], 1024, 260)
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
 def test_decode_many_splits(fmt):
     # one long context among short ones: the plan gives it many splits
     check_decode(fmt, [40000, 5, 70, 300], 16, 300)
