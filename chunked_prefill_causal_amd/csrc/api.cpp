@@ -183,7 +183,7 @@ namespace {
 // fit their double-buffered LDS), and the largest split count of any sequence.
 // MLA decode plan.  The 32-key steps of all sequences, laid end to end, are
 // cut into `units` equal ranges: a multiple of the workgroups the chip holds at
-// once (2 per CU, shared by the head blocks), rounded to 8
+// once (kMlaWgPerCu* per CU, shared by the head blocks), rounded to 8
 // so units spread evenly over the XCDs, with at most kMlaMaxUnitSteps steps
 // each.  Workspace: per-sequence step prefix sums, each unit's first sequence,
 // then per head and slot (num_seqs + units slots) the partial (m, l) and O.
@@ -196,8 +196,7 @@ MlaPlan plan_mla(const int32_t* kv_lens, int num_seqs, int heads, bool fp8) {
   MlaPlan p;
   for (int s = 0; s < num_seqs; ++s) p.steps += (kv_lens[s] + kMlaStepKeys - 1) / kMlaStepKeys;
   const int nhb = heads / 16;
-  (void)fp8;                                   // both formats hold two workgroups per CU
-  int per_hb = kNumCUs * 2 / nhb;
+  int per_hb = kNumCUs * (fp8 ? kMlaWgPerCuFp8 : kMlaWgPerCuBf16) / nhb;
   per_hb = per_hb >= 8 ? per_hb / 8 * 8 : 8;
   const int64_t cap = (int64_t)per_hb * kMlaMaxUnitSteps;
   p.units = (p.steps + cap - 1) / cap * per_hb;

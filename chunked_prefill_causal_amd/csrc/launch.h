@@ -107,6 +107,10 @@ constexpr int kMlaLatent = 512, kMlaRope = 64, kMlaRecord = 576, kMlaStepKeys = 
 // kMlaBtRegs registers): a segment of U steps starting on either half of a
 // block covers at most (U + 1) / 2 blocks.
 constexpr int kMlaBtRegs = 3;
+// LDS ring depth (32-key steps) of the decode kernel and how many of its
+// workgroups one CU holds with that ring; the plan sizes a round of units by it.
+constexpr int kMlaStagesBf16 = 2, kMlaStagesFp8 = 3;
+constexpr int kMlaWgPerCuBf16 = 2, kMlaWgPerCuFp8 = 2;
 constexpr int kMlaMaxUnitSteps = 2 * 64 * kMlaBtRegs - 1;
 // Block bytes (64 tokens): bf16 [72 runs][64][16 B].  fp8: two 32-token halves,
 // each one contiguous region of codes [32 runs][32][16 B], scales [32][4 fp32]

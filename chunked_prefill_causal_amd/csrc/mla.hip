@@ -59,9 +59,45 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds_wave_base) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_wave_base), "v"(g) : "memory", "m0");
 }
 
+// N loads of 16 bytes per lane, 1 KiB apart: global uniform base + this lane's
+// 32-bit offset + 1024 i (the instruction offset, which moves the LDS address
+// alike) into LDS at m0 + 1024 i + 16 * lane.  One m0 write, one wait state.
+template <int N>
+__device__ __forceinline__ void dma16_run(const void* base, uint32_t lane_off, uint32_t lds_wave_base) {
+  static_assert(N == 1 || N == 2 || N == 4, "runs of 1, 2 or 4 KiB (the offset field reaches 4095)");
+  if constexpr (N == 1)
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_wave_base), "v"(lane_off),
+                 "s"(base)
+                 : "memory", "m0");
+  else if constexpr (N == 2)
+    asm volatile(
+        "s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2\n\tglobal_load_lds_dwordx4 %1, %2 offset:1024" ::"s"(
+            lds_wave_base),
+        "v"(lane_off), "s"(base)
+        : "memory", "m0");
+  else
+    asm volatile(
+        "s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2\n\tglobal_load_lds_dwordx4 %1, %2 offset:1024\n\t"
+        "global_load_lds_dwordx4 %1, %2 offset:2048\n\tglobal_load_lds_dwordx4 %1, %2 offset:3072" ::"s"(lds_wave_base),
+        "v"(lane_off), "s"(base)
+        : "memory", "m0");
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmem() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Wait until at most `ahead` (<= K) steps of L loads each are still in flight.
+template <int K, int L>
+__device__ __forceinline__ void wait_steps(int ahead) {
+  static_assert(K * L <= 63, "vmcnt holds 6 bits");
+  if constexpr (K == 0) {
+    wait_vmem<0>();
+  } else {
+    if (ahead >= K) wait_vmem<K * L>();
+    else wait_steps<K - 1, L>(ahead);
+  }
 }
 
 // Eight e4m3 codes (two dwords) to eight bf16 values times `scale`.
@@ -110,7 +146,7 @@ struct MlaCfg {
   // ring depth: kStages - 1 steps in flight per wave while one is consumed.
   // fp8 steps are small, so three of them (two workgroups per CU) keep more
   // bytes in flight than two (three workgroups per CU) would.
-  static constexpr int kStages = FP8 ? 3 : 2;
+  static constexpr int kStages = FP8 ? kMlaStagesFp8 : kMlaStagesBf16;
   static constexpr int kLoads = FP8 ? 8 + 1 + 2 : 16 + 2;     // direct loads per wave per step
   // partial scores: [kXSlots][2 waves][64 lanes][8 fp32].  With two slots (by
   // step parity) one barrier per step suffices.  bf16 keeps one slot and a
@@ -118,6 +154,8 @@ struct MlaCfg {
   static constexpr int kXSlots = FP8 ? 2 : 1;
   static constexpr int kXchg = kStages * kStage;
   static constexpr int kLds = kXchg + kXSlots * 2 * 64 * 32;
+  static_assert((FP8 ? kMlaWgPerCuFp8 : kMlaWgPerCuBf16) * kLds <= 160 * 1024,
+                "the plan's workgroups per CU fit the CU's LDS");
   static constexpr int64_t kBlock = FP8 ? kMlaFp8Block : kMlaBf16Block;
 };
 
@@ -154,6 +192,10 @@ __global__ __launch_bounds__(128) void mla_decode_kernel(const MlaArgs a) {
   int64_t x = (int64_t)unit * total / a.units;
   int s = a.unit_seq[unit];
   const uint32_t smem_base = lds_addr(smem);
+  // fp8: this lane's offsets inside a half-block for the wave's code, scale and rotary loads
+  const uint32_t off_codes = lane * 16 + 8 * w * 1024, off_codes4 = off_codes + 4096;
+  const uint32_t off_scales = lane * 16 + (uint32_t)kMlaFp8HalfScales;
+  const uint32_t off_rope = lane * 16 + (uint32_t)kMlaFp8HalfRope + 2 * w * 1024;
 
   // one segment per sequence the unit touches
   for (; x < u_hi; ++s) {
@@ -204,15 +246,14 @@ __global__ __launch_bounds__(128) void mla_decode_kernel(const MlaArgs a) {
       const int blk = clamp_block(block_of((key0 >> 6) - blk0), a.num_blocks);
       const uint32_t lds = smem_base + st * C::kStage;
       if constexpr (FP8) {
-        // the step is one contiguous half-block: each load moves 1 KiB of it
-        const unsigned char* h = a.pool + (int64_t)blk * C::kBlock + ((key0 >> 5) & 1) * kMlaFp8Half + lane * 16;
-#pragma unroll
-        for (int n = 8 * w; n < 8 * w + 8; ++n) dma16(h + n * 1024, lds + C::kCodes + n * 1024);
-        // the 32 keys' scales; the upper half-wave brings the first 512 B of the rotary runs into the unused
-        // half of the slot
-        dma16(h + kMlaFp8HalfScales, lds + C::kScales + w * 1024);
-#pragma unroll
-        for (int n = 2 * w; n < 2 * w + 2; ++n) dma16(h + kMlaFp8HalfRope + n * 1024, lds + C::kRope + n * 1024);
+        // The step is one contiguous half-block, addressed from a scalar base: the wave's 8 KiB of code
+        // runs, then the 32 keys' scales (the upper half-wave brings the first 512 B of the rotary runs
+        // into the unused half of the slot), then its 2 KiB of rotary runs, 1 KiB per load.
+        const unsigned char* h = a.pool + (int64_t)blk * C::kBlock + ((key0 >> 5) & 1) * kMlaFp8Half;
+        dma16_run<4>(h, off_codes, lds + C::kCodes + 8 * w * 1024);
+        dma16_run<4>(h, off_codes4, lds + C::kCodes + 8 * w * 1024 + 4096);
+        dma16_run<1>(h, off_scales, lds + C::kScales + w * 1024);
+        dma16_run<2>(h, off_rope, lds + C::kRope + 2 * w * 1024);
       } else {
         const unsigned char* b = a.pool + (int64_t)blk * C::kBlock + ((key0 >> 5) & 1) * 32 * 16 +
                                  (lane >> 5) * 1024 + (lane & 31) * 16;
@@ -239,9 +280,7 @@ __global__ __launch_bounds__(128) void mla_decode_kernel(const MlaArgs a) {
       const int t_next = t + C::kStages - 1;
       if (t_next < n_steps) issue(t_next, st == 0 ? C::kStages - 1 : st - 1);
       const int ahead = min(C::kStages - 1, n_steps - 1 - t);   // steps issued after t
-      if (C::kStages > 2 && ahead >= 2) wait_vmem<2 * C::kLoads>();
-      else if (ahead >= 1) wait_vmem<C::kLoads>();
-      else wait_vmem<0>();
+      wait_steps<C::kStages - 1, C::kLoads>(ahead);
       unsigned char* stage = smem + st * C::kStage;
       const int key0 = key_lo + kMlaStepKeys * t;
       const int valid = key_hi - key0;                 // keys of this step that count (1..32)
@@ -292,37 +331,39 @@ __global__ __launch_bounds__(128) void mla_decode_kernel(const MlaArgs a) {
       u32x4_t rd[kQ];
 #pragma unroll
       for (int k = 0; k < kAq; ++k) rd[k] = qk_read(k);
-      f32x4_t s0 = f32x4_t{0.f, 0.f, 0.f, 0.f}, s1 = s0, t0 = s0, t1 = s0;
+      f32x4_t s0 = f32x4_t{0.f, 0.f, 0.f, 0.f}, s1 = s0;
+      // fp8: per 128-value group q and row block, the partial scores of unit-scale codes; each operand is
+      // widened one MFMA ahead into the other of two register sets, so the conversions run beside the
+      // previous MFMA
+      f32x4_t tq[2][2];
+      u32x4_t kvw[2];
+      if constexpr (FP8) tq[0][0] = tq[0][1] = tq[1][0] = tq[1][1] = s0;
 #pragma unroll
       for (int k = 0; k < kQ; ++k) {
         const int row = k & 1;
+        if constexpr (FP8)
+          if (k + 1 >= 2 && k + 1 < kQ) kvw[(k + 1) & 1] = widen8(rd[k + 1][0], rd[k + 1][1], 1.0f);
         if (k < 2) {
           if (row) s1 = mfma16(rd[k], qb[8], s1);
           else s0 = mfma16(rd[k], qb[8], s0);
         } else {
           const int j = (k - 2) >> 1;
-          if constexpr (FP8) {
-            // codes widen exactly (unit scale); the group's partial gets the key scales in fp32
-            const u32x4_t kv = widen8(rd[k][0], rd[k][1], 1.0f);
-            if (row) t1 = mfma16(kv, qb[j], t1);
-            else t0 = mfma16(kv, qb[j], t0);
-            if (row && (j & 3) == 3) {
-              const int q = j >> 2;
-#pragma unroll
-              for (int r = 0; r < 4; ++r) {
-                s0[r] = __builtin_fmaf(t0[r], vs[r][q], s0[r]);
-                s1[r] = __builtin_fmaf(t1[r], vs[4 + r][q], s1[r]);
-              }
-              t0 = f32x4_t{0.f, 0.f, 0.f, 0.f};
-              t1 = t0;
-            }
-          } else {
-            if (row) s1 = mfma16(rd[k], qb[j], s1);
-            else s0 = mfma16(rd[k], qb[j], s0);
-          }
+          if constexpr (FP8) tq[j >> 2][row] = mfma16(kvw[k & 1], qb[j], tq[j >> 2][row]);
+          else if (row) s1 = mfma16(rd[k], qb[j], s1);
+          else s0 = mfma16(rd[k], qb[j], s0);
         }
         if (k + kAq < kQ) rd[k + kAq] = qk_read(k + kAq);
         __builtin_amdgcn_sched_barrier(0);            // keep the reads kAq operations ahead
+      }
+      if constexpr (FP8) {
+        // each group's partial gets its keys' scales in fp32, group 0 first
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            s0[r] = __builtin_fmaf(tq[q][0][r], vs[r][q], s0[r]);
+            s1[r] = __builtin_fmaf(tq[q][1][r], vs[4 + r][q], s1[r]);
+          }
       }
 
       // ---- swap partial scores with the other wave (same lane = same keys and head) ----
@@ -382,10 +423,13 @@ __global__ __launch_bounds__(128) void mla_decode_kernel(const MlaArgs a) {
         for (int q = 0; q < 2; ++q)
 #pragma unroll
           for (int i = 0; i < 4; ++i) pb[q][i] = pack_bf16(p[2 * i] * vs[2 * i][q], p[2 * i + 1] * vs[2 * i + 1][q]);
+        // V^T operands widened one MFMA ahead into alternating register sets
+        u32x4_t va[2];
+        va[0] = widen8((uint32_t)rv[0][0], (uint32_t)rv[0][1], 1.0f);
 #pragma unroll
         for (int bb = 0; bb < kP; ++bb) {
-          const u32x4_t va = widen8((uint32_t)rv[bb][0], (uint32_t)rv[bb][1], 1.0f);
-          o[bb] = mfma16(va, pb[bb >> 3], o[bb]);
+          if (bb + 1 < kP) va[(bb + 1) & 1] = widen8((uint32_t)rv[bb + 1][0], (uint32_t)rv[bb + 1][1], 1.0f);
+          o[bb] = mfma16(va[bb & 1], pb[bb >> 3], o[bb]);
           if (bb + kAp < kP) rv[bb + kAp] = pv_read(bb + kAp);
           __builtin_amdgcn_sched_barrier(0);
         }
