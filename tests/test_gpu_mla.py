@@ -161,6 +161,41 @@ def build_batch(fmt, kv_lens, heads, seed):
     return pool, torch.from_numpy(tables).cuda(), q, seqs
 
 
+def build_batch_flat(fmt, kv_lens, heads, seed):
+    """build_batch for many short sequences: one draw for all the batch's records (sequence s takes the next
+    kv_lens[s] of them) and one packing pass, the block of each token looked up through its own table row."""
+    n = len(kv_lens)
+    kv = np.asarray(kv_lens, dtype=np.int64)
+    needed = (kv + 63) // 64
+    nb = inputs.pool_size(int(needed.sum()))
+    perm = inputs.block_table(int(needed.sum()), seed, nb)
+    tables = np.zeros((n, int(needed.max())), dtype=np.int32)
+    first = np.concatenate([[0], np.cumsum(needed)])
+    for s in range(n):
+        tables[s, : needed[s]] = perm[first[s]: first[s + 1]]
+    total = int(kv.sum())
+    lat = bits(inputs.normal((total, 512), seed + 1, "bf16"))
+    rope = bits(inputs.normal((total, 64), seed + 2, "bf16"))
+    seq_of = np.repeat(np.arange(n), kv)
+    tok0 = np.concatenate([[0], np.cumsum(kv)])
+    pos = np.arange(total) - tok0[seq_of]
+    # byte_offsets through a per-token table: entry t of `flat` is the block of token t's position
+    flat = tables[seq_of, pos // 64]
+    host = np.full(nb * L.chunkattn_mla_block_bytes(FMTS[fmt]), POISON, dtype=np.uint8)
+    lat_off, sc_off, rope_off = byte_offsets(fmt, flat, pos % 64 + 64 * np.arange(total))
+    host[rope_off] = rope.view(np.uint8).reshape(total, 128)
+    if fmt == "bf16":
+        host[lat_off] = lat.view(np.uint8).reshape(total, 1024)
+    else:
+        codes, scales = mla.quantize_latent(inputs_f32(lat))
+        host[lat_off] = codes
+        host[sc_off] = scales.view(np.uint8).reshape(total, 16)
+    seqs = [(lat[tok0[s]: tok0[s + 1]], rope[tok0[s]: tok0[s + 1]]) for s in range(n)]
+    q = inputs.normal((n, heads, 576), seed + 5, "bf16")
+    pool = torch.from_numpy(host.reshape(nb, -1)).cuda()
+    return pool, torch.from_numpy(tables).cuda(), q, seqs
+
+
 def bf16_half_ulp(x) -> np.ndarray:
     """Half the bf16 spacing at |x|: the most one round-to-nearest-even store can change x."""
     e = np.floor(np.log2(np.maximum(np.abs(np.asarray(x, dtype=np.float64)), 2.0 ** -126)))
@@ -172,7 +207,7 @@ def check_decode(fmt, kv_lens, heads, seed, sample=None, out_dtype=torch.bfloat1
     bf16-output run must equal that fp32 output rounded once to bf16, bit for bit (the same value stored
     twice), so its error beyond the store's own rounding is the fp32 output's; it is also reported against
     the bar plus half a bf16 spacing (up to 0.0156 for |o| in [4, 8))."""
-    pool, tables, q, seqs = build_batch(fmt, kv_lens, heads, seed)
+    pool, tables, q, seqs = (build_batch_flat if len(kv_lens) > 5000 else build_batch)(fmt, kv_lens, heads, seed)
     log(f"mla decode fmt={fmt} heads={heads} out={out_dtype} kv={list(kv_lens)[:12]} n={len(kv_lens)} seed={seed}")
     out32, lse32 = L.chunk_mla_decode(q.cuda(), pool, FMTS[fmt], tables, kv_lens, SCALE, return_lse=True,
                                       out_dtype=torch.float32)
@@ -216,6 +251,17 @@ def test_decode_more_heads(fmt, heads):
 def test_decode_most_heads(fmt):
     # 1024 heads = 64 head blocks: the plan keeps its minimum of 8 units per head block
     check_decode(fmt, [1, 77, 300], 1024, 250)
+
+
+def test_decode_most_sequences():
+    # 65535 sequences, the most the entry takes, with 1-8 keys each: the plan kernel's threads own 64
+    # sequences each, a work unit spans ~130 of them, and the merge grid is 65535 x 16 workgroups;
+    # every 199th sequence and the last ones against the oracle
+    rng = np.random.default_rng(520)
+    kv = rng.integers(1, 9, size=65535).tolist()
+    kv[0], kv[-1] = 8, 1
+    sample = list(range(0, 65535, 199)) + [65533, 65534]
+    check_decode("fp8", kv, 16, 520, sample=sample, out_dtype=torch.float32)
 
 
 @pytest.mark.parametrize("fmt", ["bf16", "fp8"])
