@@ -15,7 +15,7 @@ import torch
 from chunked_prefill_causal_amd import _lib as L
 from chunked_prefill_causal_amd import inputs
 
-from gpu_common import BF16_TOL, LSE_TOL, build_batch, log, max_err, oracle_chunk, require_gpu
+from gpu_common import BF16_TOL, LSE_TOL, Pool, build_batch, log, max_err, oracle_chunk, require_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -104,6 +104,50 @@ def test_lse_and_out_rows_untouched_outside_batch_rows():
     out = torch.full((4, 8, 128), 7.0, dtype=torch.bfloat16, device="cuda")
     L.chunk_attn_varlen(q_all.cuda(), pool.k, pool.v, tables, cu, [100, 200], 0.1, out=out[:2])
     assert torch.all(out[2:] == 7.0)
+
+
+def test_most_sequences():
+    """65535 sequences, the most the entry takes: one 300-token chunk at past 700 and 65534 decodes of 1-100
+    keys, 4 query heads over 1 KV head, d 128.  The device-side plan's threads own many sequences each and
+    the decode and merge grids span every sequence.  The batch's K/V and queries are drawn in one pass each
+    (sequence s takes the next kv_lens[s] tokens); the chunk, every 257th decode and the last ones are checked
+    against the oracle."""
+    rng = np.random.default_rng(7100)
+    n, hq, hkv, d = 65535, 4, 1, 128
+    kv = rng.integers(1, 101, size=n).astype(np.int64)
+    kv[0], kv[-1] = 1000, 1
+    q_lens = np.ones(n, dtype=np.int64)
+    q_lens[0] = 300
+    needed = (kv + 63) // 64
+    pool_blocks = inputs.pool_size(int(needed.sum()))
+    perm = inputs.block_table(int(needed.sum()), 7100, pool_blocks)
+    first = np.concatenate([[0], np.cumsum(needed)])
+    tables = np.zeros((n, int(needed.max())), dtype=np.int32)
+    for s in range(n):
+        tables[s, : needed[s]] = perm[first[s]: first[s + 1]]
+    tables_d = torch.from_numpy(tables).cuda()
+    tok0 = np.concatenate([[0], np.cumsum(kv)])
+    k_all = inputs.normal((int(kv.sum()), hkv, d), 7101, "bf16")
+    v_all = inputs.normal((int(kv.sum()), hkv, d), 7102, "bf16")
+    pool = Pool(pool_blocks, hkv, d, d, torch.bfloat16)
+    k_dev, v_dev = k_all.cuda(), v_all.cuda()
+    for s in range(n):
+        L.chunkattn_kv_append(k_dev[tok0[s]: tok0[s + 1]], v_dev[tok0[s]: tok0[s + 1]], 0, tables_d[s], pool.k, pool.v)
+    cu = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
+    q_all = inputs.normal((int(cu[-1]), hq, d), 7103, "bf16")
+    scale = 1.0 / math.sqrt(d)
+    log(f"varlen: {n} sequences, {int(kv.sum())} cached tokens, {int(cu[-1])} query rows")
+    out, lse = L.chunk_attn_varlen(q_all.cuda(), pool.k, pool.v, tables_d, cu, kv.tolist(), scale, return_lse=True)
+    torch.cuda.synchronize()
+    worst, worst_lse = 0.0, 0.0
+    for s in [0] + list(range(1, n, 257)) + [n - 2, n - 1]:
+        q = q_all[cu[s]: cu[s + 1]]
+        k, v = k_all[tok0[s]: tok0[s + 1]], v_all[tok0[s]: tok0[s + 1]]
+        ref, ref_lse = oracle_chunk(q, k, v, int(kv[s] - q_lens[s]), scale)
+        worst = max(worst, max_err(out[cu[s]: cu[s + 1]], ref))
+        worst_lse = max(worst_lse, max_err(lse[:, cu[s]: cu[s + 1]], ref_lse))
+    log(f"  sampled sequences: max err {worst:.3e}, lse {worst_lse:.2e}")
+    assert worst <= BF16_TOL and worst_lse <= LSE_TOL
 
 
 @pytest.mark.parametrize("seed", [7001, 7002, 7003, 7004])
