@@ -22,8 +22,12 @@
  *
  * Conventions for every call:
  *  - Pointers named *_host are host memory; every other pointer is device
- *    memory owned by the caller.  The library allocates no device memory and
- *    keeps no device state; scratch space is passed in as `workspace`.
+ *    memory owned by the caller.  The library makes no device allocation;
+ *    scratch space is passed in as `workspace`.  Two things it keeps per
+ *    device until the process ends: the static scratch array behind
+ *    chunk_attn_varlen_noalloc (part of its code object), and the two
+ *    CU-masked streams and three events chunk_attn_varlen creates on its
+ *    first co-scheduled call on that device.
  *  - Calls enqueue work on `stream` (a hipStream_t; NULL = the default
  *    stream) and return without synchronising.
  *  - Arguments are validated before any HIP call.  A rejected call returns a
