@@ -497,3 +497,28 @@ def test_kernel_hash_ignores_comments_but_not_code():
     assert bench.strip_comments(src) == bench.strip_comments(same)
     assert bench.strip_comments(src) != bench.strip_comments(other)
     assert "s_nop 0" in bench.strip_comments(src)
+
+
+def _mla_plan_bytes(kv_lens, heads, units):
+    """Workspace of the MLA decode plan with `units` work units, as the header lays it out: step prefix
+    sums, each unit's first sequence, then (m, l) and O per head and slot (one slot per sequence and unit)."""
+    up = lambda x: (x + 255) // 256 * 256
+    n = len(kv_lens)
+    slots = n + units
+    unit_off = up((n + 1) * 8)
+    ml_off = unit_off + up(units * 4)
+    o_off = ml_off + up(heads * slots * 2 * 4)
+    return o_off + heads * slots * 512 * 4
+
+
+@pytest.mark.parametrize("kv_lens, heads, units", [
+    ([40000] * 300, 16, 1024),     # 375000 steps: two rounds of 512 units, 367 steps each (at most 383)
+    ([17000] * 256, 16, 512),      # 136192 steps: one round of 512 units, 266 steps each
+    ([300, 77, 1], 1024, 8),       # 64 head blocks: the minimum of 8 units per head block
+    ([5] * 100, 16, 100),          # fewer steps than a round: one unit per step
+])
+def test_mla_decode_plan_units(kv_lens, heads, units):
+    """The host plan cuts the batch's 32-key steps into a whole number of rounds of the workgroups the chip
+    holds (two per CU, shared by the head blocks), each unit at most 383 steps; the workspace query pins it."""
+    for fmt in (L.CA_MLA_BF16, L.CA_MLA_FP8):
+        assert L.chunkattn_mla_decode_workspace_size(kv_lens, heads, fmt) == _mla_plan_bytes(kv_lens, heads, units)
